@@ -1,0 +1,203 @@
+"""CPU fp64 oracle for the fused dense GEMM + epilogue  D = epilogue(A.B).
+
+TEST INFRASTRUCTURE ONLY.  Nothing on the product path may import, call, link
+or run this module: only ``tests/``, ``__graft_entry__.smoke()`` and the
+``cpu_baseline`` leg of ``bench.py`` use it.  It shares no code with the HIP
+library (``dense_gemm_epilogue_fp16_amd``) and imports nothing from it.
+
+Pages cited (by title, with the part of the page meant):
+  [bias-fusion]  "通过 nvmath-python 的 cuBLASLt 绑定，在 PyTorch 中实现偏差融合以提升推理性能"
+                 (blog.hotdry.top, 2025-09-22): fusing bias / ReLU into the
+                 cuBLASLt GEMM through nvmath-python's stateful Matmul API.
+  [bindings]     "nvmath-python：cuBLAS与cuSOLVER的Python绑定加速ML线性代数"
+                 (blog.hotdry.top, 2025-09-19).
+  [op-fusion]    "模型推理中的算子融合优化从LayerNorm到残差连接的图级优化"
+                 (wmrh.cn news 429806): operator fusion for inference.
+
+What is computed (the plain definition; the fused kernel reaches the same
+result up to fp32 accumulation order and one final rounding):
+  1. P = A.B, every 16-bit operand widened exactly to fp64, summed in fp64.
+  2. Z = P + bias, bias broadcast per row (shape (m,1)) or per column (shape
+     (1,n)) [bias-fusion, body: shape-constraint item of the checklist].
+  3. Y = epilogue(Z): identity (BIAS), max(Z,0) (RELU_BIAS: multiply, add bias,
+     then activate [bias-fusion, body, paragraph before the code example]),
+     tanh-form GELU (GELU_BIAS [op-fusion §一 FFN chain; bias-fusion, body,
+     closing paragraph names GELU as an epilogue]), Z + R (BIAS_RESIDUAL: the
+     residual added to the producer's output [op-fusion §三]); DEFAULT is P.
+  4. RELU_AUX_BIAS also returns the ReLU mask needed by backward
+     [bias-fusion, body, limitations paragraph on training].
+Readings where the pages say nothing precise (each is listed in the design
+notes): the GELU is the tanh form with sqrt(2/pi) and 0.044715 (Hendrycks &
+Gimpel); the mask bit is Z > 0 on the pre-activation after the bias, packed
+row-major [m, n/8] uint8, least-significant bit first (bit b of byte c is column
+8c+b); bias, residual and output share the operand dtype.
+
+Every function here is pinned by ``tests/test_oracle_pins.py`` against brute
+force, closed forms, invariants and library routines.
+"""
+from __future__ import annotations
+
+import math
+
+import numpy as np
+
+F16 = "fp16"
+BF16 = "bf16"
+
+EPILOGS = ("DEFAULT", "BIAS", "RELU_BIAS", "GELU_BIAS", "RELU_AUX_BIAS", "BIAS_RESIDUAL")
+
+# tanh-form GELU constants (Hendrycks & Gimpel, "Gaussian Error Linear Units")
+GELU_C0 = math.sqrt(2.0 / math.pi)
+GELU_C1 = 0.044715
+
+# max |D - Y| allowed per output dtype (fp16 out, bf16 out)
+TOLERANCE = {F16: 1e-2, BF16: 2e-2}
+
+
+# ---------------------------------------------------------------------------
+# exact widening of operand bit patterns
+# ---------------------------------------------------------------------------
+def widen(bits: np.ndarray, dtype: str) -> np.ndarray:
+    """fp16 / bf16 bit patterns (uint16) -> float64, exactly."""
+    bits = np.asarray(bits, dtype=np.uint16)
+    if dtype == F16:
+        return bits.view(np.float16).astype(np.float64)
+    if dtype == BF16:
+        # a bf16 value is the upper half of the fp32 with the same pattern
+        return (bits.astype(np.uint32) << np.uint32(16)).view(np.float32).astype(np.float64)
+    raise ValueError(f"unknown dtype {dtype!r}")
+
+
+# ---------------------------------------------------------------------------
+# step 1: the product
+# ---------------------------------------------------------------------------
+def product(a64: np.ndarray, b64: np.ndarray) -> np.ndarray:
+    """P = A.B in fp64 (a textbook dgemm).  Products of two 16-bit floats are
+    exact in fp64; the summation error is below K * 2^-53 * sum|a||b|."""
+    a64 = np.asarray(a64, dtype=np.float64)
+    b64 = np.asarray(b64, dtype=np.float64)
+    if a64.shape[1] == 0:
+        return np.zeros((a64.shape[0], b64.shape[1]), dtype=np.float64)
+    return a64 @ b64
+
+
+# ---------------------------------------------------------------------------
+# step 2: bias broadcast
+# ---------------------------------------------------------------------------
+def add_bias(p: np.ndarray, bias64: np.ndarray, layout: str) -> np.ndarray:
+    """Z = P + bias; "row" = bias of shape (m,1) added to every column of row i,
+    "col" = bias of shape (1,n) added to every row of column j
+    [bias-fusion, body: shape-constraint item of the checklist]."""
+    bias64 = np.asarray(bias64, dtype=np.float64).reshape(-1)
+    if layout == "row":
+        if bias64.shape[0] != p.shape[0]:
+            raise ValueError("row bias must have m entries")
+        return p + bias64[:, None]
+    if layout == "col":
+        if bias64.shape[0] != p.shape[1]:
+            raise ValueError("col bias must have n entries")
+        return p + bias64[None, :]
+    raise ValueError(f"unknown bias layout {layout!r}")
+
+
+# ---------------------------------------------------------------------------
+# step 3: the activation / residual
+# ---------------------------------------------------------------------------
+def gelu_tanh(z: np.ndarray) -> np.ndarray:
+    """0.5 z (1 + tanh(sqrt(2/pi) (z + 0.044715 z^3))) in fp64."""
+    z = np.asarray(z, dtype=np.float64)
+    return 0.5 * z * (1.0 + np.tanh(GELU_C0 * (z + GELU_C1 * z * z * z)))
+
+
+def relu(z: np.ndarray) -> np.ndarray:
+    return np.maximum(np.asarray(z, dtype=np.float64), 0.0)
+
+
+def apply_epilog(z: np.ndarray, epilog: str, r64: np.ndarray | None = None) -> np.ndarray:
+    """Y from the pre-activation Z (Z = P for DEFAULT)."""
+    if epilog in ("DEFAULT", "BIAS"):
+        return np.asarray(z, dtype=np.float64)
+    if epilog in ("RELU_BIAS", "RELU_AUX_BIAS"):
+        return relu(z)
+    if epilog == "GELU_BIAS":
+        return gelu_tanh(z)
+    if epilog == "BIAS_RESIDUAL":
+        if r64 is None:
+            raise ValueError("BIAS_RESIDUAL needs the residual")
+        return np.asarray(z, dtype=np.float64) + np.asarray(r64, dtype=np.float64)
+    raise ValueError(f"unknown epilog {epilog!r}")
+
+
+# ---------------------------------------------------------------------------
+# step 4: the auxiliary ReLU mask
+# ---------------------------------------------------------------------------
+def relu_mask(z: np.ndarray) -> np.ndarray:
+    """Packed (Z > 0): uint8 [m, n/8], bit b of byte c = column 8c+b."""
+    z = np.asarray(z, dtype=np.float64)
+    if z.shape[1] % 8:
+        raise ValueError("n must be a multiple of 8 for the packed mask")
+    return np.packbits(z > 0.0, axis=1, bitorder="little")
+
+
+# ---------------------------------------------------------------------------
+# rounding fp64 -> fp16 / bf16 (nearest, ties to even), for ulp statistics and
+# for feeding a rounded intermediate into a following GEMM
+# ---------------------------------------------------------------------------
+_FORMAT = {
+    # significand bits (with the implicit one), exponent of the smallest normal,
+    # largest finite value
+    F16: (11, -14, 65504.0),
+    BF16: (8, -126, float.fromhex("0x1.fep127")),
+}
+
+
+def round_to_bits(y: np.ndarray, dtype: str) -> np.ndarray:
+    """Round fp64 values once, to nearest-even, to fp16 / bf16; return bits."""
+    sig, emin, vmax = _FORMAT[dtype]
+    y = np.asarray(y, dtype=np.float64)
+    _, e = np.frexp(y)                      # |y| in [2^(e-1), 2^e)
+    lead = np.maximum(e - 1, emin)          # weight of the leading bit (subnormals share emin)
+    q = np.ldexp(np.ones_like(y), lead - (sig - 1))  # spacing of representable values
+    r = np.round(y / q) * q                 # numpy rounds halves to even; scaling by 2^n is exact
+    r = np.where(np.abs(r) > vmax, np.copysign(np.inf, y), r)
+    if dtype == F16:
+        return r.astype(np.float16).view(np.uint16)          # exact: r is representable
+    return (r.astype(np.float32).view(np.uint32) >> np.uint32(16)).astype(np.uint16)
+
+
+def ulp(y: np.ndarray, dtype: str) -> np.ndarray:
+    """Spacing of the 16-bit format at |y| (for the double-rounding bound)."""
+    sig, emin, _ = _FORMAT[dtype]
+    _, e = np.frexp(np.asarray(y, dtype=np.float64))
+    return np.ldexp(1.0, np.maximum(e - 1, emin) - (sig - 1))
+
+
+# ---------------------------------------------------------------------------
+# the whole path
+# ---------------------------------------------------------------------------
+def reference(a_bits, b_bits, dtype, epilog, bias_bits=None, bias_layout=None,
+              residual_bits=None, rows=None):
+    """Unrounded Y (fp64), pre-activation Z (fp64) and, for RELU_AUX_BIAS, the
+    packed mask.  ``rows`` restricts the computation to those output rows (the
+    row bias, the residual and A are sliced to match)."""
+    if epilog not in EPILOGS:
+        raise ValueError(f"unknown epilog {epilog!r}")
+    a_bits = np.asarray(a_bits, dtype=np.uint16)
+    r_bits = None if residual_bits is None else np.asarray(residual_bits, dtype=np.uint16)
+    row_bias = bias_bits
+    if rows is not None:
+        rows = np.asarray(rows, dtype=np.int64)
+        a_bits = a_bits[rows]
+        if r_bits is not None:
+            r_bits = r_bits[rows]
+        if bias_layout == "row" and bias_bits is not None:
+            row_bias = np.asarray(bias_bits, dtype=np.uint16).reshape(-1)[rows]
+    z = product(widen(a_bits, dtype), widen(b_bits, dtype))
+    if epilog != "DEFAULT":
+        if bias_bits is None or bias_layout is None:
+            raise ValueError(f"{epilog} needs a bias")
+        z = add_bias(z, widen(row_bias, dtype), bias_layout)
+    r64 = widen(r_bits, dtype) if r_bits is not None else None
+    y = apply_epilog(z, epilog, r64)
+    mask = relu_mask(z) if epilog == "RELU_AUX_BIAS" else None
+    return y, z, mask

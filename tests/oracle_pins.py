@@ -1,0 +1,306 @@
+"""Pins that tie the CPU oracle to something other than itself.
+
+Each ``pin_*`` takes the oracle module and raises AssertionError when the
+oracle disagrees with brute force, a closed form, an invariant, a hand-derived
+golden value or an independent library routine.  ``test_oracle_pins.py`` runs
+them against the oracle; ``test_oracle_mutants.py`` plants mistakes in the
+oracle and checks that some pin catches each one.
+"""
+from __future__ import annotations
+
+import math
+import os
+from fractions import Fraction
+
+import numpy as np
+
+from egm_workloads import BF16, F16, gemm_operands, integer_operands
+
+GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
+
+
+def _frac_of_bits(bits, dtype, o):
+    # exact rational value of each 16-bit pattern, taken from float.as_integer_ratio
+    return [[Fraction(*float(v).as_integer_ratio()) for v in row] for row in o.widen(bits, dtype)]
+
+
+def _brute(a, b, bias, layout, r, epilog):
+    """Exact rational GEMM + epilogue by three nested loops (no GELU)."""
+    m, k = len(a), len(a[0]) if a and a[0] else 0
+    n = len(b[0]) if b else (len(r[0]) if r else 0)
+    y, z = [], []
+    for i in range(m):
+        yr, zr = [], []
+        for j in range(n):
+            s = Fraction(0)
+            for t in range(k):
+                s += a[i][t] * b[t][j]
+            if epilog != "DEFAULT":
+                s += bias[i] if layout == "row" else bias[j]
+            zr.append(s)
+            if epilog in ("RELU_BIAS", "RELU_AUX_BIAS"):
+                yr.append(s if s > 0 else Fraction(0))
+            elif epilog == "BIAS_RESIDUAL":
+                yr.append(s + r[i][j])
+            else:
+                yr.append(s)
+        y.append(yr)
+        z.append(zr)
+    return y, z
+
+
+# ---------------------------------------------------------------------------
+def pin_brute_force_fraction(o):
+    """Exact rational brute force on tiny shapes, every epilog but GELU."""
+    shapes = [(1, 8, 1), (2, 8, 3), (3, 16, 5), (5, 8, 8), (8, 24, 17), (17, 8, 2)]
+    for s, (m, n, k) in enumerate(shapes):
+        for dtype in (F16, BF16):
+            for layout in ("row", "col"):
+                ops = gemm_operands(m, n, k, dtype, seed=100 + s, a_std=1.3, b_std=0.7,
+                                    bias_layout=layout, bias_std=0.5, residual_std=0.9)
+                a = _frac_of_bits(ops.a, dtype, o)
+                b = _frac_of_bits(ops.b, dtype, o)
+                bias = _frac_of_bits(ops.bias[None, :], dtype, o)[0]
+                r = _frac_of_bits(ops.residual, dtype, o)
+                for ep in ("DEFAULT", "BIAS", "RELU_BIAS", "RELU_AUX_BIAS", "BIAS_RESIDUAL"):
+                    y, z, mask = o.reference(ops.a, ops.b, dtype, ep, ops.bias, layout,
+                                             ops.residual if ep == "BIAS_RESIDUAL" else None)
+                    ye, ze = _brute(a, b, bias, layout, r, ep)
+                    for i in range(m):
+                        for j in range(n):
+                            ex = float(ye[i][j])
+                            assert abs(y[i, j] - ex) <= 1e-12 * (1.0 + abs(ex)), (ep, dtype, layout, i, j)
+                    if ep == "RELU_AUX_BIAS":
+                        for i in range(m):
+                            for j in range(n):
+                                bit = (int(mask[i, j // 8]) >> (j % 8)) & 1
+                                assert bit == (1 if ze[i][j] > 0 else 0), (i, j)
+
+
+def pin_integer_exact(o):
+    """Small-integer operands: P equals the int64 matmul exactly."""
+    for dtype in (F16, BF16):
+        for (m, n, k) in [(33, 40, 64), (7, 8, 1), (64, 64, 16)]:
+            ops = integer_operands(m, n, k, dtype, seed=7, bias_layout="col")
+            ai = o.widen(ops.a, dtype).astype(np.int64)
+            bi = o.widen(ops.b, dtype).astype(np.int64)
+            y, _, _ = o.reference(ops.a, ops.b, dtype, "DEFAULT")
+            assert np.array_equal(y, (ai @ bi).astype(np.float64))
+            bb = o.widen(ops.bias, dtype).astype(np.int64)
+            y, _, _ = o.reference(ops.a, ops.b, dtype, "BIAS", ops.bias, "col")
+            assert np.array_equal(y, (ai @ bi + bb[None, :]).astype(np.float64))
+
+
+def pin_identity_a(o):
+    """A = I (m = k): D = B + bias."""
+    for dtype in (F16, BF16):
+        n, k = 24, 16
+        eye = o.round_to_bits(np.eye(k), dtype)
+        ops = gemm_operands(k, n, k, dtype, seed=3, bias_layout="row")
+        y, _, _ = o.reference(eye, ops.b, dtype, "BIAS", ops.bias, "row")
+        expect = o.widen(ops.b, dtype) + o.widen(ops.bias, dtype)[:, None]
+        assert np.array_equal(y, expect)
+        y, _, _ = o.reference(eye, ops.b, dtype, "DEFAULT")
+        assert np.array_equal(y, o.widen(ops.b, dtype))
+
+
+def pin_zero_b_gives_bias(o):
+    """B = 0: Z is the bias broadcast (row: constant along a row; col: along a column)."""
+    for dtype in (F16, BF16):
+        m, n, k = 9, 16, 8
+        ops = gemm_operands(m, n, k, dtype, seed=4, bias_layout="row", residual_std=1.0)
+        zb = np.zeros((k, n), np.uint16)
+        bias = o.widen(ops.bias, dtype)
+        y, _, _ = o.reference(ops.a, zb, dtype, "BIAS", ops.bias, "row")
+        assert np.array_equal(y, np.repeat(bias[:, None], n, axis=1))
+        colb = gemm_operands(m, n, k, dtype, seed=5, bias_layout="col").bias
+        y, _, _ = o.reference(ops.a, zb, dtype, "BIAS", colb, "col")
+        assert np.array_equal(y, np.repeat(o.widen(colb, dtype)[None, :], m, axis=0))
+        y, _, _ = o.reference(ops.a, zb, dtype, "BIAS_RESIDUAL", ops.bias, "row", ops.residual)
+        assert np.array_equal(y, bias[:, None] + o.widen(ops.residual, dtype))
+
+
+def pin_zero_bias_is_default(o):
+    for dtype in (F16, BF16):
+        ops = gemm_operands(12, 16, 40, dtype, seed=6, bias_layout="col")
+        zero = np.zeros(16, np.uint16)
+        y0, _, _ = o.reference(ops.a, ops.b, dtype, "DEFAULT")
+        y1, _, _ = o.reference(ops.a, ops.b, dtype, "BIAS", zero, "col")
+        assert np.array_equal(y0, y1)
+        assert np.allclose(y0, o.widen(ops.a, dtype) @ o.widen(ops.b, dtype), rtol=0, atol=1e-12)
+
+
+def pin_transpose_duality(o):
+    """epi(A.B + b_row) == epi(B^T.A^T + b_col)^T ties the row and column layouts."""
+    for dtype in (F16, BF16):
+        m, n, k = 16, 24, 32
+        ops = gemm_operands(m, n, k, dtype, seed=8, bias_layout="row")
+        for ep in ("BIAS", "RELU_BIAS", "GELU_BIAS", "RELU_AUX_BIAS"):
+            y1, z1, _ = o.reference(ops.a, ops.b, dtype, ep, ops.bias, "row")
+            y2, z2, _ = o.reference(np.ascontiguousarray(ops.b.T), np.ascontiguousarray(ops.a.T),
+                                    dtype, ep, ops.bias, "col")
+            assert np.allclose(y1, y2.T, rtol=0, atol=1e-12), ep
+            assert np.allclose(z1, z2.T, rtol=0, atol=1e-12), ep
+
+
+def pin_relu_invariants(o):
+    for dtype in (F16, BF16):
+        ops = gemm_operands(40, 48, 64, dtype, seed=9, a_std=1.0, bias_layout="col")
+        for ep in ("RELU_BIAS", "RELU_AUX_BIAS"):
+            y, z, _ = o.reference(ops.a, ops.b, dtype, ep, ops.bias, "col")
+            assert (y >= 0).all()
+            assert (y[z < 0] == 0).all()
+            assert np.array_equal(y[z > 0], z[z > 0])
+            assert (z < 0).any() and (z > 0).any()
+
+
+def pin_mask_golden_bit_order(o):
+    """Z[i,j] = j - i through the real path: A[i] = (1, i), B = [[j...], [-1...]]."""
+    golden = {}
+    with open(os.path.join(GOLDEN, "relu_mask_j_minus_i.txt")) as f:
+        for line in f:
+            if line.strip() and not line.startswith("#"):
+                i, b0, b1 = line.split()
+                golden[int(i)] = (int(b0, 16), int(b1, 16))
+    m, n = 16, 16
+    for dtype in (F16, BF16):
+        a = o.round_to_bits(np.stack([np.ones(m), np.arange(m)], axis=1), dtype)
+        b = o.round_to_bits(np.stack([np.arange(n), -np.ones(n)], axis=0), dtype)
+        zero = np.zeros(n, np.uint16)
+        _, z, mask = o.reference(a, b, dtype, "RELU_AUX_BIAS", zero, "col")
+        assert np.array_equal(z, np.arange(n)[None, :] - np.arange(m)[:, None])
+        assert mask.shape == (m, n // 8) and mask.dtype == np.uint8
+        for i, (b0, b1) in golden.items():
+            assert (int(mask[i, 0]), int(mask[i, 1])) == (b0, b1), i
+
+
+def pin_mask_popcount(o):
+    for dtype in (F16, BF16):
+        ops = gemm_operands(32, 64, 48, dtype, seed=10, bias_layout="row")
+        y, z, mask = o.reference(ops.a, ops.b, dtype, "RELU_AUX_BIAS", ops.bias, "row")
+        pop = int(np.unpackbits(mask).sum())
+        assert pop == int((y > 0).sum()) == int((z > 0).sum())
+        # each row's bits, read LSB-first one byte at a time, are the row's predicate
+        for i in range(0, 32, 7):
+            bits = [(int(mask[i, j >> 3]) >> (j & 7)) & 1 for j in range(64)]
+            assert bits == [int(v > 0) for v in z[i]]
+
+
+def pin_gelu_library(o):
+    """tanh-form GELU against torch's own (CPU, float64) and closed forms."""
+    import torch
+    x = np.concatenate([np.linspace(-12, 12, 4001), [-40.0, -1e-8, 0.0, 1e-8, 40.0]])
+    ref = torch.nn.functional.gelu(torch.from_numpy(x.copy()), approximate="tanh").numpy()
+    got = o.gelu_tanh(x)
+    assert np.allclose(got, ref, rtol=1e-14, atol=1e-15)
+    assert o.gelu_tanh(np.array([0.0]))[0] == 0.0
+    # odd part: gelu(z) - gelu(-z) = z  (since tanh is odd)
+    z = np.linspace(-6, 6, 1001)
+    assert np.allclose(o.gelu_tanh(z) - o.gelu_tanh(-z), z, rtol=0, atol=1e-13)
+    # asymptotes
+    assert abs(o.gelu_tanh(np.array([30.0]))[0] - 30.0) < 1e-12
+    assert abs(o.gelu_tanh(np.array([-30.0]))[0]) < 1e-12
+    # the epilog applies it to Z = P + bias
+    ops = gemm_operands(8, 16, 16, BF16, seed=11, bias_layout="col")
+    y, z, _ = o.reference(ops.a, ops.b, BF16, "GELU_BIAS", ops.bias, "col")
+    assert np.allclose(y, torch.nn.functional.gelu(torch.from_numpy(z.copy()), approximate="tanh").numpy(),
+                       rtol=1e-14, atol=1e-15)
+
+
+def pin_gelu_math_tanh(o):
+    """Elementwise against math.tanh (the C library) on exact Z from brute force."""
+    ops = gemm_operands(3, 8, 5, F16, seed=12, a_std=2.0, b_std=1.0, bias_layout="row")
+    a = _frac_of_bits(ops.a, F16, o)
+    b = _frac_of_bits(ops.b, F16, o)
+    bias = _frac_of_bits(ops.bias[None, :], F16, o)[0]
+    _, ze = _brute(a, b, bias, "row", None, "BIAS")
+    y, _, _ = o.reference(ops.a, ops.b, F16, "GELU_BIAS", ops.bias, "row")
+    c = math.sqrt(2.0 / math.pi)
+    for i in range(3):
+        for j in range(8):
+            zz = float(ze[i][j])
+            ex = 0.5 * zz * (1.0 + math.tanh(c * (zz + 0.044715 * zz ** 3)))
+            assert abs(y[i, j] - ex) <= 1e-13 * (1 + abs(ex))
+
+
+def pin_residual(o):
+    for dtype in (F16, BF16):
+        ops = gemm_operands(16, 32, 24, dtype, seed=13, bias_layout="col", residual_std=1.0)
+        zero_r = np.zeros_like(ops.residual)
+        y0, _, _ = o.reference(ops.a, ops.b, dtype, "BIAS", ops.bias, "col")
+        y1, _, _ = o.reference(ops.a, ops.b, dtype, "BIAS_RESIDUAL", ops.bias, "col", zero_r)
+        assert np.array_equal(y0, y1)
+        y2, _, _ = o.reference(ops.a, ops.b, dtype, "BIAS_RESIDUAL", ops.bias, "col", ops.residual)
+        assert np.allclose(y2 - y0, o.widen(ops.residual, dtype), rtol=0, atol=1e-12)
+
+
+def pin_row_subset(o):
+    ops = gemm_operands(64, 32, 48, F16, seed=14, bias_layout="row", residual_std=1.0)
+    rows = np.array([0, 5, 17, 63])
+    for ep in ("BIAS", "BIAS_RESIDUAL", "RELU_AUX_BIAS"):
+        r = ops.residual if ep == "BIAS_RESIDUAL" else None
+        yf, zf, mf = o.reference(ops.a, ops.b, F16, ep, ops.bias, "row", r)
+        ys, zs, ms = o.reference(ops.a, ops.b, F16, ep, ops.bias, "row", r, rows=rows)
+        assert np.array_equal(ys, yf[rows]) and np.array_equal(zs, zf[rows])
+        if mf is not None:
+            assert np.array_equal(ms, mf[rows])
+
+
+def pin_rounding_golden(o):
+    with open(os.path.join(GOLDEN, "rounding_cases.txt")) as f:
+        for line in f:
+            if not line.strip() or line.startswith("#"):
+                continue
+            dtype, val, bits = line.split()[:3]
+            got = int(o.round_to_bits(np.array([float.fromhex(val)]), dtype)[0])
+            assert got == int(bits, 16), (dtype, val, hex(got), bits)
+
+
+def pin_rounding_library(o):
+    """fp16: numpy's double->half cast; bf16: torch's float->bfloat16 cast on
+    values exact in fp32 (so torch's single rounding is the same rounding)."""
+    import torch
+    g = np.random.default_rng(15)
+    x = np.concatenate([g.standard_normal(20000) * s for s in (1e-6, 1e-3, 1, 30, 3e4)])
+    # exact fp16 midpoints and their neighbours
+    h = g.standard_normal(5000).astype(np.float16).astype(np.float64)
+    hn = np.nextafter(h.astype(np.float16), np.float16(np.inf)).astype(np.float64)
+    mid = (h + hn) / 2
+    x = np.concatenate([x, mid, np.nextafter(mid, np.inf), np.nextafter(mid, -np.inf)])
+    assert np.array_equal(o.round_to_bits(x, F16), x.astype(np.float16).view(np.uint16))
+    xf = np.concatenate([g.standard_normal(20000).astype(np.float32),
+                         (g.standard_normal(20000) * 1e-30).astype(np.float32)])
+    # exact bf16 midpoints (representable in fp32)
+    bb = torch.from_numpy(xf.copy()).to(torch.bfloat16)
+    up = torch.nextafter(bb, torch.tensor(float("inf"), dtype=torch.bfloat16))
+    mids = ((bb.float() + up.float()) / 2).numpy()
+    xf = np.concatenate([xf, mids])
+    want = torch.from_numpy(xf.copy()).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    assert np.array_equal(o.round_to_bits(xf.astype(np.float64), BF16), want)
+
+
+def pin_widen_exhaustive(o):
+    """Every fp16 / bf16 pattern widens to the value numpy / torch give it."""
+    import torch
+    allb = np.arange(65536, dtype=np.uint32).astype(np.uint16)
+    w = o.widen(allb, F16)
+    ref = allb.view(np.float16).astype(np.float64)
+    fin = np.isfinite(ref)
+    assert np.array_equal(w[fin], ref[fin])
+    w = o.widen(allb, BF16)
+    ref = torch.from_numpy(allb.view(np.int16).copy()).view(torch.bfloat16).double().numpy()
+    fin = np.isfinite(ref)
+    assert np.array_equal(w[fin], ref[fin])
+
+
+def pin_empty_k(o):
+    """K = 0: the product is zero, D = epilogue(bias)."""
+    a = np.zeros((4, 0), np.uint16)
+    b = np.zeros((0, 8), np.uint16)
+    bias = o.round_to_bits(np.array([-1.0, 0.0, 2.0, 3.5]), F16)
+    y, z, mask = o.reference(a, b, F16, "RELU_AUX_BIAS", bias, "row")
+    assert np.array_equal(y, np.repeat(np.array([[0.0], [0.0], [2.0], [3.5]]), 8, axis=1))
+    assert list(mask[:, 0]) == [0, 0, 255, 255]
+
+
+PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_")]

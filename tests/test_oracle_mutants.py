@@ -1,0 +1,120 @@
+"""Plant one plausible mistake at a time in the CPU oracle and check that at
+least one pin fails for it (CPU only; the oracle is restored after each case)."""
+import numpy as np
+import pytest
+
+from oracle import egm_oracle as eo
+from oracle_pins import PINS
+
+_orig = {name: getattr(eo, name) for name in dir(eo) if not name.startswith("__")}
+
+
+def _drop_bias(p, bias64, layout):
+    return p
+
+
+def _swapped_layout(p, bias64, layout):
+    return _orig["add_bias"](p, bias64, "col" if layout == "row" else "row")
+
+
+def _drop_last_k(a64, b64):
+    if a64.shape[1] <= 1:
+        return _orig["product"](a64, b64)
+    return a64[:, :-1] @ b64[:-1]
+
+
+def _reversed_k(a64, b64):
+    return a64 @ b64[::-1]
+
+
+def _gelu_minus(z):
+    z = np.asarray(z, dtype=np.float64)
+    return 0.5 * z * (1.0 - np.tanh(eo.GELU_C0 * (z + eo.GELU_C1 * z ** 3)))
+
+
+def _gelu_sigmoid(z):
+    z = np.asarray(z, dtype=np.float64)
+    return z / (1.0 + np.exp(-1.702 * z))
+
+
+def _mask_msb(z):
+    return np.packbits(np.asarray(z) > 0.0, axis=1, bitorder="big")
+
+
+def _mask_ge(z):
+    return np.packbits(np.asarray(z) >= 0.0, axis=1, bitorder="little")
+
+
+def _relu_abs(z):
+    return np.abs(np.asarray(z, dtype=np.float64))
+
+
+def _epilog_residual_minus(z, epilog, r64=None):
+    if epilog == "BIAS_RESIDUAL":
+        return np.asarray(z) - np.asarray(r64)
+    return _orig["apply_epilog"](z, epilog, r64)
+
+
+def _epilog_gelu_on_bias_only(z, epilog, r64=None):
+    if epilog == "GELU_BIAS":
+        return _orig["relu"](z)
+    return _orig["apply_epilog"](z, epilog, r64)
+
+
+def _round_trunc(y, dtype):
+    y = np.asarray(y, dtype=np.float64)
+    if dtype == "fp16":
+        sig, emin = 11, -14
+    else:
+        sig, emin = 8, -126
+    _, e = np.frexp(y)
+    q = np.ldexp(np.ones_like(y), np.maximum(e - 1, emin) - (sig - 1))
+    r = np.trunc(y / q) * q
+    if dtype == "fp16":
+        return r.astype(np.float16).view(np.uint16)
+    return (r.astype(np.float32).view(np.uint32) >> np.uint32(16)).astype(np.uint16)
+
+
+def _round_via_f32(y, dtype):
+    # double rounding: fp64 -> fp32 -> 16 bit
+    return _orig["round_to_bits"](np.asarray(y, np.float64).astype(np.float32).astype(np.float64), dtype)
+
+
+def _widen_bf16_shift15(bits, dtype):
+    if dtype == "bf16":
+        return (np.asarray(bits, np.uint16).astype(np.uint32) << np.uint32(15)).view(np.float32).astype(np.float64)
+    return _orig["widen"](bits, dtype)
+
+
+MUTANTS = {
+    "bias_dropped": ("add_bias", _drop_bias),
+    "bias_layout_swapped": ("add_bias", _swapped_layout),
+    "product_drops_last_k": ("product", _drop_last_k),
+    "product_reversed_k": ("product", _reversed_k),
+    "gelu_sign": ("gelu_tanh", _gelu_minus),
+    "gelu_sigmoid_form": ("gelu_tanh", _gelu_sigmoid),
+    "gelu_constant": ("GELU_C1", 0.0447),
+    "mask_msb_first": ("relu_mask", _mask_msb),
+    "mask_ge_zero": ("relu_mask", _mask_ge),
+    "relu_is_abs": ("relu", _relu_abs),
+    "residual_subtracted": ("apply_epilog", _epilog_residual_minus),
+    "gelu_epilog_wrong_activation": ("apply_epilog", _epilog_gelu_on_bias_only),
+    "round_truncates": ("round_to_bits", _round_trunc),
+    "round_twice_via_fp32": ("round_to_bits", _round_via_f32),
+    "widen_bf16_wrong_shift": ("widen", _widen_bf16_shift15),
+}
+
+
+@pytest.mark.parametrize("name", sorted(MUTANTS))
+def test_mutant_is_caught(name, monkeypatch):
+    attr, bad = MUTANTS[name]
+    monkeypatch.setattr(eo, attr, bad)
+    caught = []
+    with np.errstate(all="ignore"):
+        for pin in PINS:
+            try:
+                pin(eo)
+            except Exception as exc:  # AssertionError or a shape error both count
+                caught.append((pin.__name__, type(exc).__name__))
+                break
+    assert caught, f"no pin caught the planted mistake {name!r}"

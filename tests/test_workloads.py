@@ -1,0 +1,68 @@
+"""Seeded input generator: determinism, chunk recipe, operand rounding (CPU only)."""
+import numpy as np
+import pytest
+
+import egm_workloads as W
+
+
+def test_same_seed_same_bits_any_threads(monkeypatch):
+    a = W.normal_bits((300, 50000), 0.1, W.BF16, seed=0, tensor_index=0)
+    monkeypatch.setattr(W, "_THREADS", 1)
+    b = W.normal_bits((300, 50000), 0.1, W.BF16, seed=0, tensor_index=0)
+    assert np.array_equal(a, b)
+    c = W.normal_bits((300, 50000), 0.1, W.BF16, seed=1, tensor_index=0)
+    assert not np.array_equal(a, c)
+
+
+def test_chunk_recipe():
+    # the first chunk is exactly the documented stream, scaled in fp32, rounded once
+    x = W.normal_bits((W.CHUNK + 5,), 0.25, W.F16, seed=3, tensor_index=2)
+    g = np.random.Generator(np.random.PCG64(np.random.SeedSequence(3, spawn_key=(2, 0))))
+    v = g.standard_normal(W.CHUNK, dtype=np.float32) * np.float32(0.25)
+    assert np.array_equal(x[:W.CHUNK], v.astype(np.float16).view(np.uint16))
+    g = np.random.Generator(np.random.PCG64(np.random.SeedSequence(3, spawn_key=(2, 1))))
+    v = g.standard_normal(5, dtype=np.float32) * np.float32(0.25)
+    assert np.array_equal(x[W.CHUNK:], v.astype(np.float16).view(np.uint16))
+
+
+def test_bf16_operand_rounding_matches_torch():
+    import torch
+    g = np.random.default_rng(0)
+    x = (g.standard_normal(100000) * 3).astype(np.float32)
+    want = torch.from_numpy(x).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    assert np.array_equal(W.f32_to_bits(x, W.BF16), want)
+    assert np.array_equal(W.bits_to_f32(W.f32_to_bits(x, W.BF16), W.BF16),
+                          torch.from_numpy(x).to(torch.bfloat16).float().numpy())
+
+
+def test_distribution_scale():
+    x = W.bits_to_f32(W.normal_bits((1 << 20,), 1 / 64, W.BF16, 0, 0), W.BF16)
+    assert abs(float(x.std()) - 1 / 64) < 1e-3 / 64 * 10
+    assert abs(float(x.mean())) < 1e-4
+
+
+def test_integer_operands_exact():
+    ops = W.integer_operands(17, 24, 64, W.F16, seed=1, bias_layout="col", residual=True)
+    for arr in (ops.a, ops.b, ops.bias, ops.residual):
+        v = W.bits_to_f32(arr, W.F16)
+        assert np.array_equal(v, np.round(v))
+    assert ops.bias.shape == (24,)
+
+
+def test_sample_rows():
+    r = W.sample_rows(65536, 4096, seed=1)
+    assert len(r) == 4096 and len(set(r.tolist())) == 4096
+    assert r[0] == 0 and r[-1] == 65535 and np.all(np.diff(r) > 0)
+    assert np.array_equal(r, W.sample_rows(65536, 4096, seed=1))
+    assert np.array_equal(W.sample_rows(10, 20), np.arange(10))
+
+
+def test_workload_table():
+    names = list(W.WORKLOADS)
+    assert len(names) == 5
+    w = W.WORKLOADS["gemm_relu_bias_fp16_65536x16384x16384"]
+    assert (w.m, w.n, w.k, w.dtype, w.bias_layout) == (65536, 16384, 16384, W.F16, "row")
+    with pytest.raises(ValueError):
+        W.workload_operands("ffn_bf16_4096x1024x4096")
+    ops = W.workload_operands("gemm_bias_fp16_256x256x512")
+    assert ops.a.shape == (256, 512) and ops.b.shape == (512, 256) and ops.bias.shape == (256,)
