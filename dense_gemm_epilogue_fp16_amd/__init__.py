@@ -1,0 +1,326 @@
+"""Python binding of libegm, the fused dense GEMM + epilogue library for MI355X.
+
+Argument marshalling only: every step of D = epilogue(A.B) runs in the HIP
+kernels of ``libegm.so`` behind the C ABI of ``include/egm.h``.  PyTorch
+supplies device memory (``data_ptr()``) and the stream
+(``torch.cuda.current_stream().cuda_stream``); there is no other compute path
+and no fallback: if the library is missing, importing this package fails.
+
+Two layers:
+  * ``egm_plan`` / ``egm_execute`` / ``egm_free`` / ... : the C functions with
+    the same names, on raw integers (device pointers, sizes, a stream handle);
+  * ``Matmul``: the stateful object of the bias-fusion page
+    ("通过 nvmath-python 的 cuBLASLt 绑定，在 PyTorch 中实现偏差融合以提升推理性能",
+    body, code example): construct with the operands, ``plan(epilog=...,
+    epilog_inputs={"bias": ..., "residual": ...})``, ``execute()``, ``free()``,
+    usable as a context manager.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libegm.so")
+
+# status codes (egm_status_t)
+EGM_OK = 0
+EGM_ERR_INVALID_VALUE = 1
+EGM_ERR_NOT_SUPPORTED = 2
+EGM_ERR_SHAPE = 3
+EGM_ERR_DTYPE = 4
+EGM_ERR_ALIGNMENT = 5
+EGM_ERR_INVALID_PLAN = 6
+EGM_ERR_HIP = 7
+EGM_ERR_NO_MEMORY = 8
+EGM_ERR_WORKSPACE = 9
+
+# dtypes (egm_dtype_t)
+EGM_F16 = 0
+EGM_BF16 = 1
+
+# epilogues (egm_epilog_t)
+EPILOGS = {
+    "DEFAULT": 0,
+    "BIAS": 1,
+    "RELU_BIAS": 2,
+    "GELU_BIAS": 3,
+    "RELU_AUX_BIAS": 4,
+    "BIAS_RESIDUAL": 5,
+}
+
+# bias layouts (egm_bias_layout_t)
+EGM_BIAS_NONE = 0
+EGM_BIAS_ROW = 1  # shape (m, 1)
+EGM_BIAS_COL = 2  # shape (1, n)
+
+#: every symbol include/egm.h declares
+EXPORTS = (
+    "egm_plan", "egm_execute", "egm_free", "egm_plan_workspace_bytes", "egm_plan_describe",
+    "egm_plan_config", "egm_num_configs", "egm_config_describe", "egm_status_string", "egm_abi_version",
+)
+
+
+class EgmError(RuntimeError):
+    """A non-OK status from the library."""
+
+    def __init__(self, status: int, where: str):
+        self.status = status
+        super().__init__(f"{where}: {status_string(status)}")
+
+
+class EpilogInputs(ctypes.Structure):
+    _fields_ = [("bias", ctypes.c_void_p), ("bias_layout", ctypes.c_int32), ("residual", ctypes.c_void_p)]
+
+
+class PlanOptions(ctypes.Structure):
+    _fields_ = [("fused", ctypes.c_int32), ("force_config", ctypes.c_int32),
+                ("autotune", ctypes.c_int32), ("group_m", ctypes.c_int32)]
+
+
+def _load() -> ctypes.CDLL:
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(
+            f"{LIB_PATH} is not built: run `python -m dense_gemm_epilogue_fp16_amd.build` "
+            "(or __graft_entry__.build()); there is no fallback path")
+    # torch first, so the library binds to the HIP runtime torch already loaded
+    try:
+        import torch  # noqa: F401
+    except Exception:  # pragma: no cover - torch is part of the environment
+        pass
+    lib = ctypes.CDLL(LIB_PATH)
+    vp, i32, i64, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t
+    lib.egm_plan.argtypes = [ctypes.POINTER(vp), i64, i64, i64, i32, i32, ctypes.POINTER(EpilogInputs),
+                             ctypes.POINTER(PlanOptions)]
+    lib.egm_plan.restype = i32
+    lib.egm_execute.argtypes = [vp, vp, vp, vp, vp, vp, sz, vp]
+    lib.egm_execute.restype = i32
+    lib.egm_free.argtypes = [vp]
+    lib.egm_free.restype = i32
+    lib.egm_plan_workspace_bytes.argtypes = [vp]
+    lib.egm_plan_workspace_bytes.restype = sz
+    lib.egm_plan_describe.argtypes = [vp, ctypes.c_char_p, sz]
+    lib.egm_plan_describe.restype = i32
+    lib.egm_plan_config.argtypes = [vp]
+    lib.egm_plan_config.restype = i32
+    lib.egm_num_configs.argtypes = []
+    lib.egm_num_configs.restype = i32
+    lib.egm_config_describe.argtypes = [i32, ctypes.c_char_p, sz]
+    lib.egm_config_describe.restype = i32
+    lib.egm_status_string.argtypes = [i32]
+    lib.egm_status_string.restype = ctypes.c_char_p
+    lib.egm_abi_version.argtypes = []
+    lib.egm_abi_version.restype = i32
+    return lib
+
+
+LIB = _load()
+
+
+# ---------------------------------------------------------------------------
+# the C functions, one to one
+# ---------------------------------------------------------------------------
+def status_string(status: int) -> str:
+    return LIB.egm_status_string(int(status)).decode()
+
+
+def _check(status: int, where: str) -> None:
+    if status != EGM_OK:
+        raise EgmError(status, where)
+
+
+def egm_plan(m: int, n: int, k: int, dtype: int, epilog: int, bias: int = 0, bias_layout: int = EGM_BIAS_NONE,
+             residual: int = 0, *, fused: int = 1, force_config: int = -1, autotune: int = 0,
+             group_m: int = 0, raw_status: bool = False):
+    """Returns the plan handle (int), or (status, handle) with ``raw_status``."""
+    h = ctypes.c_void_p()
+    ins = EpilogInputs(bias or None, bias_layout, residual or None)
+    opt = PlanOptions(fused, force_config, autotune, group_m)
+    st = LIB.egm_plan(ctypes.byref(h), int(m), int(n), int(k), int(dtype), int(epilog), ctypes.byref(ins),
+                      ctypes.byref(opt))
+    if raw_status:
+        return st, h.value
+    _check(st, "egm_plan")
+    return h.value
+
+
+def egm_execute(plan: int, A: int, B: int, D: int, aux: int = 0, workspace: int = 0, workspace_bytes: int = 0,
+                stream: int = 0, raw_status: bool = False):
+    st = LIB.egm_execute(plan, A or None, B or None, D or None, aux or None, workspace or None,
+                         int(workspace_bytes), stream or None)
+    if raw_status:
+        return st
+    _check(st, "egm_execute")
+    return None
+
+
+def egm_free(plan: int, raw_status: bool = False):
+    st = LIB.egm_free(plan)
+    if raw_status:
+        return st
+    _check(st, "egm_free")
+    return None
+
+
+def egm_plan_workspace_bytes(plan: int) -> int:
+    return int(LIB.egm_plan_workspace_bytes(plan))
+
+
+def egm_plan_describe(plan: int) -> str:
+    buf = ctypes.create_string_buffer(512)
+    _check(LIB.egm_plan_describe(plan, buf, len(buf)), "egm_plan_describe")
+    return buf.value.decode()
+
+
+def egm_plan_config(plan: int) -> int:
+    return int(LIB.egm_plan_config(plan))
+
+
+def egm_num_configs() -> int:
+    return int(LIB.egm_num_configs())
+
+
+def egm_config_describe(config: int) -> str:
+    buf = ctypes.create_string_buffer(256)
+    _check(LIB.egm_config_describe(int(config), buf, len(buf)), "egm_config_describe")
+    return buf.value.decode()
+
+
+def egm_abi_version() -> int:
+    return int(LIB.egm_abi_version())
+
+
+# ---------------------------------------------------------------------------
+# torch-facing stateful object
+# ---------------------------------------------------------------------------
+def _dtype_code(t) -> int:
+    import torch
+    if t.dtype == torch.float16:
+        return EGM_F16
+    if t.dtype == torch.bfloat16:
+        return EGM_BF16
+    raise TypeError(f"dtype {t.dtype} not supported: fp16 or bf16 only")
+
+
+class Matmul:
+    """D = epilogue(a @ b) for row-major a [m,k], b [k,n] torch tensors on the GPU.
+
+    ``plan(epilog="BIAS", epilog_inputs={"bias": t})`` with ``t`` shaped
+    (m,1) or (1,n) (any other shape is rejected); ``"residual"`` [m,n] for
+    BIAS_RESIDUAL.  ``execute()`` enqueues on torch's current stream and
+    returns D (and the packed [m, n/8] uint8 mask for RELU_AUX_BIAS).
+    ``a`` and ``b`` may be rebound per call: ``execute(a=..., b=...)``.
+    """
+
+    def __init__(self, a, b):
+        self._check_operand(a, "a")
+        self._check_operand(b, "b")
+        if a.dim() != 2 or b.dim() != 2 or a.shape[1] != b.shape[0]:
+            raise ValueError(f"shapes {tuple(a.shape)} and {tuple(b.shape)} do not multiply")
+        if a.dtype != b.dtype:
+            raise TypeError("a and b must share one dtype (no implicit conversion)")
+        self.a, self.b = a, b
+        self.m, self.k = a.shape
+        self.n = b.shape[1]
+        self.dtype = a.dtype
+        self._plan = None
+        self._keep = ()
+        self.epilog = None
+
+    @staticmethod
+    def _check_operand(t, name):
+        if not t.is_cuda:
+            raise ValueError(f"{name} must be a GPU tensor")
+        if not t.is_contiguous():
+            raise ValueError(f"{name} must be contiguous row-major")
+        _dtype_code(t)
+
+    def plan(self, epilog: str = "DEFAULT", epilog_inputs: dict | None = None, *, fused: bool = True,
+             force_config: int = -1, autotune: bool = False, group_m: int = 0):
+        if epilog not in EPILOGS:
+            raise ValueError(f"unknown epilog {epilog!r}; one of {sorted(EPILOGS)}")
+        ins = dict(epilog_inputs or {})
+        unknown = set(ins) - {"bias", "residual"}
+        if unknown:
+            raise ValueError(f"unknown epilog inputs {sorted(unknown)}")
+        bias_ptr, layout, res_ptr = 0, EGM_BIAS_NONE, 0
+        keep = []
+        if "bias" in ins:
+            bias = ins["bias"]
+            self._check_operand(bias, "bias")
+            if bias.dtype != self.dtype:
+                raise TypeError("bias dtype must match a and b (no implicit conversion)")
+            if tuple(bias.shape) == (self.m, 1):
+                layout = EGM_BIAS_ROW
+            elif tuple(bias.shape) == (1, self.n):
+                layout = EGM_BIAS_COL
+            else:
+                raise ValueError(f"bias shape {tuple(bias.shape)} must be (m,1)=({self.m},1) or (1,n)=(1,{self.n})")
+            bias_ptr = bias.data_ptr()
+            keep.append(bias)
+        if "residual" in ins:
+            r = ins["residual"]
+            self._check_operand(r, "residual")
+            if r.dtype != self.dtype or tuple(r.shape) != (self.m, self.n):
+                raise ValueError("residual must be [m,n] in the operand dtype")
+            res_ptr = r.data_ptr()
+            keep.append(r)
+        self.free()
+        self._plan = egm_plan(self.m, self.n, self.k, _dtype_code(self.a), EPILOGS[epilog], bias_ptr, layout,
+                              res_ptr, fused=int(fused), force_config=force_config, autotune=int(autotune),
+                              group_m=group_m)
+        self._keep = tuple(keep)
+        self.epilog = epilog
+        self._ws = None
+        wsb = egm_plan_workspace_bytes(self._plan)
+        if wsb:
+            import torch
+            self._ws = torch.empty(wsb, dtype=torch.uint8, device=self.a.device)
+        return self
+
+    def describe(self) -> str:
+        return egm_plan_describe(self._require())
+
+    def _require(self):
+        if self._plan is None:
+            raise RuntimeError("call plan() first")
+        return self._plan
+
+    def execute(self, a=None, b=None, out=None, aux=None, stream=None):
+        import torch
+        plan = self._require()
+        a = self.a if a is None else a
+        b = self.b if b is None else b
+        for t, shape in ((a, (self.m, self.k)), (b, (self.k, self.n))):
+            self._check_operand(t, "operand")
+            if tuple(t.shape) != shape or t.dtype != self.dtype:
+                raise ValueError("rebound operand must keep the planned shape and dtype")
+        d = out if out is not None else torch.empty((self.m, self.n), dtype=self.dtype, device=a.device)
+        mask = None
+        if self.epilog == "RELU_AUX_BIAS":
+            mask = aux if aux is not None else torch.empty((self.m, self.n // 8), dtype=torch.uint8, device=a.device)
+        s = stream if stream is not None else torch.cuda.current_stream(a.device)
+        ws = self._ws
+        egm_execute(plan, a.data_ptr(), b.data_ptr(), d.data_ptr(), mask.data_ptr() if mask is not None else 0,
+                    ws.data_ptr() if ws is not None else 0, ws.numel() if ws is not None else 0, s.cuda_stream)
+        return (d, mask) if mask is not None else d
+
+    def free(self):
+        if self._plan is not None:
+            egm_free(self._plan)
+            self._plan = None
+            self._keep = ()
+            self._ws = None
+
+    def __enter__(self):
+        return self
+
+    def __exit__(self, *exc):
+        self.free()
+        return False
+
+    def __del__(self):
+        try:
+            self.free()
+        except Exception:
+            pass

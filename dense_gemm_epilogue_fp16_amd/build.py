@@ -1,0 +1,72 @@
+"""Build libegm.so (the C-ABI library) in-tree with hipcc for gfx950.
+
+    python -m dense_gemm_epilogue_fp16_amd.build      # or build() from Python
+
+Translation units: egm_kernels.hip once per dtype (fp16, bf16) and the host
+API egm_api.hip, compiled in parallel, then linked into one shared library
+next to this file.
+"""
+from __future__ import annotations
+
+import os
+import shutil
+import subprocess
+import sys
+import tempfile
+from concurrent.futures import ThreadPoolExecutor
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+CSRC = os.path.join(HERE, "csrc")
+INCLUDE = os.path.join(os.path.dirname(HERE), "include")
+LIB = os.path.join(HERE, "libegm.so")
+ARCH = "gfx950"
+
+# Packed fp32 ops (v_pk_*_f32) are disabled for all device code.
+DEVICE_FLAGS = ["-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
+COMMON = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}", "-I", INCLUDE, "-Wall",
+          "-Wno-unused-command-line-argument"]
+
+
+def hipcc() -> str:
+    for cand in (os.environ.get("HIPCC"), "/opt/rocm/bin/hipcc", shutil.which("hipcc")):
+        if cand and os.path.exists(cand):
+            return cand
+    raise RuntimeError("hipcc not found (set HIPCC or install ROCm)")
+
+
+def _units(obj_dir: str):
+    return [
+        (os.path.join(CSRC, "egm_kernels.hip"), os.path.join(obj_dir, "egm_kernels_f16.o"), ["-DEGM_DTYPE=0"]),
+        (os.path.join(CSRC, "egm_kernels.hip"), os.path.join(obj_dir, "egm_kernels_bf16.o"), ["-DEGM_DTYPE=1"]),
+        (os.path.join(CSRC, "egm_api.hip"), os.path.join(obj_dir, "egm_api.o"), []),
+    ]
+
+
+def _run(cmd, verbose):
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    r = subprocess.run(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT, text=True)
+    out = "\n".join(l for l in r.stdout.splitlines() if "packed-fp32-ops' is not a recognized feature" not in l)
+    if r.returncode != 0:
+        raise RuntimeError(f"command failed ({r.returncode}): {' '.join(cmd)}\n{out}")
+    if verbose and out.strip():
+        print(out, flush=True)
+
+
+def build(verbose: bool = False, extra_flags=None) -> str:
+    """Compile every HIP translation unit for gfx950 and link libegm.so."""
+    cc = hipcc()
+    extra = list(extra_flags or [])
+    with tempfile.TemporaryDirectory(prefix="egm_build_") as obj_dir:
+        units = _units(obj_dir)
+        cmds = [[cc, *COMMON, *DEVICE_FLAGS, *defs, *extra, "-c", src, "-o", obj] for src, obj, defs in units]
+        with ThreadPoolExecutor(len(cmds)) as ex:
+            list(ex.map(lambda c: _run(c, verbose), cmds))
+        tmp = LIB + ".tmp"
+        _run([cc, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *[o for _, o, _ in units]], verbose)
+        os.replace(tmp, LIB)
+    return LIB
+
+
+if __name__ == "__main__":
+    print(build(verbose="-v" in sys.argv))

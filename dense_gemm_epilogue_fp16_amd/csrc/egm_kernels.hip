@@ -1,0 +1,73 @@
+// egm_kernels.hip - instantiates the fused GEMM + epilogue kernel for every
+// (epilogue, tile config) and the stand-alone epilogue kernel for one dtype.
+// Built twice: -DEGM_DTYPE=0 (fp16) and -DEGM_DTYPE=1 (bf16).
+#include "egm_epilogue.hpp"
+#include "egm_gemm.hpp"
+#include "egm_launch.hpp"
+
+#ifndef EGM_DTYPE
+#error "EGM_DTYPE must be 0 (fp16) or 1 (bf16)"
+#endif
+
+namespace egm {
+namespace {
+
+constexpr int DT = EGM_DTYPE;
+
+template <int EPI, int BM, int BN>
+void launch_gemm(dim3 grid, hipStream_t s, const GemmArgs& a) {
+  hipLaunchKernelGGL((gemm_epilogue_kernel<DT, EPI, TileCfg<BM, BN>>), grid, dim3(256), 0, s, a);
+}
+
+template <int EPI>
+void launch_epi(dim3 grid, hipStream_t s, const EpiArgs& a) {
+  hipLaunchKernelGGL((epilogue_kernel<DT, EPI>), grid, dim3(256), 0, s, a);
+}
+
+template <int EPI>
+GemmLaunch gemm_row(int cfg) {
+  static_assert(kNumConfigs == 5, "update the launch table with the config table");
+  switch (cfg) {
+    case 0: return &launch_gemm<EPI, 256, 256>;
+    case 1: return &launch_gemm<EPI, 256, 128>;
+    case 2: return &launch_gemm<EPI, 128, 256>;
+    case 3: return &launch_gemm<EPI, 128, 128>;
+    case 4: return &launch_gemm<EPI, 64, 64>;
+    default: return nullptr;
+  }
+}
+
+GemmLaunch gemm_table(int epi, int cfg) {
+  switch (epi) {
+    case EPI_NONE: return gemm_row<EPI_NONE>(cfg);
+    case EPI_BIAS: return gemm_row<EPI_BIAS>(cfg);
+    case EPI_RELU: return gemm_row<EPI_RELU>(cfg);
+    case EPI_GELU: return gemm_row<EPI_GELU>(cfg);
+    case EPI_RELU_AUX: return gemm_row<EPI_RELU_AUX>(cfg);
+    case EPI_RESID: return gemm_row<EPI_RESID>(cfg);
+    default: return nullptr;
+  }
+}
+
+EpiLaunch epi_table(int epi) {
+  switch (epi) {
+    case EPI_BIAS: return &launch_epi<EPI_BIAS>;
+    case EPI_RELU: return &launch_epi<EPI_RELU>;
+    case EPI_GELU: return &launch_epi<EPI_GELU>;
+    case EPI_RELU_AUX: return &launch_epi<EPI_RELU_AUX>;
+    case EPI_RESID: return &launch_epi<EPI_RESID>;
+    default: return nullptr;
+  }
+}
+
+}  // namespace
+
+#if EGM_DTYPE == 0
+GemmLaunch gemm_launcher_f16(int epi, int cfg) { return gemm_table(epi, cfg); }
+EpiLaunch epi_launcher_f16(int epi) { return epi_table(epi); }
+#else
+GemmLaunch gemm_launcher_bf16(int epi, int cfg) { return gemm_table(epi, cfg); }
+EpiLaunch epi_launcher_bf16(int epi) { return epi_table(epi); }
+#endif
+
+}  // namespace egm

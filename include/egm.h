@@ -1,0 +1,188 @@
+/*
+ * egm.h - fused dense GEMM + epilogue for AMD Instinct MI355X (gfx950).
+ *
+ *   D = epilogue(A . B),  A [m,k], B [k,n], D [m,n], all row-major, one 16-bit
+ *   dtype (fp16 or bf16) for A, B, bias, residual and D; products accumulate in
+ *   fp32 and the epilogue runs on the fp32 accumulators before the single
+ *   round-to-nearest-even conversion to the output dtype.
+ *
+ * Pages this interface follows (cited by title):
+ *   [bias-fusion] "通过 nvmath-python 的 cuBLASLt 绑定，在 PyTorch 中实现偏差融合以提升推理性能"
+ *                 (blog.hotdry.top, 2025-09-22): the stateful Matmul object
+ *                 (construct, plan with an epilog and a dict of epilog inputs,
+ *                 execute, free) in the body's code example; the epilog names
+ *                 BIAS / RELU_BIAS / RELU_AUX_BIAS; the checklist after the
+ *                 example (matching dtypes, bias shaped (m,1) or (1,n), free
+ *                 releases the plan, autotuning through options).
+ *   [bindings]    "nvmath-python：cuBLAS与cuSOLVER的Python绑定加速ML线性代数"
+ *                 (blog.hotdry.top, 2025-09-19), body, checklist items 2-3:
+ *                 plan() chooses the algorithm, execute() is non-blocking and
+ *                 the caller synchronises the stream, the algorithm choice can
+ *                 be inspected.
+ *   [op-fusion]   "模型推理中的算子融合优化从LayerNorm到残差连接的图级优化"
+ *                 (wmrh.cn news 429806) §一 (FFN chain matmul -> bias -> GELU)
+ *                 and §三 (residual added while the producer's output is still
+ *                 in registers).
+ *
+ * Ownership: the caller owns every device buffer (A, B, D, bias, residual,
+ * aux mask, workspace).  The library never allocates device memory.  A plan is
+ * a small host object owned by the library from egm_plan until egm_free.
+ * Epilog inputs (bias, residual) are bound at plan time, as the pages bind them
+ * in plan(); they must stay valid for every execute of that plan.  A, B, D and
+ * the mask are bound per execute, so one plan serves many batches.
+ *
+ * Errors: every function returns a status; nothing is thrown across the ABI.
+ * All argument checks run on the host before any HIP call.  There is no
+ * implicit dtype conversion.  egm_execute is asynchronous and stream-ordered:
+ * it returns EGM_ERR_HIP only when the launch itself fails; a device fault
+ * shows at the caller's next synchronisation of the stream.  Plans are
+ * immutable after egm_plan, so executes of one plan on several streams may
+ * overlap (their outputs must not).
+ */
+#ifndef EGM_H_
+#define EGM_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define EGM_ABI_VERSION 1
+
+typedef enum egm_status_t {
+  EGM_OK = 0,
+  EGM_ERR_INVALID_VALUE = 1, /* NULL pointer, unknown enum, bad option */
+  EGM_ERR_NOT_SUPPORTED = 2, /* valid request outside what v1 implements */
+  EGM_ERR_SHAPE = 3,         /* negative dims, n or k not a multiple of 8, too large */
+  EGM_ERR_DTYPE = 4,         /* dtype other than fp16 / bf16 */
+  EGM_ERR_ALIGNMENT = 5,     /* device pointer not 16-byte aligned */
+  EGM_ERR_INVALID_PLAN = 6,  /* NULL, freed or foreign plan handle */
+  EGM_ERR_HIP = 7,           /* the HIP runtime reported an error at launch */
+  EGM_ERR_NO_MEMORY = 8,     /* host allocation of the plan failed */
+  EGM_ERR_WORKSPACE = 9      /* workspace missing or smaller than egm_plan_workspace_bytes */
+} egm_status_t;
+
+typedef enum egm_dtype_t {
+  EGM_F16 = 0,  /* IEEE binary16 */
+  EGM_BF16 = 1  /* bfloat16 (upper half of binary32) */
+} egm_dtype_t;
+
+/*
+ * Epilogues.  Z = A.B + bias (fp32, bias broadcast per egm_bias_layout_t).
+ *   DEFAULT        D = A.B                    (no epilog inputs)
+ *   BIAS           D = Z                      [bias-fusion] body, code example
+ *   RELU_BIAS      D = max(Z, 0)              [bias-fusion] body, before the example
+ *   GELU_BIAS      D = 0.5 Z (1 + tanh(sqrt(2/pi) (Z + 0.044715 Z^3)))
+ *                                             ([op-fusion] §一 FFN chain; the
+ *                                             tanh form of Hendrycks & Gimpel)
+ *   RELU_AUX_BIAS  D = max(Z, 0) and aux[i, j/8] bit (j%8) = (Z[i,j] > 0)
+ *                                             [bias-fusion] body, limitations
+ *                                             paragraph (mask for backward)
+ *   BIAS_RESIDUAL  D = Z + R, R [m,n] row-major   [op-fusion] §三
+ */
+typedef enum egm_epilog_t {
+  EGM_EPILOG_DEFAULT = 0,
+  EGM_EPILOG_BIAS = 1,
+  EGM_EPILOG_RELU_BIAS = 2,
+  EGM_EPILOG_GELU_BIAS = 3,
+  EGM_EPILOG_RELU_AUX_BIAS = 4,
+  EGM_EPILOG_BIAS_RESIDUAL = 5
+} egm_epilog_t;
+
+/* Bias shapes accepted by the pages ([bias-fusion] body, shape item of the
+ * checklist): (m,1) adds bias[i] to row i, (1,n) adds bias[j] to column j. */
+typedef enum egm_bias_layout_t {
+  EGM_BIAS_NONE = 0,
+  EGM_BIAS_ROW = 1, /* shape (m,1): m elements */
+  EGM_BIAS_COL = 2  /* shape (1,n): n elements */
+} egm_bias_layout_t;
+
+/* Named epilog operands (the pages' epilog_inputs dict).  Device pointers,
+ * caller-owned, 16-byte aligned, in the plan's dtype. */
+typedef struct egm_epilog_inputs_t {
+  const void* bias;      /* required for every epilog except DEFAULT */
+  int32_t bias_layout;   /* egm_bias_layout_t */
+  const void* residual;  /* [m,n] row-major; required iff BIAS_RESIDUAL, else NULL */
+} egm_epilog_inputs_t;
+
+/* Plan options ([bias-fusion] checklist: autotuning through options). */
+typedef struct egm_plan_options_t {
+  int32_t fused;         /* 1 (default): one kernel.  0: the two-kernel path kept
+                            for measurement (GEMM writes P = round(A.B) to the
+                            workspace, a second kernel applies the epilogue). */
+  int32_t force_config;  /* -1 (default): per-shape choice; else a tile-config id
+                            0 .. egm_num_configs()-1 */
+  int32_t autotune;      /* 0 (default); 1: time every tile config on the first
+                            execute and keep the fastest (that execute is not
+                            thread-safe) */
+  int32_t group_m;       /* 0 (default): per-shape choice; else tile rows per
+                            L2-sharing group in the workgroup order */
+} egm_plan_options_t;
+
+typedef struct egm_plan_s* egm_plan_t;
+
+/*
+ * egm_plan - validate a problem and choose a kernel configuration.
+ *   out     receives the plan handle (set to NULL on error).
+ *   m, n, k problem size; m >= 0, n >= 0, k >= 0; n and k multiples of 8
+ *           (16-byte rows); n, k <= 2^21; m <= 2^31-1.  m == 0 or n == 0 is an
+ *           empty problem (execute does nothing); k == 0 gives D = epilogue(bias).
+ *   dtype   EGM_F16 or EGM_BF16, shared by every operand and the output.
+ *   epilog  egm_epilog_t.
+ *   in      epilog inputs (may be NULL only for DEFAULT).  RELU_AUX_BIAS needs
+ *           n % 8 == 0 (already required) for whole mask bytes.
+ *   opt     NULL for defaults.
+ * No device work and no HIP call.
+ */
+egm_status_t egm_plan(egm_plan_t* out, int64_t m, int64_t n, int64_t k, egm_dtype_t dtype,
+                      egm_epilog_t epilog, const egm_epilog_inputs_t* in,
+                      const egm_plan_options_t* opt);
+
+/*
+ * egm_execute - enqueue the plan on a HIP stream (asynchronous).
+ *   A     [m,k] device, row-major.          B [k,n] device, row-major.
+ *   D     [m,n] device, row-major output.
+ *   aux   [m, n/8] uint8 device output, required iff RELU_AUX_BIAS, else NULL.
+ *         Bit (j%8) of byte aux[i*(n/8) + j/8] is 1 iff Z[i,j] > 0 (strict;
+ *         least-significant bit = lowest column).
+ *   workspace, workspace_bytes: scratch of at least egm_plan_workspace_bytes()
+ *         (0 for a fused plan, m*n*2 for the two-kernel path); may be NULL when
+ *         that is 0.
+ *   stream  a hipStream_t (NULL = the null stream).
+ * All pointers 16-byte aligned.  A, B, bias, residual must not alias D or aux.
+ */
+egm_status_t egm_execute(egm_plan_t plan, const void* A, const void* B, void* D, void* aux,
+                         void* workspace, size_t workspace_bytes, void* stream);
+
+/* egm_free - release a plan.  NULL is accepted (EGM_OK).  A plan must not be
+ * used after it is freed; work already enqueued is unaffected. */
+egm_status_t egm_free(egm_plan_t plan);
+
+/* Bytes of workspace egm_execute needs for this plan (0 if the plan is invalid). */
+size_t egm_plan_workspace_bytes(egm_plan_t plan);
+
+/* Write a one-line description of the chosen configuration into buf (always
+ * NUL-terminated when len > 0) ([bindings] checklist item 3: inspect the
+ * algorithm choice).  EGM_LOG=1 in the environment also prints it at plan time. */
+egm_status_t egm_plan_describe(egm_plan_t plan, char* buf, size_t len);
+
+/* Tile-config id the plan will launch (after autotune, the chosen one), or -1. */
+int32_t egm_plan_config(egm_plan_t plan);
+
+/* Number of tile configurations, and a description of one of them. */
+int32_t egm_num_configs(void);
+egm_status_t egm_config_describe(int32_t config, char* buf, size_t len);
+
+/* Static text for a status code (never NULL). */
+const char* egm_status_string(egm_status_t status);
+
+/* EGM_ABI_VERSION of the built library. */
+int32_t egm_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* EGM_H_ */

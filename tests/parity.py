@@ -1,0 +1,89 @@
+"""Harness glue for the GPU parity tests: moves seeded operands to the device,
+runs the HIP path through the C ABI (via the thin binding) and compares the
+result with the CPU oracle element by element."""
+from __future__ import annotations
+
+import numpy as np
+
+from oracle import egm_oracle as eo
+
+TOL = eo.TOLERANCE  # fp16 out: 1e-2, bf16 out: 2e-2
+MASK_EXEMPT = 1e-2  # mask bits are judged only where |Z| > this
+
+
+def torch_dtype(dtype):
+    import torch
+    return torch.float16 if dtype == "fp16" else torch.bfloat16
+
+
+def to_device(bits: np.ndarray, dtype: str):
+    import torch
+    t = torch.from_numpy(np.ascontiguousarray(bits).view(np.int16))
+    return t.view(torch_dtype(dtype)).cuda()
+
+
+def to_host_bits(t) -> np.ndarray:
+    import torch
+    return t.detach().contiguous().cpu().view(torch.int16).numpy().view(np.uint16)
+
+
+def bias_tensor(bits, layout, dtype):
+    t = to_device(bits, dtype)
+    return t.reshape(-1, 1) if layout == "row" else t.reshape(1, -1)
+
+
+def run(ops, epilog, *, fused=True, force_config=-1, group_m=0, a=None, b=None, residual=None):
+    """Run one epilog on Operands through the binding; returns (D bits, mask or None)."""
+    import torch
+    import dense_gemm_epilogue_fp16_amd as egm
+    a = to_device(ops.a, ops.dtype) if a is None else a
+    b = to_device(ops.b, ops.dtype) if b is None else b
+    ins = {}
+    if epilog != "DEFAULT":
+        ins["bias"] = bias_tensor(ops.bias, ops.bias_layout, ops.dtype)
+    if epilog == "BIAS_RESIDUAL":
+        ins["residual"] = to_device(ops.residual, ops.dtype) if residual is None else residual
+    with egm.Matmul(a, b) as mm:
+        mm.plan(epilog=epilog, epilog_inputs=ins, fused=fused, force_config=force_config, group_m=group_m)
+        out = mm.execute()
+        torch.cuda.synchronize()
+    if isinstance(out, tuple):
+        return to_host_bits(out[0]), out[1].cpu().numpy()
+    return to_host_bits(out), None
+
+
+def compare(d_bits, y, dtype, *, z=None, mask=None, mask_ref=None, unfused=False, tol=None):
+    """Assert D matches the unrounded oracle Y; returns statistics.
+
+    Fused path: max |D - Y| <= tol.  Two-kernel path (the product is rounded
+    to 16 bits before the epilogue, a second rounding): |D - Y| <= tol + ulp(Y)/2.
+    Mask: bit-exact wherever |Z| > 1e-2.
+    """
+    tol = TOL[dtype] if tol is None else tol
+    d = eo.widen(d_bits, dtype)
+    assert d.shape == y.shape, (d.shape, y.shape)
+    assert np.isfinite(d).all(), "non-finite output"
+    err = np.abs(d - y)
+    bound = tol + (0.5 * eo.ulp(y, dtype) if unfused else 0.0)
+    bad = err > bound
+    stats = {"max_abs_err": float(err.max()) if err.size else 0.0, "n_out": int(err.size),
+             "n_over": int(bad.sum())}
+    if bad.any():
+        i = np.argwhere(bad)[0]
+        raise AssertionError(f"{int(bad.sum())} of {err.size} outputs exceed the bound; first at {tuple(i)}: "
+                             f"D={d[tuple(i)]!r} Y={y[tuple(i)]!r} |err|={err[tuple(i)]:.3g}")
+    if mask_ref is not None:
+        assert mask is not None and mask.shape == mask_ref.shape and mask.dtype == np.uint8
+        got = np.unpackbits(mask, axis=1, bitorder="little")
+        want = np.unpackbits(mask_ref, axis=1, bitorder="little")
+        judged = np.abs(z) > MASK_EXEMPT
+        mism = (got != want) & judged
+        stats["mask_mismatch"] = int(mism.sum())
+        stats["mask_exempt"] = int((~judged).sum())
+        assert not mism.any(), f"{int(mism.sum())} mask bits differ where |Z| > {MASK_EXEMPT}"
+    return stats
+
+
+def exact_bits(y, dtype):
+    """The single correct rounding of an exact oracle result (integer tests)."""
+    return eo.round_to_bits(y, dtype)

@@ -1,0 +1,191 @@
+"""C-ABI library: loads, exports every declared symbol, validates arguments on
+the host before any HIP call (CPU only: no test here launches a kernel)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import dense_gemm_epilogue_fp16_amd as egm
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "egm.h")
+
+F16, BF16 = egm.EGM_F16, egm.EGM_BF16
+E = egm.EPILOGS
+ROW, COL = egm.EGM_BIAS_ROW, egm.EGM_BIAS_COL
+FAKE = 0x7F0000000000  # a 256-byte aligned address; never dereferenced by plan()
+
+
+def declared_functions():
+    src = open(HEADER).read()
+    return sorted(set(re.findall(r"^\s*(?:egm_status_t|size_t|int32_t|const char\*)\s+(egm_\w+)\s*\(", src, re.M)))
+
+
+def test_every_declared_symbol_is_exported():
+    names = declared_functions()
+    assert len(names) == 10
+    assert sorted(egm.EXPORTS) == names
+    lib = ctypes.CDLL(egm.LIB_PATH)
+    for name in names:
+        assert hasattr(lib, name), name
+
+
+def test_abi_version_and_status_strings():
+    assert egm.egm_abi_version() == 1
+    for s in range(10):
+        assert egm.status_string(s).startswith("EGM_")
+    assert "unknown" in egm.status_string(12345)
+
+
+def plan_status(m=64, n=64, k=64, dtype=F16, epilog="BIAS", bias=FAKE, layout=ROW, residual=0, **kw):
+    st, h = egm.egm_plan(m, n, k, dtype, E[epilog] if isinstance(epilog, str) else epilog, bias, layout,
+                         residual, raw_status=True, **kw)
+    if h:
+        assert egm.egm_free(h, raw_status=True) == egm.EGM_OK
+    return st
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(), egm.EGM_OK),
+    (dict(m=-1), egm.EGM_ERR_SHAPE),
+    (dict(n=12), egm.EGM_ERR_SHAPE),
+    (dict(k=20), egm.EGM_ERR_SHAPE),
+    (dict(n=(1 << 21) + 8), egm.EGM_ERR_SHAPE),
+    (dict(k=(1 << 21) + 8), egm.EGM_ERR_SHAPE),
+    (dict(n=1 << 21, k=1 << 21), egm.EGM_OK),
+    (dict(m=1 << 31), egm.EGM_ERR_SHAPE),
+    (dict(dtype=2), egm.EGM_ERR_DTYPE),
+    (dict(epilog=6), egm.EGM_ERR_INVALID_VALUE),
+    (dict(epilog=-1), egm.EGM_ERR_INVALID_VALUE),
+    (dict(bias=0), egm.EGM_ERR_INVALID_VALUE),
+    (dict(layout=0), egm.EGM_ERR_SHAPE),
+    (dict(layout=3), egm.EGM_ERR_SHAPE),
+    (dict(bias=FAKE + 8), egm.EGM_ERR_ALIGNMENT),
+    (dict(epilog="BIAS_RESIDUAL"), egm.EGM_ERR_INVALID_VALUE),
+    (dict(epilog="BIAS_RESIDUAL", residual=FAKE + 2), egm.EGM_ERR_ALIGNMENT),
+    (dict(epilog="BIAS_RESIDUAL", residual=FAKE + 4096), egm.EGM_OK),
+    (dict(epilog="RELU_BIAS", residual=FAKE + 4096), egm.EGM_ERR_INVALID_VALUE),
+    (dict(epilog="DEFAULT"), egm.EGM_ERR_INVALID_VALUE),
+    (dict(epilog="DEFAULT", bias=0, layout=0), egm.EGM_OK),
+    (dict(m=0), egm.EGM_OK),
+    (dict(n=0), egm.EGM_OK),
+    (dict(k=0), egm.EGM_OK),
+    (dict(fused=2), egm.EGM_ERR_INVALID_VALUE),
+    (dict(force_config=99), egm.EGM_ERR_INVALID_VALUE),
+    (dict(force_config=-2), egm.EGM_ERR_INVALID_VALUE),
+    (dict(autotune=1, force_config=0), egm.EGM_ERR_INVALID_VALUE),
+    (dict(autotune=1), egm.EGM_OK),
+    (dict(group_m=-1), egm.EGM_ERR_INVALID_VALUE),
+    (dict(epilog="GELU_BIAS", dtype=BF16, layout=COL), egm.EGM_OK),
+    (dict(epilog="RELU_AUX_BIAS", dtype=BF16, layout=COL, n=8), egm.EGM_OK),
+])
+def test_plan_validation(kw, status):
+    assert plan_status(**kw) == status
+
+
+def test_plan_null_out_pointer():
+    ins = egm.EpilogInputs(FAKE, ROW, None)
+    assert egm.LIB.egm_plan(None, 8, 8, 8, F16, E["BIAS"], ctypes.byref(ins), None) == egm.EGM_ERR_INVALID_VALUE
+    h = ctypes.c_void_p(123)
+    # NULL options are the defaults
+    assert egm.LIB.egm_plan(ctypes.byref(h), 8, 8, 8, F16, E["BIAS"], ctypes.byref(ins), None) == egm.EGM_OK
+    assert h.value
+    assert egm.egm_plan_config(h.value) >= 0
+    egm.egm_free(h.value)
+
+
+def test_free_and_invalid_handles():
+    assert egm.egm_free(0, raw_status=True) == egm.EGM_OK
+    assert egm.egm_execute(0, FAKE, FAKE, FAKE, raw_status=True) == egm.EGM_ERR_INVALID_PLAN
+    assert egm.egm_plan_workspace_bytes(0) == 0
+    assert egm.egm_plan_config(0) == -1
+    assert egm.LIB.egm_plan_describe(None, ctypes.create_string_buffer(8), 8) == egm.EGM_ERR_INVALID_PLAN
+
+
+def test_workspace_and_describe():
+    h = egm.egm_plan(256, 512, 64, F16, E["RELU_BIAS"], FAKE, ROW, fused=0)
+    try:
+        assert egm.egm_plan_workspace_bytes(h) == 256 * 512 * 2
+        d = egm.egm_plan_describe(h)
+        assert "unfused" in d and "RELU_BIAS" in d and "row(m,1)" in d
+    finally:
+        egm.egm_free(h)
+    h = egm.egm_plan(256, 512, 64, F16, E["RELU_BIAS"], FAKE, ROW)
+    try:
+        assert egm.egm_plan_workspace_bytes(h) == 0
+        assert "path=fused" in egm.egm_plan_describe(h)
+    finally:
+        egm.egm_free(h)
+    h = egm.egm_plan(256, 512, 64, F16, E["DEFAULT"], fused=0)
+    try:
+        assert egm.egm_plan_workspace_bytes(h) == 0  # nothing to keep apart for a bare product
+    finally:
+        egm.egm_free(h)
+
+
+def test_execute_validation_before_any_hip_call(monkeypatch):
+    h = egm.egm_plan(64, 64, 64, F16, E["RELU_AUX_BIAS"], FAKE, COL)
+    try:
+        # the mask is required for RELU_AUX_BIAS
+        assert egm.egm_execute(h, FAKE, FAKE, FAKE, 0, raw_status=True) == egm.EGM_ERR_INVALID_VALUE
+        assert egm.egm_execute(h, FAKE, FAKE, 0, FAKE, raw_status=True) == egm.EGM_ERR_INVALID_VALUE
+        assert egm.egm_execute(h, FAKE + 2, FAKE, FAKE, FAKE, raw_status=True) == egm.EGM_ERR_ALIGNMENT
+        assert egm.egm_execute(h, FAKE, FAKE + 8, FAKE, FAKE, raw_status=True) == egm.EGM_ERR_ALIGNMENT
+        assert egm.egm_execute(h, FAKE, FAKE, FAKE + 4, FAKE, raw_status=True) == egm.EGM_ERR_ALIGNMENT
+        assert egm.egm_execute(h, FAKE, FAKE, FAKE, FAKE + 1, raw_status=True) == egm.EGM_ERR_ALIGNMENT
+        assert egm.egm_execute(h, 0, FAKE, FAKE, FAKE, raw_status=True) == egm.EGM_ERR_INVALID_VALUE
+        monkeypatch.setenv("EGM_FAIL_INJECT", "launch")
+        assert egm.egm_execute(h, FAKE, FAKE, FAKE, FAKE, raw_status=True) == egm.EGM_ERR_HIP
+    finally:
+        egm.egm_free(h)
+    h = egm.egm_plan(64, 64, 64, F16, E["BIAS"], FAKE, ROW)
+    try:
+        # a mask for an epilog that has none
+        assert egm.egm_execute(h, FAKE, FAKE, FAKE, FAKE, raw_status=True) == egm.EGM_ERR_INVALID_VALUE
+    finally:
+        egm.egm_free(h)
+    h = egm.egm_plan(64, 64, 64, F16, E["BIAS"], FAKE, ROW, fused=0)
+    try:
+        need = egm.egm_plan_workspace_bytes(h)
+        assert egm.egm_execute(h, FAKE, FAKE, FAKE, 0, 0, 0, raw_status=True) == egm.EGM_ERR_WORKSPACE
+        assert egm.egm_execute(h, FAKE, FAKE, FAKE, 0, FAKE, need - 1, raw_status=True) == egm.EGM_ERR_WORKSPACE
+        assert egm.egm_execute(h, FAKE, FAKE, FAKE, 0, FAKE + 8, need, raw_status=True) == egm.EGM_ERR_ALIGNMENT
+    finally:
+        egm.egm_free(h)
+    # empty output: nothing to launch, OK without touching the device
+    h = egm.egm_plan(0, 64, 64, F16, E["BIAS"], FAKE, ROW)
+    try:
+        assert egm.egm_execute(h, 0, 0, 0, raw_status=True) == egm.EGM_OK
+    finally:
+        egm.egm_free(h)
+
+
+@pytest.mark.parametrize("m,n,k,cfg", [
+    (256, 256, 512, 4),       # small square: 16 tiles of 64x64
+    (1024, 512, 2048, 4),     # the bias-fusion page's example shape
+    (4096, 4096, 1024, 0),    # FFN up-projection: 256 tiles of 256x256, one per CU
+    (4096, 1024, 4096, 3),    # FFN down-projection: 256 tiles of 128x128
+    (8192, 8192, 8192, 0),
+    (65536, 16384, 16384, 0),
+])
+def test_per_shape_choice(m, n, k, cfg):
+    h = egm.egm_plan(m, n, k, F16, E["BIAS"], FAKE, ROW)
+    try:
+        assert egm.egm_plan_config(h) == cfg
+    finally:
+        egm.egm_free(h)
+
+
+def test_config_table():
+    n = egm.egm_num_configs()
+    assert n == 5
+    assert egm.egm_config_describe(0).startswith("tile=256x256x64")
+    assert egm.LIB.egm_config_describe(n, ctypes.create_string_buffer(8), 8) == egm.EGM_ERR_INVALID_VALUE
+
+
+def test_matmul_wrapper_rejects_without_gpu():
+    import torch
+    a = torch.zeros(8, 8, dtype=torch.float16)
+    with pytest.raises(ValueError):
+        egm.Matmul(a, a)  # CPU tensors are not device memory

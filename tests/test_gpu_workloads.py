@@ -1,0 +1,115 @@
+"""The five named workloads on the HIP path vs the CPU oracle (GPU).
+
+Inputs are the seeded synthetic operands of ``egm_workloads`` at the full
+sizes; the launch configuration is the per-shape default that bench.py times.
+The largest workload is checked on 4096 sampled rows (first and last row
+always included), every column.
+"""
+import numpy as np
+import pytest
+
+import egm_workloads as W
+from oracle import egm_oracle as eo
+from parity import compare, run, to_device, to_host_bits
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    import torch
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+
+
+def _check_gemm(name, epilog, fused=True):
+    ops = W.workload_operands(name)
+    d, mask = run(ops, epilog, fused=fused)
+    y, z, mref = eo.reference(ops.a, ops.b, ops.dtype, epilog, ops.bias, ops.bias_layout)
+    st = compare(d, y, ops.dtype, z=z, mask=mask, mask_ref=mref, unfused=not fused)
+    print(f"[{name} {epilog} {'fused' if fused else 'unfused'}] {st}", flush=True)
+    return st
+
+
+@pytest.mark.parametrize("fused", [True, False])
+def test_small_square_bias(fused):
+    _check_gemm("gemm_bias_fp16_256x256x512", "BIAS", fused)
+
+
+@pytest.mark.parametrize("fused", [True, False])
+@pytest.mark.parametrize("epilog", ["BIAS", "RELU_BIAS"])
+def test_worked_example_shape(epilog, fused):
+    _check_gemm("gemm_bias_relu_fp16_1024x512x2048", epilog, fused)
+
+
+@pytest.mark.slow
+def test_ffn_chain():
+    """Up-projection GELU_BIAS then down-projection BIAS_RESIDUAL (R = X).
+    (i) each GEMM against the oracle fed the GPU's own H; (ii) the chain against
+    the oracle's own rounded H."""
+    import torch
+    import dense_gemm_epilogue_fp16_amd as egm
+    f = W.ffn_operands()
+    x, w1, w2 = to_device(f.x, "bf16"), to_device(f.w1, "bf16"), to_device(f.w2, "bf16")
+    b1 = to_device(f.b1, "bf16").reshape(1, -1)
+    b2 = to_device(f.b2, "bf16").reshape(1, -1)
+    with egm.Matmul(x, w1) as up, egm.Matmul(torch.empty((f.tokens, f.ffn), dtype=torch.bfloat16, device="cuda"),
+                                             w2) as down:
+        up.plan("GELU_BIAS", {"bias": b1})
+        h = up.execute()
+        down.plan("BIAS_RESIDUAL", {"bias": b2, "residual": x})
+        d = down.execute(a=h)
+        torch.cuda.synchronize()
+    h_bits, d_bits = to_host_bits(h), to_host_bits(d)
+    y_up, _, _ = eo.reference(f.x, f.w1, "bf16", "GELU_BIAS", f.b1, "col")
+    print("[ffn up]", compare(h_bits, y_up, "bf16"), flush=True)
+    y_dn, _, _ = eo.reference(h_bits, f.w2, "bf16", "BIAS_RESIDUAL", f.b2, "col", f.x)
+    print("[ffn down, GPU H]", compare(d_bits, y_dn, "bf16"), flush=True)
+    h_ref = eo.round_to_bits(y_up, "bf16")
+    y_chain, _, _ = eo.reference(h_ref, f.w2, "bf16", "BIAS_RESIDUAL", f.b2, "col", f.x)
+    print("[ffn chain, oracle H]", compare(d_bits, y_chain, "bf16"), flush=True)
+
+
+@pytest.mark.slow
+def test_square_relu_aux_bias():
+    _check_gemm("gemm_relu_aux_bias_bf16_8192x8192x8192", "RELU_AUX_BIAS")
+
+
+@pytest.mark.slow
+@pytest.mark.parametrize("fused", [True, False])
+def test_largest_sampled_rows(fused):
+    import torch
+    import dense_gemm_epilogue_fp16_amd as egm
+    name = "gemm_relu_bias_fp16_65536x16384x16384"
+    ops = W.workload_operands(name)
+    rows = W.sample_rows(ops.m, 4096, seed=1)
+    a, b = to_device(ops.a, "fp16"), to_device(ops.b, "fp16")
+    bias = to_device(ops.bias, "fp16").reshape(-1, 1)
+    with egm.Matmul(a, b) as mm:
+        mm.plan("RELU_BIAS", {"bias": bias}, fused=fused)
+        d = mm.execute()
+        sel = d.index_select(0, torch.from_numpy(rows).cuda())
+        torch.cuda.synchronize()
+    del a, d
+    y, _, _ = eo.reference(ops.a, ops.b, "fp16", "RELU_BIAS", ops.bias, "row", rows=rows)
+    st = compare(to_host_bits(sel), y, "fp16", unfused=not fused)
+    print(f"[{name} fused={fused} rows={len(rows)}] {st}", flush=True)
+
+
+@pytest.mark.parametrize("name", [n for n in W.WORKLOAD_ORDER if not n.startswith("ffn_")][:3] +
+                         ["ffn_up", "ffn_down"])
+def test_supplementary_unit_scale(name):
+    """A ~ N(0,1), B ~ N(0,1)/sqrt(K), zero bias: the GEMM term itself is O(1)
+    and is held to the same tolerance (the workloads' own scaling makes it
+    O(K^-1/2) next to an N(0,1) bias)."""
+    shapes = {"ffn_up": (4096, 4096, 1024, "bf16"), "ffn_down": (4096, 1024, 4096, "bf16")}
+    if name in shapes:
+        m, n, k, dtype = shapes[name]
+    else:
+        w = W.WORKLOADS[name]
+        m, n, k, dtype = w.m, w.n, w.k, w.dtype
+    ops = W.gemm_operands(m, n, k, dtype, seed=21, a_std=1.0, bias_layout="col")
+    ops.bias = np.zeros_like(ops.bias)
+    d, _ = run(ops, "BIAS")
+    y, _, _ = eo.reference(ops.a, ops.b, dtype, "BIAS", ops.bias, "col")
+    print(f"[unit-scale {name}]", compare(d, y, dtype), flush=True)
