@@ -1,0 +1,326 @@
+#!/usr/bin/env python3
+"""Benchmark of the fused dense GEMM + epilogue on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+
+A step is one pass of the hot path over one batch of synthetic input already
+resident in HBM: one fused GEMM + epilogue launch (for the FFN workload, the
+up- and down-projection launches).  The deliberately unfused two-kernel path
+is timed the same way in the same run for the fused-vs-unfused speedup.
+
+Prints ONE JSON line: metric = fused TFLOP/s (value), % of the fp16/bf16 dense
+MFMA peak (roofline.frac), fused vs unfused speedup; roofline of the dominant
+kernel with its average duration from HIP events on the launch stream; and the
+CPU fp64 oracle timed on a bounded row sample of the same workload
+(cpu_baseline).
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_TFLOPS = 2500.0      # MI355X dense fp16 / bf16 MFMA (published)
+PEAK_HBM_GBS = 8000.0     # MI355X HBM3E (published)
+DEFAULT_WORKLOAD = "gemm_relu_bias_fp16_65536x16384x16384"
+KERNEL_SOURCES = ("egm_gemm.hpp", "egm_device.hpp", "egm_epilogue.hpp", "egm_kernels.hip", "egm_api.hip")
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, "dense_gemm_epilogue_fp16_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def traffic_from_profile(workload: str):
+    """Measured HBM bytes per launch (rocprofv3 FETCH_SIZE + WRITE_SIZE, scaled
+    by a plain-copy calibration), if taken on the current kernel sources."""
+    path = os.path.join(ROOT, "profiles", f"traffic_{workload}.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        t = json.load(f)
+    if t.get("kernel_source_hash") != kernel_source_hash():
+        return None
+    return t.get("bytes_per_launch")
+
+
+def algorithmic_bytes(m, n, k, epilog, bias_layout):
+    """Fused path: read A, B, bias (+R) once, write D (+mask) once."""
+    b = 2 * (m * k + k * n + m * n)
+    b += 2 * (m if bias_layout == "row" else n)
+    if epilog == "BIAS_RESIDUAL":
+        b += 2 * m * n
+    if epilog == "RELU_AUX_BIAS":
+        b += m * n // 8
+    return b
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0, help="target CPU time of the oracle sample")
+    ap.add_argument("--copy-mib", type=int, default=0,
+                    help="also run one plain device copy of this many MiB (calibrates rocprofv3 byte counters)")
+    ap.add_argument("--ingest-pmc", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
+                    help="turn two rocprofv3 --pmc runs (FETCH_SIZE, WRITE_SIZE) of this benchmark with "
+                         "--copy-mib into profiles/traffic_<workload>.json, then exit")
+    args = ap.parse_args()
+    if args.ingest_pmc:
+        ingest_pmc(args.workload, *args.ingest_pmc, copy_mib=args.copy_mib or 1024)
+        return
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(json.dumps({"error": "this benchmark runs on one GPU only: the fused GEMM + epilogue needs no "
+                          "collective, and every workload fits one MI355X; run with --gpus 1"}), flush=True)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import dense_gemm_epilogue_fp16_amd as egm
+    import egm_workloads as W
+
+    if not torch.cuda.is_available():
+        print(json.dumps({"error": "no GPU"}), flush=True)
+        sys.exit(1)
+    dev = torch.device("cuda:0")
+    stream = torch.cuda.current_stream(dev)
+
+    def to_dev(bits, dtype, shape):
+        t = torch.from_numpy(np.ascontiguousarray(bits).view(np.int16))
+        return t.view(torch.float16 if dtype == "fp16" else torch.bfloat16).reshape(shape).to(dev)
+
+    t_setup = time.time()
+    name = args.workload
+    wl = W.WORKLOADS[name]
+    keep = []
+    if name.startswith("ffn_"):
+        f = W.ffn_operands()
+        x = to_dev(f.x, "bf16", (f.tokens, f.hidden))
+        w1 = to_dev(f.w1, "bf16", (f.hidden, f.ffn))
+        w2 = to_dev(f.w2, "bf16", (f.ffn, f.hidden))
+        b1 = to_dev(f.b1, "bf16", (1, f.ffn))
+        b2 = to_dev(f.b2, "bf16", (1, f.hidden))
+        h = torch.empty((f.tokens, f.ffn), dtype=torch.bfloat16, device=dev)
+        d = torch.empty((f.tokens, f.hidden), dtype=torch.bfloat16, device=dev)
+        specs = [((x, w1), "GELU_BIAS", {"bias": b1}, dict(out=h), (f.tokens, f.ffn, f.hidden), "col"),
+                 ((h, w2), "BIAS_RESIDUAL", {"bias": b2, "residual": x}, dict(out=d), (f.tokens, f.hidden, f.ffn),
+                  "col")]
+        keep += [x, w1, w2, b1, b2, h, d]
+        host_ops = None
+    else:
+        ops = W.workload_operands(name)
+        a = to_dev(ops.a, ops.dtype, (ops.m, ops.k))
+        b = to_dev(ops.b, ops.dtype, (ops.k, ops.n))
+        bias = to_dev(ops.bias, ops.dtype, (ops.m, 1) if ops.bias_layout == "row" else (1, ops.n))
+        d = torch.empty((ops.m, ops.n), dtype=a.dtype, device=dev)
+        epilog = wl.epilogs[-1]
+        out = dict(out=d)
+        if epilog == "RELU_AUX_BIAS":
+            out["aux"] = torch.empty((ops.m, ops.n // 8), dtype=torch.uint8, device=dev)
+        specs = [((a, b), epilog, {"bias": bias}, out, (ops.m, ops.n, ops.k), ops.bias_layout)]
+        keep += [a, b, bias, d]
+        host_ops = ops
+    if args.copy_mib:
+        src = torch.empty(args.copy_mib << 20, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        del src, dst
+    torch.cuda.synchronize(dev)
+    setup_s = time.time() - t_setup
+
+    def make(fused):
+        res = []
+        for (aa, bb), ep, ins, out, (m, n, k), layout in specs:
+            mm = egm.Matmul(aa, bb)
+            mm.plan(ep, ins, fused=fused)
+            res.append((mm, out, (m, n, k), ep, layout))
+        return res
+
+    fused_plans = make(True)
+    unfused_plans = make(False)
+    flops = sum(2 * m * n * k for _, _, (m, n, k), _, _ in fused_plans)
+
+    def step(plans):
+        for mm, out, _, _, _ in plans:
+            mm.execute(**out)
+
+    def timed(plans, steps, warmup):
+        for _ in range(warmup):
+            step(plans)
+        torch.cuda.synchronize(dev)
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        t0 = time.perf_counter()
+        e0.record(stream)
+        for _ in range(steps):
+            step(plans)
+        e1.record(stream)
+        torch.cuda.synchronize(dev)
+        wall = time.perf_counter() - t0
+        return e0.elapsed_time(e1) / steps, wall
+
+    fused_ms, fused_wall = timed(fused_plans, args.steps, args.warmup)
+    unfused_ms, _ = timed(unfused_plans, args.steps, args.warmup)
+    # fused again after the unfused leg (same step count); the two fused legs are averaged
+    fused_ms2, fused_wall2 = timed(fused_plans, args.steps, 1)
+    fused_ms = 0.5 * (fused_ms + fused_ms2)
+    fused_wall += fused_wall2
+
+    # per-launch roofline of the dominant kernel (the largest GEMM of the step)
+    dom = max(fused_plans, key=lambda p: p[2][0] * p[2][1] * p[2][2])
+    dm, dn, dk = dom[2]
+    if len(fused_plans) > 1:
+        only = [dom]
+        dom_ms, _ = timed(only, args.steps, 1)
+    else:
+        dom_ms = fused_ms
+    dom_flops = 2 * dm * dn * dk
+    achieved = dom_flops / (dom_ms * 1e-3) / 1e12
+    tb = traffic_from_profile(name)
+
+    value = flops / (fused_ms * 1e-3) / 1e12
+    alg = sum(algorithmic_bytes(m, n, k, ep, lay) for _, _, (m, n, k), ep, lay in fused_plans)
+    extra = sum(4 * m * n for _, _, (m, n, k), _, _ in fused_plans)  # P written and read back
+    result = {
+        "metric": "fused GEMM+epilogue TFLOP/s (fp16/bf16 MFMA, fp32 accumulate)",
+        "value": round(value, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(fused_ms, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": wl.dtype,
+        "data": "synthetic (seeded normal operands, resident in HBM)",
+        "config": {"workload": name, "m": wl.m, "n": wl.n, "k": wl.k, "epilog": "+".join(wl.epilogs),
+                   "bias": "(m,1)" if wl.bias_layout == "row" else "(1,n)", "accumulate": "fp32",
+                   "plan": fused_plans[0][0].describe()},
+        "pct_of_mfma_peak": round(100.0 * value / PEAK_TFLOPS, 2),
+        "unfused_ms_per_step": round(unfused_ms, 4),
+        "speedup_vs_unfused": round(unfused_ms / fused_ms, 4),
+        "bytes_fused_algorithmic": alg,
+        "bytes_saved_by_fusion": extra,
+        "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(achieved / PEAK_TFLOPS, 4), "traffic": tb,
+                     "kernel": f"gemm_epilogue_kernel {dm}x{dn}x{dk} {dom[3]}",
+                     "avg_launch_ms": round(dom_ms, 4), "flops_per_launch": dom_flops,
+                     "algorithmic_bytes_per_launch": algorithmic_bytes(dm, dn, dk, dom[3], dom[4])},
+        "setup_s": round(setup_s, 1),
+        "timed_wall_s": round(fused_wall, 3),
+    }
+
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline(name, host_ops, keep, args.cpu_seconds)
+
+    for mm, *_ in fused_plans + unfused_plans:
+        mm.free()
+    print(json.dumps(result), flush=True)
+
+
+def _pmc_per_kernel(directory, counter):
+    """Average counter value per dispatch, by kernel name, from rocprofv3 CSVs."""
+    import csv
+    import glob
+    sums, counts = {}, {}
+    for path in glob.glob(os.path.join(directory, "**", "*counter_collection.csv"), recursive=True):
+        with open(path) as f:
+            for row in csv.DictReader(f):
+                if row.get("Counter_Name") != counter:
+                    continue
+                k = row.get("Kernel_Name", "?")
+                sums[k] = sums.get(k, 0.0) + float(row["Counter_Value"])
+                counts[k] = counts.get(k, 0) + 1
+    return {k: sums[k] / counts[k] for k in sums}
+
+
+def ingest_pmc(workload, fetch_dir, write_dir, copy_mib):
+    """HBM bytes per launch of the dominant kernel: FETCH_SIZE and WRITE_SIZE
+    (KiB per dispatch) scaled by what the same counters read for a plain copy
+    of copy_mib MiB (which moves exactly that many bytes each way)."""
+    fetch = _pmc_per_kernel(fetch_dir, "FETCH_SIZE")
+    write = _pmc_per_kernel(write_dir, "WRITE_SIZE")
+    copy_k = [k for k in fetch if "copy" in k.lower() or "elementwise" in k.lower()]
+    gemm_k = [k for k in fetch if "gemm_epilogue_kernel" in k]
+    if not copy_k or not gemm_k:
+        raise SystemExit(f"kernels not found: {sorted(fetch)}")
+    copy_bytes = float(copy_mib << 20)
+    ck = max(copy_k, key=lambda k: fetch[k])
+    f_scale = copy_bytes / (fetch[ck] * 1024.0)
+    w_scale = copy_bytes / (write[ck] * 1024.0)
+    gk = max(gemm_k, key=lambda k: fetch[k])
+    out = {"workload": workload, "kernel": gk, "kernel_source_hash": kernel_source_hash(),
+           "fetch_kib_per_launch": fetch[gk], "write_kib_per_launch": write.get(gk),
+           "copy_kernel": ck, "copy_bytes": copy_bytes, "copy_fetch_kib": fetch[ck], "copy_write_kib": write[ck],
+           "fetch_scale": f_scale, "write_scale": w_scale,
+           "bytes_per_launch": fetch[gk] * 1024.0 * f_scale + (write.get(gk) or 0.0) * 1024.0 * w_scale}
+    path = os.path.join(ROOT, "profiles", f"traffic_{workload}.json")
+    with open(path, "w") as f:
+        json.dump(out, f, indent=1)
+    print(json.dumps(out, indent=1))
+
+
+def cpu_baseline(name, ops, keep, target_s):
+    """The CPU fp64 oracle on a row sample of the same workload; also checks
+    the GPU's D on those rows (a bench-time parity spot check)."""
+    import numpy as np
+    import torch
+
+    import egm_workloads as W
+    from oracle import egm_oracle as eo
+
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([i.get("num_threads", 1) for i in threadpool_info() if i.get("user_api") == "blas"] or [1])
+    except Exception:  # pragma: no cover
+        cores = len(os.sched_getaffinity(0))
+    if ops is None:  # FFN chain: time the up-projection oracle on a row sample
+        f = W.ffn_operands()
+        a, b, bias, layout, epilog, dtype = f.x, f.w1, f.b1, "col", "GELU_BIAS", "bf16"
+        m, n, k = f.tokens, f.ffn, f.hidden
+        gpu_d = None
+    else:
+        a, b, bias, layout, epilog, dtype = ops.a, ops.b, ops.bias, ops.bias_layout, W.WORKLOADS[name].epilogs[-1], ops.dtype
+        m, n, k = ops.m, ops.n, ops.k
+        gpu_d = keep[3]
+    rows = W.sample_rows(m, min(m, 64), seed=2)
+    t0 = time.perf_counter()
+    eo.reference(a, b, dtype, epilog, bias, layout, rows=rows)
+    t_small = time.perf_counter() - t0
+    count = int(min(m, max(64, 64 * target_s / max(t_small, 1e-3))))
+    count = min(count, 8192)
+    rows = W.sample_rows(m, count, seed=2)
+    t0 = time.perf_counter()
+    y, _, _ = eo.reference(a, b, dtype, epilog, bias, layout, rows=rows)
+    secs = time.perf_counter() - t0
+    flops = 2.0 * len(rows) * n * k
+    out = {"value": round(flops / secs / 1e12, 4), "unit": "TFLOP/s", "cores": int(cores), "kind": "oracle",
+           "sample": f"{len(rows)} of {m} output rows x all {n} columns (k={k}), {epilog}, fp64 numpy oracle; "
+                     f"{secs:.1f} s",
+           "seconds": round(secs, 2)}
+    if gpu_d is not None:
+        sel = gpu_d.index_select(0, torch.from_numpy(rows).to(gpu_d.device)).cpu()
+        d = eo.widen(sel.view(torch.int16).numpy().view(np.uint16), dtype)
+        out["parity_max_abs_err"] = float(np.abs(d - y).max())
+        out["parity_tol"] = eo.TOLERANCE[dtype]
+    return out
+
+
+if __name__ == "__main__":
+    main()

@@ -18,7 +18,7 @@
 #include <cstring>
 #include <new>
 
-#include "../../include/egm.h"
+#include "egm.h"
 #include "egm_epilogue.hpp"
 #include "egm_gemm.hpp"
 #include "egm_launch.hpp"

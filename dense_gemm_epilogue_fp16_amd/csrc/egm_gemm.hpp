@@ -1,22 +1,27 @@
 // egm_gemm.hpp - the fused GEMM + epilogue kernel for gfx950.
 //
-// One workgroup (4 waves) computes a BM x BN tile of D = epilogue(A.B):
-//   * operand streaming: A [BM x 64] and B [64 x BN] k-slabs are read from HBM
-//     with 16-byte buffer loads (out-of-range lanes read 0, so ragged edges
-//     need no branches), staged in registers one k-slab ahead, and written to
-//     a double-buffered LDS ring.  B arrives n-contiguous; each thread
-//     transposes its 8-column unit in registers so that LDS holds B^T, i.e.
-//     both operands k-contiguous, which is what the MFMA operand layout wants.
-//     In LDS each slab is split into 4 k-slices of 16 k-values (32 bytes per
-//     row), which is exactly what one MFMA step reads: every fragment address
-//     is one per-lane base plus an immediate, and a small swizzle of the two
-//     16-byte halves spreads the reads of a wave over all banks.
+// One workgroup (4 waves, 2 x 2) computes a BM x BN tile of D = epilogue(A.B):
+//   * operand streaming: A [BM x 32] and B [32 x BN] k-slabs go from HBM
+//     straight into LDS with the gfx950 buffer-load-to-LDS instruction (16 bytes
+//     per lane, no VGPR staging); out-of-range lanes read 0, so ragged edges
+//     need no branches.  The slabs live in a ring of STAGES LDS buffers, so the
+//     loads of a slab are issued STAGES-2 slabs before the MFMAs need it.
+//   * LDS layouts: A is row-major, 64 bytes (32 k) per row, its four 16-byte
+//     chunks XOR-swizzled by row; B stays row-major as it arrives (k rows of
+//     BN values), its 16-byte chunks XOR-swizzled by k.  A fragments are read
+//     with 16-byte loads; B fragments with the gfx950 transposing LDS read
+//     (ds_read_b64_tr_b16), which hands each lane 4 consecutive k-values of one
+//     column, exactly the MFMA operand layout, so B never needs a transpose
+//     pass.
 //   * main loop: v_mfma_f32_32x32x16_{f16,bf16}, fp32 accumulators, each wave
 //     owning a (BM/2) x (BN/2) sub-tile as FM x FN blocks of 32x32.  The MFMA
-//     is fed B^T as its row operand and A as its column operand, so it
-//     produces D^T blocks: lane l then holds one row of D (l % 32) and runs of
-//     4 consecutive columns, which makes the output and residual accesses
-//     8-byte vectors and keeps one lane's mask bits in nibbles.
+//     gets B as its row operand and A as its column operand, so it produces
+//     D^T blocks: lane l holds one row of D (l % 32) and runs of 4 consecutive
+//     columns, which makes the output and residual accesses 8-byte vectors and
+//     keeps a lane's mask bits in nibbles.  Per slab: read the second k-slice
+//     while the first one's MFMAs run; one barrier (after which the next slab
+//     is complete and the oldest buffer free); refill that buffer; read the
+//     next slab's first k-slice while the second one's MFMAs run.
 //   * epilogue, in registers, on the fp32 accumulators: bias (per row or per
 //     column), then ReLU / tanh-GELU / residual add, the ReLU mask bits, one
 //     round-to-nearest-even conversion, and the store.  The product never goes
@@ -46,40 +51,40 @@ struct GemmArgs {
   int32_t group_m;
 };
 
-template <int BM_, int BN_>
+template <int BM_, int BN_, int STAGES_ = 4>
 struct TileCfg {
-  static constexpr int BM = BM_, BN = BN_, BK = 64, NT = 256;
-  static constexpr int WM = 2, WN = 2;                    // 2 x 2 waves
-  static constexpr int WTM = BM / WM, WTN = BN / WN;      // wave sub-tile
-  static constexpr int FM = WTM / 32, FN = WTN / 32;      // 32x32 blocks per wave
-  static constexpr int A_LD = BM * 8 / NT;                // 16-byte A chunks per thread per slab
-  static constexpr int KR = 8 * BN / NT;                  // k-rows in a thread's 8-column B unit
-  static constexpr int KG = BK / KR;                      // B units along k
-  // LDS layout of one operand slab: 4 k-slices of 16 k-values; slice s holds,
-  // for every row, its 16 k-values (32 bytes) of that slice.  A slice is
-  // padded by 32 bytes so that the 4 slices of one row start on different
-  // banks (16-byte writes of a row's 8 chunks by 8 lanes are conflict-free).
-  static constexpr int PAD = 32;
-  static constexpr int A_SLICE = BM * 32 + PAD, B_SLICE = BN * 32 + PAD;
-  static constexpr int A_BYTES = 4 * A_SLICE;
-  static constexpr int B_BYTES = 4 * B_SLICE;
-  static constexpr int LDS_BYTES = 2 * (A_BYTES + B_BYTES);
+  static constexpr int BM = BM_, BN = BN_, BK = 32, NT = 256, STAGES = STAGES_;
+  static constexpr int WM = 2, WN = 2;                // 2 x 2 waves
+  static constexpr int WTM = BM / WM, WTN = BN / WN;  // wave sub-tile
+  static constexpr int FM = WTM / 32, FN = WTN / 32;  // 32x32 blocks per wave
+  static constexpr int A_ROW = BK * 2;                // bytes per A row in LDS
+  static constexpr int B_ROW = BN * 2;                // bytes per B k-row in LDS
+  static constexpr int A_BYTES = BM * A_ROW;
+  static constexpr int B_BYTES = BK * B_ROW;
+  static constexpr int STAGE_BYTES = A_BYTES + B_BYTES;
+  static constexpr int LDS_BYTES = STAGES * STAGE_BYTES;
+  // one load-to-LDS instruction moves 64 lanes x 16 bytes = 1 KiB
+  static constexpr int A_DMA = A_BYTES / 1024, B_DMA = B_BYTES / 1024;
+  static constexpr int A_PW = A_DMA / 4, B_PW = B_DMA / 4;  // per wave
+  static constexpr int PW = A_PW + B_PW;
+  static constexpr int B_CHUNKS = BN / 8;                   // 16-byte chunks per B row
+  static constexpr int B_ROWS_PER_DMA = 1024 / B_ROW;
   static_assert(FM >= 1 && FN >= 1, "tile too small for 2x2 waves of 32x32 blocks");
-  static_assert(A_LD >= 1 && (BM * 8) % NT == 0, "A slab does not split over the threads");
-  static_assert(KR == 2 || KR == 4 || KR == 8, "B unit must be 2, 4 or 8 k-rows");
+  static_assert(A_DMA % 4 == 0 && B_DMA % 4 == 0, "slab must split into whole loads per wave");
+  static_assert(STAGES >= 3, "the ring needs a buffer in flight besides the two in use");
+  static_assert(LDS_BYTES <= 160 * 1024, "LDS ring exceeds 160 KiB");
 };
 
-// Inside a slice a row's two 16-byte halves (k 0-7, k 8-15) swap places when
-// bit 2 xor bit 3 of the row is set.  An MFMA operand read has lane l reading
-// half (l / 32) of row (base + l % 32): any 8 consecutive rows then cover all
-// 32 four-byte banks, and any 16 consecutive rows all 64 of a 64-bank LDS.
-__device__ __forceinline__ uint32_t half_swz(uint32_t row) { return ((row >> 2) ^ (row >> 3)) & 1u; }
+// A: the 4 chunks of a 64-byte row are XOR-ed with bits 2..3 of the row.  On
+// gfx950's 64 x 4-byte LDS banks this makes the 16-byte fragment reads (lane l
+// -> row l%32, chunk l/32) conflict-free; measured with the bank-conflict
+// counter, the other 2-bit row functions tried cost 2- to 4-way conflicts.
+__device__ __forceinline__ uint32_t a_swz(uint32_t row) { return (row >> 2) & 3u; }
 
-// byte offset of (row, 16-byte chunk c = 8 k-values) inside one operand slab
-template <int SLICE>
-__device__ __forceinline__ uint32_t lds_off(uint32_t row, uint32_t c) {
-  return (c >> 1) * SLICE + row * 32u + (((c & 1u) ^ half_swz(row)) << 4);
-}
+// B: chunk index bits 2..3 are XOR-ed with k mod 4, so the four k-rows a
+// transposing read touches at once land on different 64-byte bank groups.
+template <int B_CHUNKS>
+__device__ __forceinline__ uint32_t b_swz(uint32_t krow) { return ((krow & 3u) << 2) & (B_CHUNKS - 1); }
 
 // Workgroup -> output tile.  Workgroups are handed to the 8 XCDs round-robin
 // (bid % 8), and each XCD has its own L2: give each XCD one contiguous run of
@@ -100,156 +105,78 @@ __device__ __forceinline__ void tile_coords(int bid, int tiles_m, int tiles_n, i
   tn = in / gm;
 }
 
-template <int DT, int EPI, class C>
-__global__ void __launch_bounds__(256, 1) gemm_epilogue_kernel(GemmArgs p) {
-  __shared__ __attribute__((aligned(16))) uint8_t smem[C::LDS_BYTES];
-  uint8_t* const ldsA = smem;                      // 2 stages of A   [BM][64]
-  uint8_t* const ldsB = smem + 2 * C::A_BYTES;     // 2 stages of B^T [BN][64]
+// 16-byte global -> LDS copy per lane; lane L lands at lds + 16 L.  Written
+// as inline assembly on purpose: the compiler cannot tell which LDS bytes the
+// copy writes, and through the builtin it would make every later LDS read wait
+// for all copies in flight, which defeats the ring.  The kernel orders the
+// copies itself (explicit vmcnt waits before the barrier that publishes a slab).
+typedef int32_t i32x4 __attribute__((ext_vector_type(4)));
 
-  const int tid = threadIdx.x;
-  const int lane = tid & 63;
-  const int wave = tid >> 6;
-  const int M = p.M, N = p.N, K = p.K;
+__device__ __forceinline__ i32x4 make_srd(const void* base, uint64_t bytes) {
+  const uint64_t a = (uint64_t)(uintptr_t)base;
+  const uint32_t n = bytes > MAX_RECORDS ? MAX_RECORDS : (uint32_t)bytes;
+  return i32x4{(int32_t)(uint32_t)a, (int32_t)(uint32_t)((a >> 32) & 0xffffu), (int32_t)n, RSRC_FLAGS};
+}
 
-  int tm, tn;
-  tile_coords(blockIdx.x, p.tiles_m, p.tiles_n, p.group_m, tm, tn);
-  const int m0 = tm * C::BM;
-  const int n0 = tn * C::BN;
-  const int KT = (K + C::BK - 1) / C::BK;
+__device__ __forceinline__ void dma16(i32x4 srd, uint8_t* lds, uint32_t voff) {
+  // the LDS address is wave-uniform by construction; make that explicit for M0
+  const uint32_t lds_addr =
+      __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(__attribute__((address_space(3))) uint8_t*)lds);
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
+  // (an M0 write needs a wait state before a load-to-LDS reads it)
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 1\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
+               :
+               : "s"(lds_addr), "v"(voff), "s"(srd)
+               : "memory", "m0");
+#pragma clang diagnostic pop
+}
 
-  // ------------------------------------------------------------------ streaming setup
-  // A: thread owns chunk ac (8 k-values) of rows ar0 + 32*i.
-  const int ac = tid & 7;
-  const int ar0 = tid >> 3;
-  constexpr int AROWS = C::NT / 8;
-  const auto rA = make_rsrc((const uint8_t*)p.A + (size_t)m0 * K * 2, (uint64_t)(M - m0) * K * 2);
-  uint32_t aoff[C::A_LD];
-#pragma unroll
-  for (int i = 0; i < C::A_LD; ++i) aoff[i] = (uint32_t)(ar0 + AROWS * i) * (uint32_t)K * 2u + ac * 16u;
+// Transposing LDS read: within each 16-lane group, lane i receives element
+// (i mod 4) of the 4-element rows addressed by lanes i/4, 4 + i/4, 8 + i/4 and
+// 12 + i/4.
+template <int DT>
+__device__ __forceinline__ u32x2 lds_read_tr(const uint8_t* p) {
+  typedef __attribute__((address_space(3))) void* lds_ptr;
+  if constexpr (DT == DT_F16) {
+    typedef __fp16 h4 __attribute__((__vector_size__(4 * sizeof(__fp16))));
+    typedef __attribute__((address_space(3))) h4* hp;
+    return __builtin_bit_cast(u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4f16((hp)(lds_ptr)p));
+  } else {
+    typedef __bf16 b4 __attribute__((__vector_size__(4 * sizeof(__bf16))));
+    typedef __attribute__((address_space(3))) b4* bp;
+    return __builtin_bit_cast(u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4bf16((bp)(lds_ptr)p));
+  }
+}
 
-  // B: thread owns a KR x 8 unit: k-rows kg*KR .. +KR-1, columns n0 + cg*8 .. +7.
-  const int kg = tid % C::KG;
-  const int cg = tid / C::KG;
-  const bool bcol_ok = (n0 + cg * 8) < N;
-  const uint32_t boff = (uint32_t)(kg * C::KR) * (uint32_t)N * 2u + cg * 16u;
+// s_waitcnt vmcnt(n) with the other counters left alone (gfx9 encoding).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt is 6 bits");
+  __builtin_amdgcn_s_waitcnt((N & 0xf) | ((N >> 4) << 14) | (0x7 << 4) | (0xf << 8));
+}
 
-  u32x4 ra[C::A_LD];
-  u32x4 rb[C::KR];  // KR rows of 8 columns
-
-  auto gload = [&](int kt) {
-    const int kbase = kt * C::BK;
-    const bool ak_ok = (kbase + ac * 8) < K;
-#pragma unroll
-    for (int i = 0; i < C::A_LD; ++i)
-      ra[i] = buf_load16(rA, ak_ok ? aoff[i] + (uint32_t)kbase * 2u : OOB_OFFSET);
-    const uint64_t bstart = (uint64_t)kbase * N + n0;
-    const uint64_t bsize = (uint64_t)K * N;
-    const auto rB = make_rsrc((const uint8_t*)p.B + (bstart < bsize ? bstart : 0) * 2,
-                              bstart < bsize ? (bsize - bstart) * 2 : 0);
-#pragma unroll
-    for (int r = 0; r < C::KR; ++r)
-      rb[r] = buf_load16(rB, bcol_ok ? boff + (uint32_t)r * (uint32_t)N * 2u : OOB_OFFSET);
-  };
-
-  auto swrite = [&](uint32_t stage) {
-    uint8_t* const sa = ldsA + stage * C::A_BYTES;
-#pragma unroll
-    for (int i = 0; i < C::A_LD; ++i) {
-      const uint32_t row = ar0 + AROWS * i;
-      *(u32x4*)(sa + lds_off<C::A_SLICE>(row, ac)) = ra[i];
-    }
-    // transpose the KR x 8 unit: column c gets the KR k-values of that column
-    uint8_t* const sb = ldsB + stage * C::B_BYTES;
-#pragma unroll
-    for (int c = 0; c < 8; ++c) {
-      uint32_t w[C::KR / 2];
-#pragma unroll
-      for (int q = 0; q < C::KR / 2; ++q) {
-        const uint32_t lo = rb[2 * q][c >> 1];
-        const uint32_t hi = rb[2 * q + 1][c >> 1];
-        w[q] = (c & 1) ? ((lo >> 16) | (hi & 0xffff0000u)) : ((lo & 0xffffu) | (hi << 16));
-      }
-      const uint32_t row = cg * 8 + c;
-      if constexpr (C::KR == 8) {
-        *(u32x4*)(sb + lds_off<C::B_SLICE>(row, kg)) = u32x4{w[0], w[1], w[2], w[3]};
-      } else if constexpr (C::KR == 4) {
-        *(u32x2*)(sb + lds_off<C::B_SLICE>(row, kg >> 1) + (kg & 1) * 8) = u32x2{w[0], w[1]};
-      } else {
-        *(uint32_t*)(sb + lds_off<C::B_SLICE>(row, kg >> 2) + (kg & 3) * 4) = w[0];
-      }
-    }
-  };
-
-  // ------------------------------------------------------------------ main loop
-  const int wm0 = (wave / C::WN) * C::WTM;
-  const int wn0 = (wave % C::WN) * C::WTN;
+// ---------------------------------------------------------------------------
+// Epilogue on the fp32 accumulators of one wave, then the store.
+// lane holds D[m0 + wm0 + 32i + lr][n0 + wn0 + 32j + 8g + 4lh + e] = acc[i][j][4g + e]
+// ---------------------------------------------------------------------------
+template <int DT, int EPI, int FM, int FN>
+__device__ __forceinline__ void epilogue_store(const GemmArgs& p, f32x16 (&acc)[FM][FN], int m0, int n0, int wm0,
+                                               int wn0, int lane) {
+  const int M = p.M, N = p.N;
   const int lr = lane & 31;
   const int lh = lane >> 5;
-
-  f32x16 acc[C::FM][C::FN];
-#pragma unroll
-  for (int i = 0; i < C::FM; ++i)
-#pragma unroll
-    for (int j = 0; j < C::FN; ++j)
-#pragma unroll
-      for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.0f;
-
-  // per-lane fragment bases: row (w?0 + lr), half lh of the k-slice; block i /
-  // j and slice ks only add immediates (32*32 bytes per block, one slice each)
-  const uint32_t a_lane = (uint32_t)(wm0 + lr) * 32u + (((uint32_t)lh ^ half_swz(lr)) << 4);
-  const uint32_t b_lane = (uint32_t)(wn0 + lr) * 32u + (((uint32_t)lh ^ half_swz(lr)) << 4);
-
-  auto compute = [&](uint32_t a_base, uint32_t b_base) {
-    const uint8_t* const sa = ldsA + a_base;
-    const uint8_t* const sb = ldsB + b_base;
-#pragma unroll
-    for (int ks = 0; ks < C::BK / 16; ++ks) {
-      u32x4 af[C::FM], bf[C::FN];
-#pragma unroll
-      for (int i = 0; i < C::FM; ++i) af[i] = *(const u32x4*)(sa + ks * C::A_SLICE + i * 1024);
-#pragma unroll
-      for (int j = 0; j < C::FN; ++j) bf[j] = *(const u32x4*)(sb + ks * C::B_SLICE + j * 1024);
-#pragma unroll
-      for (int i = 0; i < C::FM; ++i)
-#pragma unroll
-        for (int j = 0; j < C::FN; ++j) acc[i][j] = mfma32<DT>(bf[j], af[i], acc[i][j]);
-    }
-  };
-
-  // Prologue: slab 0 -> LDS stage 0, slab 1 -> registers.  Steady state: write
-  // the registers (slab kt+1) to the other stage, issue the loads of slab kt+2
-  // (slabs past K read as zeros and move no data), run the MFMAs on stage kt,
-  // one barrier.  The loop body has a single path so the accumulators stay in
-  // place across iterations.
-  if (KT > 0) {
-    gload(0);
-    swrite(0);
-    gload(1);
-    __syncthreads();
-    uint32_t cur = 0;
-    for (int kt = 0; kt < KT - 1; ++kt) {
-      swrite(cur ^ 1u);
-      gload(kt + 2);
-      compute(a_lane + cur * C::A_BYTES, b_lane + cur * C::B_BYTES);
-      __syncthreads();
-      cur ^= 1u;
-    }
-    compute(a_lane + cur * C::A_BYTES, b_lane + cur * C::B_BYTES);
-  }
-
-  // ------------------------------------------------------------------ epilogue
-  // lane holds D[m0 + wm0 + 32i + lr][n0 + wn0 + 32j + 8g + 4lh + e] = acc[i][j][4g + e]
   const uint32_t rowbytes = (uint32_t)N * 2u;
   const auto rD = make_rsrc((uint8_t*)p.D + (size_t)m0 * N * 2, (uint64_t)(M - m0) * N * 2);
   const auto rR = make_rsrc(EPI == EPI_RESID ? (const uint8_t*)p.R + (size_t)m0 * N * 2 : (const uint8_t*)p.D,
                             EPI == EPI_RESID ? (uint64_t)(M - m0) * N * 2 : 0);
 
-  float bcol[C::FN][4][4];
+  float bcol[FN][4][4];
   if constexpr (EPI != EPI_NONE) {
     if (p.bias_layout == BIAS_COL) {
       const auto rbias = make_rsrc(p.bias, (uint64_t)N * 2);
 #pragma unroll
-      for (int j = 0; j < C::FN; ++j)
+      for (int j = 0; j < FN; ++j)
 #pragma unroll
         for (int g = 0; g < 4; ++g) {
           const int col = n0 + wn0 + 32 * j + 8 * g + 4 * lh;
@@ -261,7 +188,7 @@ __global__ void __launch_bounds__(256, 1) gemm_epilogue_kernel(GemmArgs p) {
         }
     } else {
 #pragma unroll
-      for (int j = 0; j < C::FN; ++j)
+      for (int j = 0; j < FN; ++j)
 #pragma unroll
         for (int g = 0; g < 4; ++g)
 #pragma unroll
@@ -270,7 +197,7 @@ __global__ void __launch_bounds__(256, 1) gemm_epilogue_kernel(GemmArgs p) {
   }
 
 #pragma unroll
-  for (int i = 0; i < C::FM; ++i) {
+  for (int i = 0; i < FM; ++i) {
     const uint32_t lrow = wm0 + 32 * i + lr;  // row within the tile
     float brow = 0.0f;
     if constexpr (EPI != EPI_NONE) {
@@ -281,7 +208,7 @@ __global__ void __launch_bounds__(256, 1) gemm_epilogue_kernel(GemmArgs p) {
       }
     }
 #pragma unroll
-    for (int j = 0; j < C::FN; ++j) {
+    for (int j = 0; j < FN; ++j) {
       uint32_t mword = 0;
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
@@ -322,14 +249,202 @@ __global__ void __launch_bounds__(256, 1) gemm_epilogue_kernel(GemmArgs p) {
 #pragma unroll
             for (int b = 0; b < 4; ++b) {
               const int c8 = cb + 8 * b;
-              buf_store1((uint8_t)(mword >> (8 * b)), rM,
-                         c8 < N ? lrow * mrow + (uint32_t)c8 / 8u : OOB_OFFSET);
+              buf_store1((uint8_t)(mword >> (8 * b)), rM, c8 < N ? lrow * mrow + (uint32_t)c8 / 8u : OOB_OFFSET);
             }
           }
         }
       }
     }
   }
+}
+
+template <int DT, int EPI, class C>
+__global__ void __launch_bounds__(256, 1) gemm_epilogue_kernel(GemmArgs p) {
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[C::LDS_BYTES];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform per wave
+  const int M = p.M, N = p.N, K = p.K;
+
+  int tm, tn;
+  tile_coords(blockIdx.x, p.tiles_m, p.tiles_n, p.group_m, tm, tn);
+  const int m0 = tm * C::BM;
+  const int n0 = tn * C::BN;
+  const int KT = (K + C::BK - 1) / C::BK;
+
+  // ------------------------------------------------------------------ streaming setup
+  // A load q (0 .. A_DMA-1) fills rows 16q .. 16q+15: lane L -> row 16q + L/4,
+  // physical chunk L%4, which holds logical chunk (L%4) ^ a_swz(row).
+  uint32_t a_off[C::A_PW], a_k8[C::A_PW];
+#pragma unroll
+  for (int u = 0; u < C::A_PW; ++u) {
+    const uint32_t q = wave * C::A_PW + u;
+    const uint32_t row = 16 * q + (lane >> 2);
+    const uint32_t lc = (lane & 3) ^ a_swz(row);
+    a_k8[u] = lc * 8;
+    a_off[u] = (row * (uint32_t)K + lc * 8) * 2u;
+  }
+  // B load q fills k-rows q*R .. q*R+R-1 (R = B_ROWS_PER_DMA): lane L -> k-row
+  // q*R + L/B_CHUNKS, physical chunk L%B_CHUNKS holding logical chunk
+  // (L%B_CHUNKS) ^ b_swz(k-row).  Columns past N read 0.
+  uint32_t b_off[C::B_PW];
+#pragma unroll
+  for (int u = 0; u < C::B_PW; ++u) {
+    const uint32_t q = wave * C::B_PW + u;
+    const uint32_t krow = q * C::B_ROWS_PER_DMA + lane / C::B_CHUNKS;
+    const uint32_t lc = (lane % C::B_CHUNKS) ^ b_swz<C::B_CHUNKS>(krow);
+    b_off[u] = (n0 + (int)lc * 8 < N) ? (krow * (uint32_t)N + lc * 8) * 2u : OOB_OFFSET;
+  }
+
+  // Load q (0 .. PW-1) of this wave for slab kt into ring buffer `stage`: the
+  // first A_PW are A loads, the rest B loads.  Slabs past K read 0 and move no
+  // data, but are still issued so every slab costs the same count of
+  // outstanding loads.
+  auto issue_one = [&](int kt, int stage, int q) {
+    const uint32_t kbase = (uint32_t)kt * C::BK;
+    uint8_t* const sa = smem + stage * C::STAGE_BYTES;
+    if (q < C::A_PW) {
+      const uint64_t a_start = (uint64_t)m0 * K + kbase, a_size = (uint64_t)M * K;
+      const i32x4 rA = make_srd((const uint8_t*)p.A + (a_start < a_size ? a_start : 0) * 2,
+                                a_start < a_size ? (a_size - a_start) * 2 : 0);
+      dma16(rA, sa + (wave * C::A_PW + q) * 1024, kbase + a_k8[q] < (uint32_t)K ? a_off[q] : OOB_OFFSET);
+    } else {
+      const int u = q - C::A_PW;
+      const uint64_t b_start = (uint64_t)kbase * N + n0, b_size = (uint64_t)K * N;
+      const i32x4 rB = make_srd((const uint8_t*)p.B + (b_start < b_size ? b_start : 0) * 2,
+                                b_start < b_size ? (b_size - b_start) * 2 : 0);
+      dma16(rB, sa + C::A_BYTES + (wave * C::B_PW + u) * 1024, b_off[u]);
+    }
+  };
+
+  // ------------------------------------------------------------------ fragments
+  const int wm0 = (wave / C::WN) * C::WTM;
+  const int wn0 = (wave % C::WN) * C::WTN;
+  const int lr = lane & 31;
+  const int lh = lane >> 5;
+
+  // A fragment of block i, k-slice ks: row wm0 + 32i + lr, logical chunk 2ks + lh.
+  // a_swz depends on row bits 1..4 only, i.e. on lr: block i adds 32*64 bytes.
+  uint32_t a_frag_off[2];
+#pragma unroll
+  for (int ks = 0; ks < 2; ++ks)
+    a_frag_off[ks] = (uint32_t)(wm0 + lr) * C::A_ROW + (((2u * ks + lh) ^ a_swz(lr)) << 4);
+  // B fragment of block j, k-slice ks, half t: within 16-lane group g = lane/16
+  // lane r = lane%16 addresses k-row 16ks + 8(g/2) + 4t + r/4 and the 4 columns
+  // wn0 + 32j + 16(g%2) + 4(r%4); the transposing read then gives lane l the
+  // k-values 16ks + 8(l/32) + 4t .. +3 of column wn0 + 32j + l%32.
+  const int g16 = lane >> 4, r16 = lane & 15;
+  uint32_t b_frag_off[2][2][C::FN];
+#pragma unroll
+  for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+    for (int t = 0; t < 2; ++t)
+#pragma unroll
+      for (int j = 0; j < C::FN; ++j) {
+        const uint32_t krow = 16 * ks + 8 * (g16 >> 1) + 4 * t + (r16 >> 2);
+        const uint32_t col = wn0 + 32 * j + 16 * (g16 & 1) + 4 * (r16 & 3);
+        b_frag_off[ks][t][j] = C::A_BYTES + krow * C::B_ROW + (((col >> 3) ^ b_swz<C::B_CHUNKS>(krow)) << 4) +
+                               (col & 4) * 2;
+      }
+
+  f32x16 acc[C::FM][C::FN];
+#pragma unroll
+  for (int i = 0; i < C::FM; ++i)
+#pragma unroll
+    for (int j = 0; j < C::FN; ++j)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.0f;
+
+  // Two fragment sets (k-slice in flight / k-slice being read).  A fragment i
+  // is one 16-byte read; B fragment j is two transposing 8-byte reads (lo: k
+  // 0..3, hi: k 4..7 of the lane's 8).  A k-slice is read as NRD "pieces".
+  constexpr int NMF = C::FM * C::FN;      // MFMAs per k-slice
+  constexpr int NRD = C::FM + 2 * C::FN;  // LDS read instructions per k-slice
+  u32x4 fa0[C::FM], fa1[C::FM];
+  u32x2 fb0[C::FN][2], fb1[C::FN][2];
+  auto read_piece = [&](u32x4 (&fa)[C::FM], u32x2 (&fb)[C::FN][2], int stage, int ks, int piece) {
+    const uint8_t* const st = smem + stage * C::STAGE_BYTES;
+    // order of first use by the MFMAs (i outer, j inner): A0, then the B
+    // halves j = 0..FN-1, then A1 .. A(FM-1)
+    if (piece == 0 || piece > 2 * C::FN) {
+      const int i = piece == 0 ? 0 : piece - 2 * C::FN;
+      fa[i] = *(const u32x4*)(st + a_frag_off[ks] + i * 32 * C::A_ROW);
+    } else {
+      const int j = (piece - 1) >> 1, t = (piece - 1) & 1;
+      fb[j][t] = lds_read_tr<DT>(st + b_frag_off[ks][t][j]);
+    }
+  };
+  auto read_frags = [&](u32x4 (&fa)[C::FM], u32x2 (&fb)[C::FN][2], int stage, int ks) {
+#pragma unroll
+    for (int q = 0; q < NRD; ++q) read_piece(fa, fb, stage, ks, q);
+  };
+  auto mfmas = [&](const u32x4 (&fa)[C::FM], const u32x2 (&fb)[C::FN][2]) {
+#pragma unroll
+    for (int i = 0; i < C::FM; ++i)
+#pragma unroll
+      for (int j = 0; j < C::FN; ++j)
+        acc[i][j] = mfma32<DT>(u32x4{fb[j][0][0], fb[j][0][1], fb[j][1][0], fb[j][1][1]}, fa[i], acc[i][j]);
+  };
+  // Scheduling hint for one half-slab: alternate the MFMAs with the LDS reads
+  // of the next k-slice so neither the MFMA pipe nor the LDS queue idles.
+  constexpr int RD_PER_MF = (NRD + NMF - 1) / NMF;
+  auto interleave = [&]() {
+#pragma unroll
+    for (int t = 0; t < NMF; ++t) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                                   // one MFMA
+      if (t * RD_PER_MF < NRD) __builtin_amdgcn_sched_group_barrier(0x100, RD_PER_MF, 0);  // LDS reads
+    }
+  };
+
+  // ------------------------------------------------------------------ main loop
+  // Ring of STAGES slabs.  Slab kt sits in buffer kt % STAGES; its loads were
+  // issued STAGES-2 slabs earlier.  Per slab:
+  //   read k-slice 1 | MFMAs of k-slice 0
+  //   wait until this wave's loads of slab kt+1 landed; barrier (slab kt+1 is
+  //     complete for every wave, and every wave is done with slab kt-1)
+  //   refill buffer (kt-1) % STAGES with slab kt+STAGES-1
+  //   read k-slice 0 of slab kt+1 | MFMAs of k-slice 1
+  if (KT > 0) {
+#pragma unroll
+    for (int s = 0; s < C::STAGES - 1; ++s)
+#pragma unroll
+      for (int q = 0; q < C::PW; ++q) issue_one(s, s, q);
+    wait_vmcnt<(C::STAGES - 2) * C::PW>();
+    __syncthreads();
+    read_frags(fa0, fb0, 0, 0);
+    int st = 0;
+    for (int kt = 0; kt < KT; ++kt) {
+      const int st_next = st + 1 == C::STAGES ? 0 : st + 1;
+      const int st_prev = st == 0 ? C::STAGES - 1 : st - 1;
+      read_frags(fa1, fb1, st, 1);
+      mfmas(fa0, fb0);
+      interleave();
+      __builtin_amdgcn_sched_barrier(0);
+      wait_vmcnt<(C::STAGES - 3) * C::PW>();
+      // a bare s_barrier: the LDS writes that matter are the copies, already
+      // waited for above, so no LDS fence (which would also stall on the
+      // k-slice reads just issued) is needed
+      __builtin_amdgcn_s_barrier();
+      // the refill loads go out one at a time between the reads of the next
+      // k-slice (and so between the MFMAs), never as a burst that would
+      // back up the address unit and stall MFMA issue
+#pragma unroll
+      for (int q = 0; q < C::PW; ++q) {
+        issue_one(kt + C::STAGES - 1, st_prev, q);
+#pragma unroll
+        for (int r = q * NRD / C::PW; r < (q + 1) * NRD / C::PW; ++r) read_piece(fa0, fb0, st_next, 0, r);
+      }
+      mfmas(fa1, fb1);
+      interleave();
+      __builtin_amdgcn_sched_barrier(0);
+      st = st_next;
+    }
+    // drain: no load may still be writing LDS when the workgroup retires
+    wait_vmcnt<0>();
+  }
+
+  epilogue_store<DT, EPI>(p, acc, m0, n0, wm0, wn0, lane);
 }
 
 }  // namespace egm
