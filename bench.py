@@ -29,7 +29,8 @@ sys.path.insert(0, ROOT)
 PEAK_TFLOPS = 2500.0      # MI355X dense fp16 / bf16 MFMA (published)
 PEAK_HBM_GBS = 8000.0     # MI355X HBM3E (published)
 DEFAULT_WORKLOAD = "gemm_relu_bias_fp16_65536x16384x16384"
-KERNEL_SOURCES = ("egm_gemm.hpp", "egm_device.hpp", "egm_epilogue.hpp", "egm_kernels.hip", "egm_api.hip")
+# device code of the fused kernel and the config table that picks its instance
+KERNEL_SOURCES = ("egm_gemm.hpp", "egm_device.hpp", "egm_kernels.hip", "egm_launch.hpp")
 
 
 def kernel_source_hash() -> str:
@@ -299,12 +300,17 @@ def cpu_baseline(name, ops, keep, target_s):
         a, b, bias, layout, epilog, dtype = ops.a, ops.b, ops.bias, ops.bias_layout, W.WORKLOADS[name].epilogs[-1], ops.dtype
         m, n, k = ops.m, ops.n, ops.k
         gpu_d = keep[3]
-    rows = W.sample_rows(m, min(m, 64), seed=2)
-    t0 = time.perf_counter()
-    eo.reference(a, b, dtype, epilog, bias, layout, rows=rows)
-    t_small = time.perf_counter() - t0
-    count = int(min(m, max(64, 64 * target_s / max(t_small, 1e-3))))
-    count = min(count, 8192)
+    # two short calibration runs give the per-row cost (the oracle also widens
+    # all of B once per call, a fixed cost); then size the timed sample
+    times = {}
+    for cnt in (64, 192):
+        rows = W.sample_rows(m, min(m, cnt), seed=2)
+        t0 = time.perf_counter()
+        eo.reference(a, b, dtype, epilog, bias, layout, rows=rows)
+        times[cnt] = time.perf_counter() - t0
+    per_row = max((times[192] - times[64]) / 128.0, 1e-6)
+    fixed = max(times[64] - 64 * per_row, 0.0)
+    count = int(min(m, 32768, max(64, (target_s - fixed) / per_row)))
     rows = W.sample_rows(m, count, seed=2)
     t0 = time.perf_counter()
     y, _, _ = eo.reference(a, b, dtype, epilog, bias, layout, rows=rows)

@@ -92,14 +92,21 @@ namespace {
 
 bool valid_plan(egm_plan_t p) { return p != nullptr && p->magic == kPlanMagic; }
 
+// tile rows per L2-sharing group actually launched
+int32_t effective_group_m(const egm_plan_s* p, int cfg) {
+  const int64_t tiles_m = (p->m + kConfigs[cfg].bm - 1) / kConfigs[cfg].bm;
+  const int64_t g = p->group_m > 0 ? p->group_m : 4;
+  return int32_t(g < tiles_m ? g : (tiles_m > 0 ? tiles_m : 1));
+}
+
 void describe(const egm_plan_s* p, char* buf, size_t len) {
   const ConfigInfo& c = kConfigs[p->config];
   snprintf(buf, len,
-           "egm m=%lld n=%lld k=%lld dtype=%s epilog=%s bias=%s path=%s tile=%dx%dx64 waves=2x2 "
-           "mfma=32x32x16 lds_stages=2 group_m=%d tiles=%lld workspace=%zu%s",
+           "egm m=%lld n=%lld k=%lld dtype=%s epilog=%s bias=%s path=%s tile=%dx%d kslab=32 waves=2x2 "
+           "mfma=32x32x16 lds_ring=4 group_m=%d tiles=%lld workspace=%zu%s",
            (long long)p->m, (long long)p->n, (long long)p->k, p->dtype == EGM_F16 ? "fp16" : "bf16",
            epilog_name(p->epilog), p->bias_layout == EGM_BIAS_ROW ? "row(m,1)" : p->bias_layout == EGM_BIAS_COL ? "col(1,n)" : "none",
-           p->fused ? "fused" : "unfused(gemm+epilogue)", c.bm, c.bn, p->group_m,
+           p->fused ? "fused" : "unfused(gemm+epilogue)", c.bm, c.bn, effective_group_m(p, p->config),
            (long long)(cdiv(p->m, c.bm) * cdiv(p->n, c.bn)), p->workspace_bytes,
            p->autotune_pending ? " autotune=pending" : "");
 }
@@ -119,8 +126,7 @@ hipError_t launch_plan(const egm_plan_s* p, int cfg, const void* A, const void* 
   g.bias_layout = p->bias_layout;
   g.tiles_m = int32_t(cdiv(p->m, c.bm));
   g.tiles_n = int32_t(cdiv(p->n, c.bn));
-  g.group_m = p->group_m > 0 ? p->group_m : 4;
-  if (g.group_m > g.tiles_m) g.group_m = g.tiles_m;
+  g.group_m = effective_group_m(p, cfg);
   const dim3 grid(uint32_t(int64_t(g.tiles_m) * g.tiles_n));
   const int epi = epi_of(p->epilog);
   const bool two_kernels = !p->fused && epi != egm::EPI_NONE;
@@ -316,8 +322,8 @@ egm_status_t egm_config_describe(int32_t config, char* buf, size_t len) {
   if (config < 0 || config >= kNumConfigs) return EGM_ERR_INVALID_VALUE;
   if (buf == nullptr || len == 0) return EGM_ERR_INVALID_VALUE;
   const ConfigInfo& c = kConfigs[config];
-  snprintf(buf, len, "tile=%dx%dx64 waves=2x2 wave_tile=%dx%d mfma=32x32x16 lds_bytes=%d", c.bm, c.bn, c.bm / 2,
-           c.bn / 2, 2 * (c.bm + c.bn) * 64 * 2);
+  snprintf(buf, len, "tile=%dx%d kslab=32 waves=2x2 wave_tile=%dx%d mfma=32x32x16 lds_ring=4 lds_bytes=%d", c.bm,
+           c.bn, c.bm / 2, c.bn / 2, 4 * (c.bm + c.bn) * 32 * 2);
   return EGM_OK;
 }
 

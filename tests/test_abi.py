@@ -180,7 +180,7 @@ def test_per_shape_choice(m, n, k, cfg):
 def test_config_table():
     n = egm.egm_num_configs()
     assert n == 5
-    assert egm.egm_config_describe(0).startswith("tile=256x256x64")
+    assert egm.egm_config_describe(0).startswith("tile=256x256 kslab=32")
     assert egm.LIB.egm_config_describe(n, ctypes.create_string_buffer(8), 8) == egm.EGM_ERR_INVALID_VALUE
 
 
