@@ -162,8 +162,18 @@ __device__ __forceinline__ void wait_vmcnt() {
 // ---------------------------------------------------------------------------
 template <int DT, int EPI, int FM, int FN>
 __device__ __forceinline__ void epilogue_store(const GemmArgs& p, f32x16 (&acc)[FM][FN], int m0, int n0, int wm0,
-                                               int wn0, int lane) {
+                                               int wn0, int lane, uint8_t* stage,
+                                               const uint8_t* bias_lds) {
   const int M = p.M, N = p.N;
+  // The packed outputs of one 32-row block-row go through this wave's private
+  // LDS stage so that D leaves as 16-byte row chunks, 4 full rows of the wave
+  // tile per store instruction (instead of 8-byte pieces of 32 rows).  Stage
+  // rows are ROWB bytes (SLOTS 8-byte slots); slot s of row r sits at slot
+  // s ^ xr(r), which makes both the 8-byte writes (32 rows, one slot each) and
+  // the 16-byte reads (whole rows) hit distinct banks.
+  constexpr int SLOTS = 8 * FN, ROWB = 8 * SLOTS, CH = SLOTS / 2;
+  constexpr int RSHIFT = ROWB >= 256 ? 0 : ROWB == 128 ? 1 : 2;  // rows sharing a 256-byte bank window
+  auto xr = [](uint32_t r) { return (r >> RSHIFT) & (SLOTS - 1); };
   const int lr = lane & 31;
   const int lh = lane >> 5;
   const uint32_t rowbytes = (uint32_t)N * 2u;
@@ -171,16 +181,15 @@ __device__ __forceinline__ void epilogue_store(const GemmArgs& p, f32x16 (&acc)[
   const auto rR = make_rsrc(EPI == EPI_RESID ? (const uint8_t*)p.R + (size_t)m0 * N * 2 : (const uint8_t*)p.D,
                             EPI == EPI_RESID ? (uint64_t)(M - m0) * N * 2 : 0);
 
+  // a (1,n) bias: the tile's BN values sit in LDS (bias_lds), by tile column
   float bcol[FN][4][4];
   if constexpr (EPI != EPI_NONE) {
     if (p.bias_layout == BIAS_COL) {
-      const auto rbias = make_rsrc(p.bias, (uint64_t)N * 2);
 #pragma unroll
       for (int j = 0; j < FN; ++j)
 #pragma unroll
         for (int g = 0; g < 4; ++g) {
-          const int col = n0 + wn0 + 32 * j + 8 * g + 4 * lh;
-          const u32x2 v = buf_load8(rbias, col < N ? (uint32_t)col * 2u : OOB_OFFSET);
+          const u32x2 v = *(const u32x2*)(bias_lds + 2 * (wn0 + 32 * j + 8 * g + 4 * lh));
           bcol[j][g][0] = lo_f32<DT>(v[0]);
           bcol[j][g][1] = hi_f32<DT>(v[0]);
           bcol[j][g][2] = lo_f32<DT>(v[1]);
@@ -195,6 +204,14 @@ __device__ __forceinline__ void epilogue_store(const GemmArgs& p, f32x16 (&acc)[
           for (int e = 0; e < 4; ++e) bcol[j][g][e] = 0.0f;
     }
   }
+  // the packed ReLU mask of a block-row: 32 rows x WTN/8 bytes, staged right
+  // after the output stage when the wave tile's mask bytes go out as one
+  // 16-byte row piece (full-width tiles with 16-byte-aligned mask rows)
+  const uint32_t mrow = (uint32_t)N / 8u;
+  uint8_t* const mstage = stage + 32 * ROWB;
+  const bool mask_rows16 = FN == 4 && n0 + wn0 + 32 * FN <= N && (mrow & 15u) == 0;
+  const auto rM = make_rsrc(EPI == EPI_RELU_AUX ? (uint8_t*)p.aux + (size_t)m0 * mrow : (uint8_t*)p.D,
+                            EPI == EPI_RELU_AUX ? (uint64_t)(M - m0) * mrow : 0);
 
 #pragma unroll
   for (int i = 0; i < FM; ++i) {
@@ -234,15 +251,16 @@ __device__ __forceinline__ void epilogue_store(const GemmArgs& p, f32x16 (&acc)[
         float y[4];
 #pragma unroll
         for (int e = 0; e < 4; ++e) y[e] = activate<EPI>(z[e]);
-        buf_store8(u32x2{pack2<DT>(y[0], y[1]), pack2<DT>(y[2], y[3])}, rD, off);
+        const uint32_t slot = (uint32_t)(8 * j + 2 * g + lh);
+        *(u32x2*)(stage + lr * ROWB + ((slot ^ xr(lr)) << 3)) = u32x2{pack2<DT>(y[0], y[1]), pack2<DT>(y[2], y[3])};
       }
       if constexpr (EPI == EPI_RELU_AUX) {
         // lanes l and l+32 hold complementary nibbles of the same row's 32 columns
         mword |= (uint32_t)__shfl_xor((int)mword, 32);
-        const uint32_t mrow = (uint32_t)N / 8u;
-        const auto rM = make_rsrc((uint8_t*)p.aux + (size_t)m0 * mrow, (uint64_t)(M - m0) * mrow);
         const int cb = n0 + wn0 + 32 * j;  // first column of the word
-        if (lh == (j & 1)) {
+        if (mask_rows16) {
+          if (lh == 0) *(uint32_t*)(mstage + lr * 16 + 4 * j) = mword;
+        } else if (lh == (j & 1)) {
           if (cb + 32 <= N && (mrow & 3u) == 0) {
             buf_store4(mword, rM, lrow * mrow + (uint32_t)cb / 8u);
           } else {
@@ -255,12 +273,32 @@ __device__ __forceinline__ void epilogue_store(const GemmArgs& p, f32x16 (&acc)[
         }
       }
     }
+    if constexpr (EPI == EPI_RELU_AUX) {
+      if (mask_rows16 && lane < 32) {
+        const u32x4 mv = *(const u32x4*)(mstage + lane * 16);
+        buf_store16(mv, rM, (wm0 + 32 * i + lane) * mrow + (uint32_t)(n0 + wn0) / 8u);
+      }
+    }
+    // the block-row is staged: write it out as 16-byte row chunks (the same
+    // wave wrote it, and a wave's LDS accesses complete in order)
+    constexpr int RPI = 1024 / ROWB;  // stage rows per 1 KiB read
+#pragma unroll
+    for (int q = 0; q < 32 / RPI; ++q) {
+      const uint32_t r = q * RPI + lane / CH, m = lane % CH;
+      const uint32_t x = xr(r);
+      u32x4 v = *(const u32x4*)(stage + r * ROWB + ((((2 * m) ^ x) >> 1) << 4));
+      if (x & 1) v = u32x4{v[2], v[3], v[0], v[1]};
+      const int col = n0 + wn0 + 8 * (int)m;
+      buf_store16(v, rD, col < N ? (wm0 + 32 * i + r) * rowbytes + (uint32_t)col * 2u : OOB_OFFSET);
+    }
   }
 }
 
 template <int DT, int EPI, class C>
 __global__ void __launch_bounds__(256, 1) gemm_epilogue_kernel(GemmArgs p) {
-  __shared__ __attribute__((aligned(1024))) uint8_t smem[C::LDS_BYTES];
+  // the k-slab ring, then the tile's bias slice
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[C::LDS_BYTES + 1024];
+  uint8_t* const bias_lds = smem + C::LDS_BYTES;
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -272,6 +310,17 @@ __global__ void __launch_bounds__(256, 1) gemm_epilogue_kernel(GemmArgs p) {
   const int m0 = tm * C::BM;
   const int n0 = tn * C::BN;
   const int KT = (K + C::BK - 1) / C::BK;
+
+  // A (1,n) bias: wave 0 copies the tile's BN values straight into LDS ahead
+  // of the operand loads (its completion is covered by the prologue's wait;
+  // lanes past BN/8 write zeros).  A (m,1) bias is read in the epilogue.
+  if constexpr (EPI != EPI_NONE) {
+    if (p.bias_layout == BIAS_COL && wave == 0) {
+      const uint32_t c = (uint32_t)n0 + 8u * (uint32_t)lane;  // n is a multiple of 8: whole 16-byte pieces
+      dma16(make_srd(p.bias, (uint64_t)N * 2), bias_lds,
+            lane < C::BN / 8 && c < (uint32_t)N ? c * 2u : OOB_OFFSET);
+    }
+  }
 
   // ------------------------------------------------------------------ streaming setup
   // A load q (0 .. A_DMA-1) fills rows 16q .. 16q+15: lane L -> row 16q + L/4,
@@ -440,11 +489,13 @@ __global__ void __launch_bounds__(256, 1) gemm_epilogue_kernel(GemmArgs p) {
       __builtin_amdgcn_sched_barrier(0);
       st = st_next;
     }
-    // drain: no load may still be writing LDS when the workgroup retires
-    wait_vmcnt<0>();
   }
 
-  epilogue_store<DT, EPI>(p, acc, m0, n0, wm0, wn0, lane);
+  // drain: no load may still be writing LDS when the workgroup retires
+  wait_vmcnt<0>();
+  // the ring is free once every wave is past its last fragment read
+  __syncthreads();
+  epilogue_store<DT, EPI>(p, acc, m0, n0, wm0, wn0, lane, smem + wave * (32 * C::WTN * 2 + 512), bias_lds);
 }
 
 }  // namespace egm
