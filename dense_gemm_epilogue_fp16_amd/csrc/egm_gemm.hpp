@@ -1,6 +1,8 @@
 // egm_gemm.hpp - the fused GEMM + epilogue kernel for gfx950.
 //
-// One workgroup (4 waves, 2 x 2) computes a BM x BN tile of D = epilogue(A.B):
+// One workgroup of WM x WN waves computes a BM x BN tile of D = epilogue(A.B)
+// (4 waves, 2 x 2, for the smaller tiles; 8 waves, 4 x 2, two per SIMD, for
+// 256 x 256, so that one wave's MFMAs issue while its partner waits):
 //   * operand streaming: A [BM x 32] and B [32 x BN] k-slabs go from HBM
 //     straight into LDS with the gfx950 buffer-load-to-LDS instruction (16 bytes
 //     per lane, no VGPR staging); out-of-range lanes read 0, so ragged edges
@@ -14,7 +16,7 @@
 //     column, exactly the MFMA operand layout, so B never needs a transpose
 //     pass.
 //   * main loop: v_mfma_f32_32x32x16_{f16,bf16}, fp32 accumulators, each wave
-//     owning a (BM/2) x (BN/2) sub-tile as FM x FN blocks of 32x32.  The MFMA
+//     owning a (BM/WM) x (BN/WN) sub-tile as FM x FN blocks of 32x32.  The MFMA
 //     gets B as its row operand and A as its column operand, so it produces
 //     D^T blocks: lane l holds one row of D (l % 32) and runs of 4 consecutive
 //     columns, which makes the output and residual accesses 8-byte vectors and
@@ -51,10 +53,11 @@ struct GemmArgs {
   int32_t group_m;
 };
 
-template <int BM_, int BN_, int STAGES_ = 4>
+template <int BM_, int BN_, int STAGES_ = 4, int WM_ = 2, int WN_ = 2>
 struct TileCfg {
-  static constexpr int BM = BM_, BN = BN_, BK = 32, NT = 256, STAGES = STAGES_;
-  static constexpr int WM = 2, WN = 2;                // 2 x 2 waves
+  static constexpr int BM = BM_, BN = BN_, BK = 32, STAGES = STAGES_;
+  static constexpr int WM = WM_, WN = WN_;            // WM x WN waves
+  static constexpr int NW = WM * WN, NT = 64 * NW;
   static constexpr int WTM = BM / WM, WTN = BN / WN;  // wave sub-tile
   static constexpr int FM = WTM / 32, FN = WTN / 32;  // 32x32 blocks per wave
   static constexpr int A_ROW = BK * 2;                // bytes per A row in LDS
@@ -65,12 +68,15 @@ struct TileCfg {
   static constexpr int LDS_BYTES = STAGES * STAGE_BYTES;
   // one load-to-LDS instruction moves 64 lanes x 16 bytes = 1 KiB
   static constexpr int A_DMA = A_BYTES / 1024, B_DMA = B_BYTES / 1024;
-  static constexpr int A_PW = A_DMA / 4, B_PW = B_DMA / 4;  // per wave
+  static constexpr int A_PW = A_DMA / NW, B_PW = B_DMA / NW;  // per wave
   static constexpr int PW = A_PW + B_PW;
   static constexpr int B_CHUNKS = BN / 8;                   // 16-byte chunks per B row
   static constexpr int B_ROWS_PER_DMA = 1024 / B_ROW;
   static_assert(FM >= 1 && FN >= 1, "tile too small for 2x2 waves of 32x32 blocks");
-  static_assert(A_DMA % 4 == 0 && B_DMA % 4 == 0, "slab must split into whole loads per wave");
+  static_assert(A_DMA % NW == 0 && B_DMA % NW == 0, "slab must split into whole loads per wave");
+  // per-wave epilogue stage: 32 rows of the wave tile in T, then 32 mask rows
+  static constexpr int EPI_STAGE = 32 * WTN * 2 + 512;
+  static_assert(NW * EPI_STAGE <= LDS_BYTES, "epilogue stages must fit in the ring");
   static_assert(STAGES >= 3, "the ring needs a buffer in flight besides the two in use");
   static_assert(LDS_BYTES <= 160 * 1024, "LDS ring exceeds 160 KiB");
 };
@@ -204,12 +210,12 @@ __device__ __forceinline__ void epilogue_store(const GemmArgs& p, f32x16 (&acc)[
           for (int e = 0; e < 4; ++e) bcol[j][g][e] = 0.0f;
     }
   }
-  // the packed ReLU mask of a block-row: 32 rows x WTN/8 bytes, staged right
-  // after the output stage when the wave tile's mask bytes go out as one
-  // 16-byte row piece (full-width tiles with 16-byte-aligned mask rows)
+  // the packed ReLU mask of a block-row: 32 rows x 4*FN bytes, staged right
+  // after the output stage when the wave tile's mask bytes of a row go out as
+  // one aligned piece (full-width wave tiles, mask rows a multiple of 4*FN)
   const uint32_t mrow = (uint32_t)N / 8u;
   uint8_t* const mstage = stage + 32 * ROWB;
-  const bool mask_rows16 = FN == 4 && n0 + wn0 + 32 * FN <= N && (mrow & 15u) == 0;
+  const bool mask_rows = n0 + wn0 + 32 * FN <= N && mrow % (4u * FN) == 0;
   const auto rM = make_rsrc(EPI == EPI_RELU_AUX ? (uint8_t*)p.aux + (size_t)m0 * mrow : (uint8_t*)p.D,
                             EPI == EPI_RELU_AUX ? (uint64_t)(M - m0) * mrow : 0);
 
@@ -258,7 +264,7 @@ __device__ __forceinline__ void epilogue_store(const GemmArgs& p, f32x16 (&acc)[
         // lanes l and l+32 hold complementary nibbles of the same row's 32 columns
         mword |= (uint32_t)__shfl_xor((int)mword, 32);
         const int cb = n0 + wn0 + 32 * j;  // first column of the word
-        if (mask_rows16) {
+        if (mask_rows) {
           if (lh == 0) *(uint32_t*)(mstage + lr * 16 + 4 * j) = mword;
         } else if (lh == (j & 1)) {
           if (cb + 32 <= N && (mrow & 3u) == 0) {
@@ -274,9 +280,15 @@ __device__ __forceinline__ void epilogue_store(const GemmArgs& p, f32x16 (&acc)[
       }
     }
     if constexpr (EPI == EPI_RELU_AUX) {
-      if (mask_rows16 && lane < 32) {
-        const u32x4 mv = *(const u32x4*)(mstage + lane * 16);
-        buf_store16(mv, rM, (wm0 + 32 * i + lane) * mrow + (uint32_t)(n0 + wn0) / 8u);
+      if (mask_rows && lane < 32) {
+        const uint32_t moff = (wm0 + 32 * i + lane) * mrow + (uint32_t)(n0 + wn0) / 8u;
+        if constexpr (FN == 4) {
+          buf_store16(*(const u32x4*)(mstage + lane * 16), rM, moff);
+        } else if constexpr (FN == 2) {
+          buf_store8(*(const u32x2*)(mstage + lane * 16), rM, moff);
+        } else {
+          buf_store4(*(const uint32_t*)(mstage + lane * 16), rM, moff);
+        }
       }
     }
     // the block-row is staged: write it out as 16-byte row chunks (the same
@@ -295,7 +307,7 @@ __device__ __forceinline__ void epilogue_store(const GemmArgs& p, f32x16 (&acc)[
 }
 
 template <int DT, int EPI, class C>
-__global__ void __launch_bounds__(256, 1) gemm_epilogue_kernel(GemmArgs p) {
+__global__ void __launch_bounds__(C::NT, 1) gemm_epilogue_kernel(GemmArgs p) {
   // the k-slab ring, then the tile's bias slice
   __shared__ __attribute__((aligned(1024))) uint8_t smem[C::LDS_BYTES + 1024];
   uint8_t* const bias_lds = smem + C::LDS_BYTES;
@@ -495,7 +507,7 @@ __global__ void __launch_bounds__(256, 1) gemm_epilogue_kernel(GemmArgs p) {
   wait_vmcnt<0>();
   // the ring is free once every wave is past its last fragment read
   __syncthreads();
-  epilogue_store<DT, EPI>(p, acc, m0, n0, wm0, wn0, lane, smem + wave * (32 * C::WTN * 2 + 512), bias_lds);
+  epilogue_store<DT, EPI>(p, acc, m0, n0, wm0, wn0, lane, smem + wave * C::EPI_STAGE, bias_lds);
 }
 
 }  // namespace egm

@@ -14,9 +14,11 @@ namespace {
 
 constexpr int DT = EGM_DTYPE;
 
-template <int EPI, int BM, int BN>
+template <int EPI, int CFG>
 void launch_gemm(dim3 grid, hipStream_t s, const GemmArgs& a) {
-  hipLaunchKernelGGL((gemm_epilogue_kernel<DT, EPI, TileCfg<BM, BN>>), grid, dim3(256), 0, s, a);
+  constexpr ConfigInfo ci = kConfigs[CFG];
+  using C = TileCfg<ci.bm, ci.bn, ci.stages, ci.wm, ci.wn>;
+  hipLaunchKernelGGL((gemm_epilogue_kernel<DT, EPI, C>), grid, dim3(C::NT), 0, s, a);
 }
 
 template <int EPI>
@@ -28,11 +30,11 @@ template <int EPI>
 GemmLaunch gemm_row(int cfg) {
   static_assert(kNumConfigs == 5, "update the launch table with the config table");
   switch (cfg) {
-    case 0: return &launch_gemm<EPI, 256, 256>;
-    case 1: return &launch_gemm<EPI, 256, 128>;
-    case 2: return &launch_gemm<EPI, 128, 256>;
-    case 3: return &launch_gemm<EPI, 128, 128>;
-    case 4: return &launch_gemm<EPI, 64, 64>;
+    case 0: return &launch_gemm<EPI, 0>;
+    case 1: return &launch_gemm<EPI, 1>;
+    case 2: return &launch_gemm<EPI, 2>;
+    case 3: return &launch_gemm<EPI, 3>;
+    case 4: return &launch_gemm<EPI, 4>;
     default: return nullptr;
   }
 }

@@ -12,17 +12,22 @@ struct GemmArgs;
 struct EpiArgs;
 
 struct ConfigInfo {
-  int bm, bn;
+  int bm, bn;      // output tile
+  int wm, wn;      // waves along m and n (the workgroup is 64 * wm * wn lanes)
+  int stages;      // LDS ring depth, in 32-deep k-slabs
   double rel_eff;  // relative per-CU MFMA efficiency, used by the shape heuristic
 };
 
-// Tile configurations (4 waves each, 2 x 2, 32x32x16 MFMA blocks, BK = 64).
+// Tile configurations: 32x32x16 MFMA blocks, 32-deep k-slabs.  The 256x256
+// tile runs 8 waves (2 per SIMD, 64x128 each) so that one wave's MFMAs can
+// issue while its SIMD partner waits on LDS reads or copies; the smaller tiles
+// run 4 waves (2 x 2).
 inline constexpr ConfigInfo kConfigs[] = {
-    {256, 256, 1.00},
-    {256, 128, 0.90},
-    {128, 256, 0.90},
-    {128, 128, 0.75},
-    {64, 64, 0.40},
+    {256, 256, 4, 2, 4, 1.00},
+    {256, 128, 2, 2, 4, 0.90},
+    {128, 256, 2, 2, 4, 0.90},
+    {128, 128, 2, 2, 4, 0.75},
+    {64, 64, 2, 2, 4, 0.40},
 };
 inline constexpr int kNumConfigs = int(sizeof(kConfigs) / sizeof(kConfigs[0]));
 
