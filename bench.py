@@ -8,6 +8,12 @@ resident in HBM: one fused GEMM + epilogue launch (for the FFN workload, the
 up- and down-projection launches).  The deliberately unfused two-kernel path
 is timed the same way in the same run for the fused-vs-unfused speedup.
 
+The large shapes run the MI355X at its board power limit, where the clock
+settles only after the first launches; so, unless given, the warm-up covers
+about 1.5 s and the timed region about 2 s of work (step counts derived from
+one probe step).  The timed region is exactly K steps; the speedup comes from
+further alternating unfused / fused legs of K steps each.
+
 Prints ONE JSON line: metric = fused TFLOP/s (value), % of the fp16/bf16 dense
 MFMA peak (roofline.frac), fused vs unfused speedup; roofline of the dominant
 kernel with its average duration from HIP events on the launch stream; and the
@@ -68,8 +74,8 @@ def algorithmic_bytes(m, n, k, epilog, bias_layout):
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--steps", type=int, default=None, help="timed steps (default: about 2 s of work)")
+    ap.add_argument("--warmup", type=int, default=None, help="untimed warm-up steps (default: about 1.5 s of work)")
     ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="target CPU time of the oracle sample")
@@ -78,6 +84,10 @@ def main():
     ap.add_argument("--ingest-pmc", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
                     help="turn two rocprofv3 --pmc runs (FETCH_SIZE, WRITE_SIZE) of this benchmark with "
                          "--copy-mib into profiles/traffic_<workload>.json, then exit")
+    ap.add_argument("--sustain", type=float, default=0.0,
+                    help="instead of the bench line: run the fused step back to back for this many seconds and "
+                         "print one JSON line per second with its throughput and the board power and clocks "
+                         "that amd-smi reports meanwhile")
     args = ap.parse_args()
     if args.ingest_pmc:
         ingest_pmc(args.workload, *args.ingest_pmc, copy_mib=args.copy_mib or 1024)
@@ -137,9 +147,11 @@ def main():
         keep += [a, b, bias, d]
         host_ops = ops
     if args.copy_mib:
-        src = torch.empty(args.copy_mib << 20, dtype=torch.uint8, device=dev)
+        # counter calibration: an elementwise pass that reads and writes
+        # exactly copy_mib MiB, under a kernel name nothing else here uses
+        src = torch.zeros(args.copy_mib << 20, dtype=torch.uint8, device=dev)
         dst = torch.empty_like(src)
-        dst.copy_(src)
+        torch.bitwise_not(src, out=dst)
         del src, dst
     torch.cuda.synchronize(dev)
     setup_s = time.time() - t_setup
@@ -175,12 +187,28 @@ def main():
         wall = time.perf_counter() - t0
         return e0.elapsed_time(e1) / steps, wall
 
-    fused_ms, fused_wall = timed(fused_plans, args.steps, args.warmup)
-    unfused_ms, _ = timed(unfused_plans, args.steps, args.warmup)
-    # fused again after the unfused leg (same step count); the two fused legs are averaged
-    fused_ms2, fused_wall2 = timed(fused_plans, args.steps, 1)
-    fused_ms = 0.5 * (fused_ms + fused_ms2)
-    fused_wall += fused_wall2
+    # step counts: from one probe step unless given
+    probe_ms, _ = timed(fused_plans, 1, 1)
+    if args.sustain > 0:
+        sustain(lambda: step(fused_plans), probe_ms, flops, args.sustain, dev, stream)
+        for mm, *_ in fused_plans + unfused_plans:
+            mm.free()
+        return
+    warmup = args.warmup if args.warmup is not None else max(3, int(1500.0 / max(probe_ms, 1e-3)))
+    steps = args.steps if args.steps is not None else max(10, int(2000.0 / max(probe_ms, 1e-3)))
+    args.warmup, args.steps = warmup, steps
+    for _ in range(warmup):
+        step(fused_plans)
+    # the timed region: exactly `steps` fused steps
+    fused_ms, fused_wall = timed(fused_plans, steps, 0)
+    # fused-vs-unfused: alternating legs of the same length after it
+    unfused_legs, fused_legs = [], [fused_ms]
+    for _ in range(2):
+        unfused_legs.append(timed(unfused_plans, steps, 1)[0])
+        if len(fused_legs) < 2:
+            fused_legs.append(timed(fused_plans, steps, 1)[0])
+    unfused_ms = sum(unfused_legs) / len(unfused_legs)
+    fused_cmp_ms = sum(fused_legs) / len(fused_legs)
 
     # per-launch roofline of the dominant kernel (the largest GEMM of the step)
     dom = max(fused_plans, key=lambda p: p[2][0] * p[2][1] * p[2][2])
@@ -215,7 +243,7 @@ def main():
                    "plan": fused_plans[0][0].describe()},
         "pct_of_mfma_peak": round(100.0 * value / PEAK_TFLOPS, 2),
         "unfused_ms_per_step": round(unfused_ms, 4),
-        "speedup_vs_unfused": round(unfused_ms / fused_ms, 4),
+        "speedup_vs_unfused": round(unfused_ms / fused_cmp_ms, 4),
         "bytes_fused_algorithmic": alg,
         "bytes_saved_by_fusion": extra,
         "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_TFLOPS, "unit": "TFLOP/s",
@@ -233,6 +261,74 @@ def main():
     for mm, *_ in fused_plans + unfused_plans:
         mm.free()
     print(json.dumps(result), flush=True)
+
+
+def _smi_sample():
+    """Board power (W) and per-XCD graphics clocks (MHz) from amd-smi, or None."""
+    import csv
+    import io
+    import re
+    import subprocess
+    try:
+        r = subprocess.run(["amd-smi", "metric", "-p", "-c", "--csv"], capture_output=True, text=True, timeout=10)
+        rows = list(csv.DictReader(io.StringIO(r.stdout)))
+    except Exception:  # pragma: no cover - tool missing or failed
+        return None
+    if not rows:
+        return None
+    row = rows[0]
+    clks = [int(v) for k, v in row.items() if k and re.fullmatch(r"gfx_\d+_clk", k) and v.isdigit()]
+    power = row.get("socket_power")
+    return {"power_w": int(power) if power and power.isdigit() else None, "gfx_clk_mhz": clks}
+
+
+def sustain(run_step, probe_ms, flops, seconds, dev, stream):
+    """Back-to-back fused steps for `seconds`, in windows of about one second,
+    each timed with HIP events on the launch stream; amd-smi is sampled in a
+    side thread.  Shows where the board's power limit settles the clock."""
+    import threading
+
+    import torch
+    samples = []
+    stop = threading.Event()
+
+    def sampler():
+        while not stop.is_set():
+            smp = _smi_sample()
+            if smp is not None:
+                samples.append((time.perf_counter(), smp))
+            stop.wait(0.5)
+
+    th = threading.Thread(target=sampler, daemon=True)
+    th.start()
+    per_window = max(1, int(1000.0 / max(probe_ms, 1e-3)))
+    t_start = time.perf_counter()
+    while time.perf_counter() - t_start < seconds:
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        w0 = time.perf_counter()
+        e0.record(stream)
+        for _ in range(per_window):
+            run_step()
+        e1.record(stream)
+        torch.cuda.synchronize(dev)
+        w1 = time.perf_counter()
+        ms = e0.elapsed_time(e1) / per_window
+        inwin = [smp for (ts, smp) in samples if w0 <= ts <= w1]
+        line = {"t_s": round(w1 - t_start, 2), "steps": per_window, "ms_per_step": round(ms, 4),
+                "tflops": round(flops / (ms * 1e-3) / 1e12, 1)}
+        if inwin:
+            pw = [smp["power_w"] for smp in inwin if smp["power_w"] is not None]
+            clk = [c for smp in inwin for c in smp["gfx_clk_mhz"]]
+            line["power_w"] = round(sum(pw) / len(pw)) if pw else None
+            line["gfx_clk_mhz_mean"] = round(sum(clk) / len(clk)) if clk else None
+            line["gfx_clk_mhz_range"] = [min(clk), max(clk)] if clk else None
+        print(json.dumps(line), flush=True)
+    stop.set()
+    th.join(timeout=15)
+    idle = _smi_sample()
+    if idle is not None:
+        print(json.dumps({"after_run": idle}), flush=True)
 
 
 def _pmc_per_kernel(directory, counter):
@@ -253,11 +349,13 @@ def _pmc_per_kernel(directory, counter):
 
 def ingest_pmc(workload, fetch_dir, write_dir, copy_mib):
     """HBM bytes per launch of the dominant kernel: FETCH_SIZE and WRITE_SIZE
-    (KiB per dispatch) scaled by what the same counters read for a plain copy
-    of copy_mib MiB (which moves exactly that many bytes each way)."""
+    (KiB per dispatch) scaled by what the same counters read for the
+    calibration pass over copy_mib MiB (an elementwise bitwise-not, which
+    reads and writes exactly that many bytes; host-to-device copies of the
+    inputs use other kernels)."""
     fetch = _pmc_per_kernel(fetch_dir, "FETCH_SIZE")
     write = _pmc_per_kernel(write_dir, "WRITE_SIZE")
-    copy_k = [k for k in fetch if "copy" in k.lower() or "elementwise" in k.lower()]
+    copy_k = [k for k in fetch if "bitwise_not" in k]
     gemm_k = [k for k in fetch if "gemm_epilogue_kernel" in k]
     if not copy_k or not gemm_k:
         raise SystemExit(f"kernels not found: {sorted(fetch)}")
