@@ -84,6 +84,9 @@ def main():
     ap.add_argument("--ingest-pmc", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
                     help="turn two rocprofv3 --pmc runs (FETCH_SIZE, WRITE_SIZE) of this benchmark with "
                          "--copy-mib into profiles/traffic_<workload>.json, then exit")
+    ap.add_argument("--cold", action="store_true",
+                    help="also time single steps with the caches flushed (a 512 MiB write between steps, outside "
+                         "the events), and the host-side latency of one launch plus synchronize")
     ap.add_argument("--sustain", type=float, default=0.0,
                     help="instead of the bench line: run the fused step back to back for this many seconds and "
                          "print one JSON line per second with its throughput and the board power and clocks "
@@ -255,12 +258,56 @@ def main():
         "timed_wall_s": round(fused_wall, 3),
     }
 
+    if args.cold:
+        result["cold_cache"] = cold_and_latency(lambda: step(fused_plans), lambda: step(unfused_plans),
+                                                flops, alg, dev, stream)
+
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(name, host_ops, keep, args.cpu_seconds)
 
     for mm, *_ in fused_plans + unfused_plans:
         mm.free()
     print(json.dumps(result), flush=True)
+
+
+def cold_and_latency(run_fused, run_unfused, flops, alg_bytes, dev, stream, reps=30):
+    """Median single-step GPU time (HIP events) with L2 and MALL flushed before
+    every step by a 512 MiB write outside the events, for the fused and the
+    unfused path; and the median host time of one fused launch followed by a
+    synchronize (warm), which includes the launch overhead."""
+    import statistics
+
+    import torch
+    flush = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
+
+    def one(run, cold):
+        if cold:
+            flush.fill_(1)
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        run()
+        e1.record(stream)
+        torch.cuda.synchronize(dev)
+        return e0.elapsed_time(e1)
+
+    out = {}
+    for label, run in (("fused", run_fused), ("unfused", run_unfused)):
+        one(run, True)
+        ms = statistics.median(one(run, True) for _ in range(reps))
+        out[f"{label}_ms"] = round(ms, 5)
+    out["fused_tflops"] = round(flops / (out["fused_ms"] * 1e-3) / 1e12, 2)
+    out["fused_algorithmic_gbs"] = round(alg_bytes / (out["fused_ms"] * 1e-3) / 1e9, 1)
+    out["speedup_vs_unfused"] = round(out["unfused_ms"] / out["fused_ms"], 4)
+    lat = []
+    for _ in range(reps):
+        t0 = time.perf_counter()
+        run_fused()
+        torch.cuda.synchronize(dev)
+        lat.append(time.perf_counter() - t0)
+    out["single_shot_fused_us"] = round(statistics.median(lat) * 1e6, 1)
+    del flush
+    return out
 
 
 def _smi_sample():
@@ -414,7 +461,14 @@ def cpu_baseline(name, ops, keep, target_s):
     y, _, _ = eo.reference(a, b, dtype, epilog, bias, layout, rows=rows)
     secs = time.perf_counter() - t0
     flops = 2.0 * len(rows) * n * k
+    cpu_model = None
+    try:
+        with open("/proc/cpuinfo") as f:
+            cpu_model = next((ln.split(":", 1)[1].strip() for ln in f if ln.startswith("model name")), None)
+    except OSError:  # pragma: no cover
+        pass
     out = {"value": round(flops / secs / 1e12, 4), "unit": "TFLOP/s", "cores": int(cores), "kind": "oracle",
+           "cpu": cpu_model, "full_workload_seconds_extrapolated": round(secs * m / len(rows), 1),
            "sample": f"{len(rows)} of {m} output rows x all {n} columns (k={k}), {epilog}, fp64 numpy oracle; "
                      f"{secs:.1f} s",
            "seconds": round(secs, 2)}
