@@ -102,11 +102,11 @@ int32_t effective_group_m(const egm_plan_s* p, int cfg) {
 void describe(const egm_plan_s* p, char* buf, size_t len) {
   const ConfigInfo& c = kConfigs[p->config];
   snprintf(buf, len,
-           "egm m=%lld n=%lld k=%lld dtype=%s epilog=%s bias=%s path=%s tile=%dx%d kslab=32 waves=%dx%d "
+           "egm m=%lld n=%lld k=%lld dtype=%s epilog=%s bias=%s path=%s tile=%dx%d kslab=%d waves=%dx%d "
            "mfma=32x32x16 lds_ring=%d group_m=%d tiles=%lld workspace=%zu%s",
            (long long)p->m, (long long)p->n, (long long)p->k, p->dtype == EGM_F16 ? "fp16" : "bf16",
            epilog_name(p->epilog), p->bias_layout == EGM_BIAS_ROW ? "row(m,1)" : p->bias_layout == EGM_BIAS_COL ? "col(1,n)" : "none",
-           p->fused ? "fused" : "unfused(gemm+epilogue)", c.bm, c.bn, c.wm, c.wn, c.stages, effective_group_m(p, p->config),
+           p->fused ? "fused" : "unfused(gemm+epilogue)", c.bm, c.bn, c.bk, c.wm, c.wn, c.stages, effective_group_m(p, p->config),
            (long long)(cdiv(p->m, c.bm) * cdiv(p->n, c.bn)), p->workspace_bytes,
            p->autotune_pending ? " autotune=pending" : "");
 }
@@ -322,8 +322,8 @@ egm_status_t egm_config_describe(int32_t config, char* buf, size_t len) {
   if (config < 0 || config >= kNumConfigs) return EGM_ERR_INVALID_VALUE;
   if (buf == nullptr || len == 0) return EGM_ERR_INVALID_VALUE;
   const ConfigInfo& c = kConfigs[config];
-  snprintf(buf, len, "tile=%dx%d kslab=32 waves=%dx%d wave_tile=%dx%d mfma=32x32x16 lds_ring=%d lds_bytes=%d", c.bm,
-           c.bn, c.wm, c.wn, c.bm / c.wm, c.bn / c.wn, c.stages, c.stages * (c.bm + c.bn) * 32 * 2);
+  snprintf(buf, len, "tile=%dx%d kslab=%d waves=%dx%d wave_tile=%dx%d mfma=32x32x16 lds_ring=%d lds_bytes=%d", c.bm,
+           c.bn, c.bk, c.wm, c.wn, c.bm / c.wm, c.bn / c.wn, c.stages, c.stages * (c.bm + c.bn) * c.bk * 2);
   return EGM_OK;
 }
 

@@ -3,14 +3,15 @@
 // One workgroup of WM x WN waves computes a BM x BN tile of D = epilogue(A.B)
 // (4 waves, 2 x 2, for the smaller tiles; 8 waves, 4 x 2, two per SIMD, for
 // 256 x 256, so that one wave's MFMAs issue while its partner waits):
-//   * operand streaming: A [BM x 32] and B [32 x BN] k-slabs go from HBM
+//   * operand streaming: A [BM x BK] and B [BK x BN] k-slabs go from HBM
 //     straight into LDS with the gfx950 buffer-load-to-LDS instruction (16 bytes
 //     per lane, no VGPR staging); out-of-range lanes read 0, so ragged edges
-//     need no branches.  The slabs live in a ring of STAGES LDS buffers, so the
-//     loads of a slab are issued STAGES-2 slabs before the MFMAs need it.
-//   * LDS layouts: A is row-major, 64 bytes (32 k) per row, its four 16-byte
-//     chunks XOR-swizzled by row; B stays row-major as it arrives (k rows of
-//     BN values), its 16-byte chunks XOR-swizzled by k.  A fragments are read
+//     need no branches.  The slabs live in a ring of STAGES LDS buffers: a
+//     buffer is refilled as soon as every wave has finished reading it, so a
+//     slab's loads are issued STAGES-1 slabs before its MFMAs.
+//   * LDS layouts: A is row-major, 2*BK bytes per row, its 16-byte chunks
+//     XOR-swizzled by row; B stays row-major as it arrives (k rows of BN
+//     values), its 16-byte chunks XOR-swizzled by k.  A fragments are read
 //     with 16-byte loads; B fragments with the gfx950 transposing LDS read
 //     (ds_read_b64_tr_b16), which hands each lane 4 consecutive k-values of one
 //     column, exactly the MFMA operand layout, so B never needs a transpose
@@ -20,10 +21,11 @@
 //     gets B as its row operand and A as its column operand, so it produces
 //     D^T blocks: lane l holds one row of D (l % 32) and runs of 4 consecutive
 //     columns, which makes the output and residual accesses 8-byte vectors and
-//     keeps a lane's mask bits in nibbles.  Per slab: read the second k-slice
-//     while the first one's MFMAs run; one barrier (after which the next slab
-//     is complete and the oldest buffer free); refill that buffer; read the
-//     next slab's first k-slice while the second one's MFMAs run.
+//     keeps a lane's mask bits in nibbles.  A slab is BK/16 k-slices; each
+//     slice's fragments are read while the previous slice's MFMAs run.  After
+//     the last slice's reads: one barrier (the next slab is complete and this
+//     buffer free), the refill of this buffer, and the next slab's first-slice
+//     reads while the last slice's MFMAs run.
 //   * epilogue, in registers, on the fp32 accumulators: bias (per row or per
 //     column), then ReLU / tanh-GELU / residual add, the ReLU mask bits, one
 //     round-to-nearest-even conversion, and the store.  The product never goes
@@ -53,14 +55,16 @@ struct GemmArgs {
   int32_t group_m;
 };
 
-template <int BM_, int BN_, int STAGES_ = 4, int WM_ = 2, int WN_ = 2>
+template <int BM_, int BN_, int STAGES_ = 4, int WM_ = 2, int WN_ = 2, int BK_ = 32>
 struct TileCfg {
-  static constexpr int BM = BM_, BN = BN_, BK = 32, STAGES = STAGES_;
+  static constexpr int BM = BM_, BN = BN_, BK = BK_, STAGES = STAGES_;
   static constexpr int WM = WM_, WN = WN_;            // WM x WN waves
   static constexpr int NW = WM * WN, NT = 64 * NW;
   static constexpr int WTM = BM / WM, WTN = BN / WN;  // wave sub-tile
   static constexpr int FM = WTM / 32, FN = WTN / 32;  // 32x32 blocks per wave
+  static constexpr int NS = BK / 16;                  // 16-deep k-slices per slab
   static constexpr int A_ROW = BK * 2;                // bytes per A row in LDS
+  static constexpr int A_CHUNKS = A_ROW / 16;         // 16-byte chunks per A row
   static constexpr int B_ROW = BN * 2;                // bytes per B k-row in LDS
   static constexpr int A_BYTES = BM * A_ROW;
   static constexpr int B_BYTES = BK * B_ROW;
@@ -70,22 +74,32 @@ struct TileCfg {
   static constexpr int A_DMA = A_BYTES / 1024, B_DMA = B_BYTES / 1024;
   static constexpr int A_PW = A_DMA / NW, B_PW = B_DMA / NW;  // per wave
   static constexpr int PW = A_PW + B_PW;
+  static constexpr int A_ROWS_PER_DMA = 1024 / A_ROW;
   static constexpr int B_CHUNKS = BN / 8;                   // 16-byte chunks per B row
   static constexpr int B_ROWS_PER_DMA = 1024 / B_ROW;
-  static_assert(FM >= 1 && FN >= 1, "tile too small for 2x2 waves of 32x32 blocks");
+  static_assert(FM >= 1 && FN >= 1, "tile too small for the wave grid of 32x32 blocks");
+  static_assert(BK == 32 || BK == 64, "slabs are 32 or 64 deep");
   static_assert(A_DMA % NW == 0 && B_DMA % NW == 0, "slab must split into whole loads per wave");
+  static_assert((STAGES - 1) * PW < 64, "outstanding loads must fit the 6-bit vmcnt");
   // per-wave epilogue stage: 32 rows of the wave tile in T, then 32 mask rows
   static constexpr int EPI_STAGE = 32 * WTN * 2 + 512;
   static_assert(NW * EPI_STAGE <= LDS_BYTES, "epilogue stages must fit in the ring");
-  static_assert(STAGES >= 3, "the ring needs a buffer in flight besides the two in use");
-  static_assert(LDS_BYTES <= 160 * 1024, "LDS ring exceeds 160 KiB");
+  static_assert(STAGES >= 2, "the ring needs a buffer being filled besides the one being read");
+  static_assert(LDS_BYTES + 1024 <= 160 * 1024, "LDS ring exceeds 160 KiB");
 };
 
-// A: the 4 chunks of a 64-byte row are XOR-ed with bits 2..3 of the row.  On
-// gfx950's 64 x 4-byte LDS banks this makes the 16-byte fragment reads (lane l
-// -> row l%32, chunk l/32) conflict-free; measured with the bank-conflict
-// counter, the other 2-bit row functions tried cost 2- to 4-way conflicts.
-__device__ __forceinline__ uint32_t a_swz(uint32_t row) { return (row >> 2) & 3u; }
+// A: the 16-byte chunks of an A row are XOR-ed with row bits, so that the
+// 16-byte fragment reads (16 lanes at a time: consecutive rows, one logical
+// chunk) cover all 64 4-byte banks.  64-byte rows (4 chunks): rows r and r+4
+// share banks, so the chunk is XOR-ed with bits 2..3; 128-byte rows (8
+// chunks): rows r and r+2 share banks, so bits 1..3.  Measured with the
+// bank-conflict counter for the 4-chunk case, the other 2-bit row functions
+// tried cost 2- to 4-way conflicts.
+template <int A_CHUNKS>
+__device__ __forceinline__ uint32_t a_swz(uint32_t row) {
+  if constexpr (A_CHUNKS == 4) return (row >> 2) & 3u;
+  else return (row >> 1) & 7u;
+}
 
 // B: chunk index bits 2..3 are XOR-ed with k mod 4, so the four k-rows a
 // transposing read touches at once land on different 64-byte bank groups.
@@ -153,6 +167,13 @@ __device__ __forceinline__ u32x2 lds_read_tr(const uint8_t* p) {
     typedef __attribute__((address_space(3))) b4* bp;
     return __builtin_bit_cast(u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4bf16((bp)(lds_ptr)p));
   }
+}
+
+// s_waitcnt lgkmcnt(n) with the other counters left alone (gfx9 encoding).
+template <int N>
+__device__ __forceinline__ void wait_lgkmcnt() {
+  static_assert(N >= 0 && N < 16, "lgkmcnt is 4 bits");
+  __builtin_amdgcn_s_waitcnt(0xf | (0x7 << 4) | (N << 8) | (0x3 << 14));
 }
 
 // s_waitcnt vmcnt(n) with the other counters left alone (gfx9 encoding).
@@ -335,20 +356,23 @@ __global__ void __launch_bounds__(C::NT, 1) gemm_epilogue_kernel(GemmArgs p) {
   }
 
   // ------------------------------------------------------------------ streaming setup
-  // A load q (0 .. A_DMA-1) fills rows 16q .. 16q+15: lane L -> row 16q + L/4,
-  // physical chunk L%4, which holds logical chunk (L%4) ^ a_swz(row).
+  // A load q (0 .. A_DMA-1) fills rows R*q .. R*q+R-1 (R = A_ROWS_PER_DMA):
+  // lane L -> row R*q + L/A_CHUNKS, physical chunk L%A_CHUNKS, which holds
+  // logical chunk (L%A_CHUNKS) ^ a_swz(row).  Offsets are relative to the
+  // slab's first column; columns past K read 0.
   uint32_t a_off[C::A_PW], a_k8[C::A_PW];
 #pragma unroll
   for (int u = 0; u < C::A_PW; ++u) {
     const uint32_t q = wave * C::A_PW + u;
-    const uint32_t row = 16 * q + (lane >> 2);
-    const uint32_t lc = (lane & 3) ^ a_swz(row);
+    const uint32_t row = C::A_ROWS_PER_DMA * q + lane / C::A_CHUNKS;
+    const uint32_t lc = (lane % C::A_CHUNKS) ^ a_swz<C::A_CHUNKS>(row);
     a_k8[u] = lc * 8;
     a_off[u] = (row * (uint32_t)K + lc * 8) * 2u;
   }
   // B load q fills k-rows q*R .. q*R+R-1 (R = B_ROWS_PER_DMA): lane L -> k-row
   // q*R + L/B_CHUNKS, physical chunk L%B_CHUNKS holding logical chunk
-  // (L%B_CHUNKS) ^ b_swz(k-row).  Columns past N read 0.
+  // (L%B_CHUNKS) ^ b_swz(k-row).  Columns past N read 0; k-rows past K fall
+  // outside the slab's buffer range and read 0.
   uint32_t b_off[C::B_PW];
 #pragma unroll
   for (int u = 0; u < C::B_PW; ++u) {
@@ -358,24 +382,34 @@ __global__ void __launch_bounds__(C::NT, 1) gemm_epilogue_kernel(GemmArgs p) {
     b_off[u] = (n0 + (int)lc * 8 < N) ? (krow * (uint32_t)N + lc * 8) * 2u : OOB_OFFSET;
   }
 
-  // Load q (0 .. PW-1) of this wave for slab kt into ring buffer `stage`: the
-  // first A_PW are A loads, the rest B loads.  Slabs past K read 0 and move no
-  // data, but are still issued so every slab costs the same count of
-  // outstanding loads.
-  auto issue_one = [&](int kt, int stage, int q) {
-    const uint32_t kbase = (uint32_t)kt * C::BK;
+  // Buffer ranges of slab kt (uniform: computed once per slab): A from
+  // (m0, kbase) to the end of A, B from (kbase, n0) to the end of B.  Slabs
+  // past K get empty ranges: their loads move no data but still count as
+  // outstanding, so every slab costs the same vmcnt.
+  struct SlabSrd {
+    i32x4 a, b;
+    uint32_t kbase;
+  };
+  auto slab_srd = [&](int kt) {
+    SlabSrd r;
+    r.kbase = (uint32_t)kt * C::BK;
+    const uint64_t a_start = (uint64_t)m0 * K + r.kbase, a_size = (uint64_t)M * K;
+    r.a = make_srd((const uint8_t*)p.A + (a_start < a_size ? a_start : 0) * 2,
+                   a_start < a_size && r.kbase < (uint32_t)K ? (a_size - a_start) * 2 : 0);
+    const uint64_t b_start = (uint64_t)r.kbase * N + n0, b_size = (uint64_t)K * N;
+    r.b = make_srd((const uint8_t*)p.B + (b_start < b_size ? b_start : 0) * 2,
+                   b_start < b_size ? (b_size - b_start) * 2 : 0);
+    return r;
+  };
+  // Load q (0 .. PW-1) of this wave for a slab into ring buffer `stage`: the
+  // first A_PW are A loads, the rest B loads.
+  auto issue_one = [&](const SlabSrd& r, int stage, int q) {
     uint8_t* const sa = smem + stage * C::STAGE_BYTES;
     if (q < C::A_PW) {
-      const uint64_t a_start = (uint64_t)m0 * K + kbase, a_size = (uint64_t)M * K;
-      const i32x4 rA = make_srd((const uint8_t*)p.A + (a_start < a_size ? a_start : 0) * 2,
-                                a_start < a_size ? (a_size - a_start) * 2 : 0);
-      dma16(rA, sa + (wave * C::A_PW + q) * 1024, kbase + a_k8[q] < (uint32_t)K ? a_off[q] : OOB_OFFSET);
+      dma16(r.a, sa + (wave * C::A_PW + q) * 1024, r.kbase + a_k8[q] < (uint32_t)K ? a_off[q] : OOB_OFFSET);
     } else {
       const int u = q - C::A_PW;
-      const uint64_t b_start = (uint64_t)kbase * N + n0, b_size = (uint64_t)K * N;
-      const i32x4 rB = make_srd((const uint8_t*)p.B + (b_start < b_size ? b_start : 0) * 2,
-                                b_start < b_size ? (b_size - b_start) * 2 : 0);
-      dma16(rB, sa + C::A_BYTES + (wave * C::B_PW + u) * 1024, b_off[u]);
+      dma16(r.b, sa + C::A_BYTES + (wave * C::B_PW + u) * 1024, b_off[u]);
     }
   };
 
@@ -385,29 +419,29 @@ __global__ void __launch_bounds__(C::NT, 1) gemm_epilogue_kernel(GemmArgs p) {
   const int lr = lane & 31;
   const int lh = lane >> 5;
 
-  // A fragment of block i, k-slice ks: row wm0 + 32i + lr, logical chunk 2ks + lh.
-  // a_swz depends on row bits 1..4 only, i.e. on lr: block i adds 32*64 bytes.
-  uint32_t a_frag_off[2];
+  // A fragment of block i, k-slice ks: row wm0 + 32i + lr, logical chunk
+  // 2ks + lh.  a_swz depends on row bits 1..4 only, i.e. on lr: block i adds
+  // 32 rows.
+  uint32_t a_frag_off[C::NS];
 #pragma unroll
-  for (int ks = 0; ks < 2; ++ks)
-    a_frag_off[ks] = (uint32_t)(wm0 + lr) * C::A_ROW + (((2u * ks + lh) ^ a_swz(lr)) << 4);
-  // B fragment of block j, k-slice ks, half t: within 16-lane group g = lane/16
-  // lane r = lane%16 addresses k-row 16ks + 8(g/2) + 4t + r/4 and the 4 columns
-  // wn0 + 32j + 16(g%2) + 4(r%4); the transposing read then gives lane l the
-  // k-values 16ks + 8(l/32) + 4t .. +3 of column wn0 + 32j + l%32.
+  for (int ks = 0; ks < C::NS; ++ks)
+    a_frag_off[ks] = (uint32_t)(wm0 + lr) * C::A_ROW + (((2u * ks + lh) ^ a_swz<C::A_CHUNKS>(lr)) << 4);
+  // B fragment of block j, half t (k-slice 0; slice ks adds 16 k-rows, which
+  // leaves b_swz unchanged): within 16-lane group g = lane/16 lane r = lane%16
+  // addresses k-row 8(g/2) + 4t + r/4 and the 4 columns wn0 + 32j + 16(g%2) +
+  // 4(r%4); the transposing read then gives lane l the k-values
+  // 16ks + 8(l/32) + 4t .. +3 of column wn0 + 32j + l%32.
   const int g16 = lane >> 4, r16 = lane & 15;
-  uint32_t b_frag_off[2][2][C::FN];
+  uint32_t b_frag_off[2][C::FN];
 #pragma unroll
-  for (int ks = 0; ks < 2; ++ks)
+  for (int t = 0; t < 2; ++t)
 #pragma unroll
-    for (int t = 0; t < 2; ++t)
-#pragma unroll
-      for (int j = 0; j < C::FN; ++j) {
-        const uint32_t krow = 16 * ks + 8 * (g16 >> 1) + 4 * t + (r16 >> 2);
-        const uint32_t col = wn0 + 32 * j + 16 * (g16 & 1) + 4 * (r16 & 3);
-        b_frag_off[ks][t][j] = C::A_BYTES + krow * C::B_ROW + (((col >> 3) ^ b_swz<C::B_CHUNKS>(krow)) << 4) +
-                               (col & 4) * 2;
-      }
+    for (int j = 0; j < C::FN; ++j) {
+      const uint32_t krow = 8 * (g16 >> 1) + 4 * t + (r16 >> 2);
+      const uint32_t col = wn0 + 32 * j + 16 * (g16 & 1) + 4 * (r16 & 3);
+      b_frag_off[t][j] = C::A_BYTES + krow * C::B_ROW + (((col >> 3) ^ b_swz<C::B_CHUNKS>(krow)) << 4) +
+                         (col & 4) * 2;
+    }
 
   f32x16 acc[C::FM][C::FN];
 #pragma unroll
@@ -417,38 +451,41 @@ __global__ void __launch_bounds__(C::NT, 1) gemm_epilogue_kernel(GemmArgs p) {
 #pragma unroll
       for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.0f;
 
-  // Two fragment sets (k-slice in flight / k-slice being read).  A fragment i
-  // is one 16-byte read; B fragment j is two transposing 8-byte reads (lo: k
-  // 0..3, hi: k 4..7 of the lane's 8).  A k-slice is read as NRD "pieces".
+  // Two fragment sets (k-slice being computed / k-slice being read).  A
+  // fragment i is one 16-byte read; B fragment j is two transposing 8-byte
+  // reads (lo: k 0..3, hi: k 4..7 of the lane's 8).  A k-slice is read as NRD
+  // "pieces".
   constexpr int NMF = C::FM * C::FN;      // MFMAs per k-slice
   constexpr int NRD = C::FM + 2 * C::FN;  // LDS read instructions per k-slice
-  u32x4 fa0[C::FM], fa1[C::FM];
-  u32x2 fb0[C::FN][2], fb1[C::FN][2];
-  auto read_piece = [&](u32x4 (&fa)[C::FM], u32x2 (&fb)[C::FN][2], int stage, int ks, int piece) {
+  u32x4 fa[2][C::FM];
+  u32x2 fb[2][C::FN][2];
+  auto read_piece = [&](int set, int stage, int ks, int piece) {
     const uint8_t* const st = smem + stage * C::STAGE_BYTES;
     // order of first use by the MFMAs (i outer, j inner): A0, then the B
     // halves j = 0..FN-1, then A1 .. A(FM-1)
     if (piece == 0 || piece > 2 * C::FN) {
       const int i = piece == 0 ? 0 : piece - 2 * C::FN;
-      fa[i] = *(const u32x4*)(st + a_frag_off[ks] + i * 32 * C::A_ROW);
+      fa[set][i] = *(const u32x4*)(st + a_frag_off[ks] + i * 32 * C::A_ROW);
     } else {
       const int j = (piece - 1) >> 1, t = (piece - 1) & 1;
-      fb[j][t] = lds_read_tr<DT>(st + b_frag_off[ks][t][j]);
+      fb[set][j][t] = lds_read_tr<DT>(st + b_frag_off[t][j] + ks * 16 * C::B_ROW);
     }
   };
-  auto read_frags = [&](u32x4 (&fa)[C::FM], u32x2 (&fb)[C::FN][2], int stage, int ks) {
+  auto read_slice = [&](int set, int stage, int ks) {
 #pragma unroll
-    for (int q = 0; q < NRD; ++q) read_piece(fa, fb, stage, ks, q);
+    for (int q = 0; q < NRD; ++q) read_piece(set, stage, ks, q);
   };
-  auto mfmas = [&](const u32x4 (&fa)[C::FM], const u32x2 (&fb)[C::FN][2]) {
+  auto mfmas = [&](int set) {
 #pragma unroll
     for (int i = 0; i < C::FM; ++i)
 #pragma unroll
       for (int j = 0; j < C::FN; ++j)
-        acc[i][j] = mfma32<DT>(u32x4{fb[j][0][0], fb[j][0][1], fb[j][1][0], fb[j][1][1]}, fa[i], acc[i][j]);
+        acc[i][j] = mfma32<DT>(u32x4{fb[set][j][0][0], fb[set][j][0][1], fb[set][j][1][0], fb[set][j][1][1]},
+                               fa[set][i], acc[i][j]);
   };
-  // Scheduling hint for one half-slab: alternate the MFMAs with the LDS reads
-  // of the next k-slice so neither the MFMA pipe nor the LDS queue idles.
+  // Scheduling hint for one k-slice: alternate the MFMAs with the LDS reads
+  // of the next k-slice, reads first, so neither the MFMA pipe nor the LDS
+  // queue idles and the reads land well before the slice ends.
   constexpr int RD_PER_MF = (NRD + NMF - 1) / NMF;
   auto interleave = [&]() {
 #pragma unroll
@@ -459,44 +496,54 @@ __global__ void __launch_bounds__(C::NT, 1) gemm_epilogue_kernel(GemmArgs p) {
   };
 
   // ------------------------------------------------------------------ main loop
-  // Ring of STAGES slabs.  Slab kt sits in buffer kt % STAGES; its loads were
-  // issued STAGES-2 slabs earlier.  Per slab:
-  //   read k-slice 1 | MFMAs of k-slice 0
-  //   wait until this wave's loads of slab kt+1 landed; barrier (slab kt+1 is
-  //     complete for every wave, and every wave is done with slab kt-1)
-  //   refill buffer (kt-1) % STAGES with slab kt+STAGES-1
-  //   read k-slice 0 of slab kt+1 | MFMAs of k-slice 1
+  // Ring of STAGES slabs; slab kt sits in buffer kt % STAGES.  Per slab:
+  //   for each k-slice but the last: read the next k-slice | its MFMAs
+  //   wait until this wave's reads of the slab returned and its loads of slab
+  //     kt+1 landed; barrier (slab kt+1 is complete for every wave, and no
+  //     wave reads this buffer any more)
+  //   refill this buffer with slab kt+STAGES; read k-slice 0 of slab kt+1 |
+  //     MFMAs of the last k-slice
+  // Set parity: k-slice ks of a slab computes from set ks % 2; BK/16 is even,
+  // so the next slab's first slice lands in set 0.
+  static_assert(C::NS % 2 == 0, "the fragment sets alternate per k-slice");
   if (KT > 0) {
 #pragma unroll
-    for (int s = 0; s < C::STAGES - 1; ++s)
+    for (int s = 0; s < C::STAGES; ++s) {
+      const SlabSrd r = slab_srd(s);
 #pragma unroll
-      for (int q = 0; q < C::PW; ++q) issue_one(s, s, q);
-    wait_vmcnt<(C::STAGES - 2) * C::PW>();
+      for (int q = 0; q < C::PW; ++q) issue_one(r, s, q);
+    }
+    wait_vmcnt<(C::STAGES - 1) * C::PW>();
     __syncthreads();
-    read_frags(fa0, fb0, 0, 0);
+    read_slice(0, 0, 0);
     int st = 0;
     for (int kt = 0; kt < KT; ++kt) {
       const int st_next = st + 1 == C::STAGES ? 0 : st + 1;
-      const int st_prev = st == 0 ? C::STAGES - 1 : st - 1;
-      read_frags(fa1, fb1, st, 1);
-      mfmas(fa0, fb0);
-      interleave();
-      __builtin_amdgcn_sched_barrier(0);
-      wait_vmcnt<(C::STAGES - 3) * C::PW>();
-      // a bare s_barrier: the LDS writes that matter are the copies, already
-      // waited for above, so no LDS fence (which would also stall on the
-      // k-slice reads just issued) is needed
+#pragma unroll
+      for (int ks = 0; ks < C::NS - 1; ++ks) {
+        read_slice((ks + 1) & 1, st, ks + 1);
+        mfmas(ks & 1);
+        interleave();
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      wait_lgkmcnt<0>();
+      wait_vmcnt<(C::STAGES - 2) * C::PW>();
+      // a bare s_barrier: the copies it publishes were waited for above
+      asm volatile("" ::: "memory");
       __builtin_amdgcn_s_barrier();
+      asm volatile("" ::: "memory");
+      __builtin_amdgcn_sched_barrier(0);
       // the refill loads go out one at a time between the reads of the next
-      // k-slice (and so between the MFMAs), never as a burst that would
-      // back up the address unit and stall MFMA issue
+      // k-slice (and so between the MFMAs), never as a burst that would back
+      // up the address unit and stall MFMA issue
+      const SlabSrd r = slab_srd(kt + C::STAGES);
 #pragma unroll
       for (int q = 0; q < C::PW; ++q) {
-        issue_one(kt + C::STAGES - 1, st_prev, q);
+        issue_one(r, st, q);
 #pragma unroll
-        for (int r = q * NRD / C::PW; r < (q + 1) * NRD / C::PW; ++r) read_piece(fa0, fb0, st_next, 0, r);
+        for (int pc = q * NRD / C::PW; pc < (q + 1) * NRD / C::PW; ++pc) read_piece(0, st_next, 0, pc);
       }
-      mfmas(fa1, fb1);
+      mfmas((C::NS - 1) & 1);
       interleave();
       __builtin_amdgcn_sched_barrier(0);
       st = st_next;

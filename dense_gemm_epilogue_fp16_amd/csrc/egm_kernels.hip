@@ -17,7 +17,7 @@ constexpr int DT = EGM_DTYPE;
 template <int EPI, int CFG>
 void launch_gemm(dim3 grid, hipStream_t s, const GemmArgs& a) {
   constexpr ConfigInfo ci = kConfigs[CFG];
-  using C = TileCfg<ci.bm, ci.bn, ci.stages, ci.wm, ci.wn>;
+  using C = TileCfg<ci.bm, ci.bn, ci.stages, ci.wm, ci.wn, ci.bk>;
   hipLaunchKernelGGL((gemm_epilogue_kernel<DT, EPI, C>), grid, dim3(C::NT), 0, s, a);
 }
 

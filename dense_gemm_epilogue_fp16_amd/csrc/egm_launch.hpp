@@ -14,20 +14,23 @@ struct EpiArgs;
 struct ConfigInfo {
   int bm, bn;      // output tile
   int wm, wn;      // waves along m and n (the workgroup is 64 * wm * wn lanes)
-  int stages;      // LDS ring depth, in 32-deep k-slabs
+  int stages;      // LDS ring depth, in k-slabs
+  int bk;          // k-slab depth (32 or 64)
   double rel_eff;  // relative per-CU MFMA efficiency, used by the shape heuristic
 };
 
-// Tile configurations: 32x32x16 MFMA blocks, 32-deep k-slabs.  The 256x256
-// tile runs 8 waves (2 per SIMD, 64x128 each) so that one wave's MFMAs can
-// issue while its SIMD partner waits on LDS reads or copies; the smaller tiles
-// run 4 waves (2 x 2).
+// Tile configurations: 32x32x16 MFMA blocks, 64-deep k-slabs (128-byte A
+// rows: whole cache lines per row, half the barriers of 32-deep slabs).  The
+// 256x256 tile runs 8 waves (2 per SIMD, 64x128 each) so that one wave's
+// MFMAs can issue while its SIMD partner waits on LDS reads or copies; its
+// 64 KiB slabs leave room for a ring of 2.  The smaller tiles run 4 waves
+// (2 x 2) with deeper rings.
 inline constexpr ConfigInfo kConfigs[] = {
-    {256, 256, 4, 2, 4, 1.00},
-    {256, 128, 2, 2, 4, 0.90},
-    {128, 256, 2, 2, 4, 0.90},
-    {128, 128, 2, 2, 4, 0.75},
-    {64, 64, 2, 2, 4, 0.40},
+    {256, 256, 4, 2, 2, 64, 1.00},
+    {256, 128, 2, 2, 3, 64, 0.90},
+    {128, 256, 2, 2, 3, 64, 0.90},
+    {128, 128, 2, 2, 4, 64, 0.75},
+    {64, 64, 2, 2, 4, 64, 0.40},
 };
 inline constexpr int kNumConfigs = int(sizeof(kConfigs) / sizeof(kConfigs[0]));
 

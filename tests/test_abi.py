@@ -180,7 +180,15 @@ def test_per_shape_choice(m, n, k, cfg):
 def test_config_table():
     n = egm.egm_num_configs()
     assert n == 5
-    assert egm.egm_config_describe(0).startswith("tile=256x256 kslab=32")
+    assert egm.egm_config_describe(0).startswith("tile=256x256 kslab=64 waves=4x2")
+    for c in range(n):
+        d = dict(kv.split("=") for kv in egm.egm_config_describe(c).split())
+        bm, bn = (int(x) for x in d["tile"].split("x"))
+        wm, wn = (int(x) for x in d["waves"].split("x"))
+        assert d["wave_tile"] == f"{bm // wm}x{bn // wn}"
+        # the ring plus the tile's bias slice fit the 160 KiB of LDS
+        assert int(d["lds_bytes"]) == int(d["lds_ring"]) * (bm + bn) * int(d["kslab"]) * 2
+        assert int(d["lds_bytes"]) + 1024 <= 160 * 1024
     assert egm.LIB.egm_config_describe(n, ctypes.create_string_buffer(8), 8) == egm.EGM_ERR_INVALID_VALUE
 
 
