@@ -138,10 +138,14 @@ __device__ __forceinline__ i32x4 make_srd(const void* base, uint64_t bytes) {
   return i32x4{(int32_t)(uint32_t)a, (int32_t)(uint32_t)((a >> 32) & 0xffffu), (int32_t)n, RSRC_FLAGS};
 }
 
-__device__ __forceinline__ void dma16(i32x4 srd, uint8_t* lds, uint32_t voff) {
+// LDS byte address of a __shared__ array (a 32-bit offset into the workgroup's LDS)
+__device__ __forceinline__ uint32_t lds_address(uint8_t* shared_array) {
+  return (uint32_t)(uintptr_t)(__attribute__((address_space(3))) uint8_t*)shared_array;
+}
+
+__device__ __forceinline__ void dma16(i32x4 srd, uint32_t lds_byte_addr, uint32_t voff) {
   // the LDS address is wave-uniform by construction; make that explicit for M0
-  const uint32_t lds_addr =
-      __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(__attribute__((address_space(3))) uint8_t*)lds);
+  const uint32_t lds_addr = __builtin_amdgcn_readfirstlane(lds_byte_addr);
 #pragma clang diagnostic push
 #pragma clang diagnostic ignored "-Winline-asm"
   // (an M0 write needs a wait state before a load-to-LDS reads it)
@@ -332,6 +336,7 @@ __global__ void __launch_bounds__(C::NT, 1) gemm_epilogue_kernel(GemmArgs p) {
   // the k-slab ring, then the tile's bias slice
   __shared__ __attribute__((aligned(1024))) uint8_t smem[C::LDS_BYTES + 1024];
   uint8_t* const bias_lds = smem + C::LDS_BYTES;
+  const uint32_t smem_lds = lds_address(smem);  // the same array as an LDS byte address, for the copies
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -350,7 +355,7 @@ __global__ void __launch_bounds__(C::NT, 1) gemm_epilogue_kernel(GemmArgs p) {
   if constexpr (EPI != EPI_NONE) {
     if (p.bias_layout == BIAS_COL && wave == 0) {
       const uint32_t c = (uint32_t)n0 + 8u * (uint32_t)lane;  // n is a multiple of 8: whole 16-byte pieces
-      dma16(make_srd(p.bias, (uint64_t)N * 2), bias_lds,
+      dma16(make_srd(p.bias, (uint64_t)N * 2), smem_lds + C::LDS_BYTES,
             lane < C::BN / 8 && c < (uint32_t)N ? c * 2u : OOB_OFFSET);
     }
   }
@@ -404,12 +409,12 @@ __global__ void __launch_bounds__(C::NT, 1) gemm_epilogue_kernel(GemmArgs p) {
   // Load q (0 .. PW-1) of this wave for a slab into ring buffer `stage`: the
   // first A_PW are A loads, the rest B loads.
   auto issue_one = [&](const SlabSrd& r, int stage, int q) {
-    uint8_t* const sa = smem + stage * C::STAGE_BYTES;
+    const uint32_t sa = smem_lds + (uint32_t)(stage * C::STAGE_BYTES);
     if (q < C::A_PW) {
-      dma16(r.a, sa + (wave * C::A_PW + q) * 1024, r.kbase + a_k8[q] < (uint32_t)K ? a_off[q] : OOB_OFFSET);
+      dma16(r.a, sa + (wave * C::A_PW + q) * 1024u, r.kbase + a_k8[q] < (uint32_t)K ? a_off[q] : OOB_OFFSET);
     } else {
       const int u = q - C::A_PW;
-      dma16(r.b, sa + C::A_BYTES + (wave * C::B_PW + u) * 1024, b_off[u]);
+      dma16(r.b, sa + C::A_BYTES + (wave * C::B_PW + u) * 1024u, b_off[u]);
     }
   };
 
