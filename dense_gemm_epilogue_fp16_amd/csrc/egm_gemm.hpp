@@ -538,19 +538,32 @@ __global__ void __launch_bounds__(C::NT, 1) gemm_epilogue_kernel(GemmArgs p) {
       __builtin_amdgcn_s_barrier();
       asm volatile("" ::: "memory");
       __builtin_amdgcn_sched_barrier(0);
-      // the refill loads go out one at a time between the reads of the next
-      // k-slice (and so between the MFMAs), never as a burst that would back
-      // up the address unit and stall MFMA issue
       const SlabSrd r = slab_srd(kt + C::STAGES);
+      if constexpr (C::NW == 8) {
+        // two waves per SIMD: the last k-slice's MFMAs go out first and the
+        // refill loads after them, while the SIMD partner keeps the MFMA pipe
+        // busy (measured faster than interleaving for this layout)
+        read_slice(0, st_next, 0);
+        mfmas((C::NS - 1) & 1);
+        interleave();
+        __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-      for (int q = 0; q < C::PW; ++q) {
-        issue_one(r, st, q);
+        for (int q = 0; q < C::PW; ++q) issue_one(r, st, q);
+        __builtin_amdgcn_sched_barrier(0);
+      } else {
+        // one wave per SIMD: the refill loads go out one at a time between the
+        // reads of the next k-slice (and so between the MFMAs), never as a
+        // burst that would back up the address unit and stall MFMA issue
 #pragma unroll
-        for (int pc = q * NRD / C::PW; pc < (q + 1) * NRD / C::PW; ++pc) read_piece(0, st_next, 0, pc);
+        for (int q = 0; q < C::PW; ++q) {
+          issue_one(r, st, q);
+#pragma unroll
+          for (int pc = q * NRD / C::PW; pc < (q + 1) * NRD / C::PW; ++pc) read_piece(0, st_next, 0, pc);
+        }
+        mfmas((C::NS - 1) & 1);
+        interleave();
+        __builtin_amdgcn_sched_barrier(0);
       }
-      mfmas((C::NS - 1) & 1);
-      interleave();
-      __builtin_amdgcn_sched_barrier(0);
       st = st_next;
     }
   }
