@@ -32,6 +32,17 @@ Gimpel); the mask bit is Z > 0 on the pre-activation after the bias, packed
 row-major [m, n/8] uint8, least-significant bit first (bit b of byte c is column
 8c+b); bias, residual and output share the operand dtype.
 
+Backward epilogues (the consumers of that mask; [bias-fusion], body: the
+training paragraph says the forward pass must leave the mask the backward pass
+needs, and the closing paragraph names dBias as an epilogue to come):
+  DRELU        dZ = P (.) mask, where P = A.B is the gradient reaching the
+               ReLU output and mask is the packed (Z > 0) of the forward pass;
+               D = dZ rounded to the operand dtype.
+  DRELU_BGRAD  the same, plus the bias gradient: dZ summed over the axis the
+               forward bias was broadcast along ((1,n) bias: over rows, n
+               values; (m,1) bias: over columns, m values), from the unrounded
+               dZ, returned in fp32.
+
 Every function here is pinned by ``tests/test_oracle_pins.py`` against brute
 force, closed forms, invariants and library routines.
 """
@@ -45,6 +56,10 @@ F16 = "fp16"
 BF16 = "bf16"
 
 EPILOGS = ("DEFAULT", "BIAS", "RELU_BIAS", "GELU_BIAS", "RELU_AUX_BIAS", "BIAS_RESIDUAL")
+BACKWARD_EPILOGS = ("DRELU", "DRELU_BGRAD")
+
+# unit roundoff of the fp32 accumulation the GPU path uses
+FP32_U = 2.0 ** -24
 
 # tanh-form GELU constants (Hendrycks & Gimpel, "Gaussian Error Linear Units")
 GELU_C0 = math.sqrt(2.0 / math.pi)
@@ -201,3 +216,60 @@ def reference(a_bits, b_bits, dtype, epilog, bias_bits=None, bias_layout=None,
     y = apply_epilog(z, epilog, r64)
     mask = relu_mask(z) if epilog == "RELU_AUX_BIAS" else None
     return y, z, mask
+
+
+# ---------------------------------------------------------------------------
+# backward: the ReLU mask applied to an incoming gradient, and the bias gradient
+# ---------------------------------------------------------------------------
+def unpack_mask(mask: np.ndarray, n: int) -> np.ndarray:
+    """Packed uint8 [m, n/8] (bit b of byte c = column 8c+b) -> bool [m, n]."""
+    mask = np.asarray(mask, dtype=np.uint8)
+    if mask.shape[1] * 8 != n:
+        raise ValueError("mask must hold n/8 bytes per row")
+    return np.unpackbits(mask, axis=1, bitorder="little").astype(bool)
+
+
+def drelu(p: np.ndarray, mask: np.ndarray) -> np.ndarray:
+    """dZ = dY (.) 1[Z > 0]: the gradient P = A.B reaching the ReLU output,
+    kept where the forward pre-activation was positive."""
+    p = np.asarray(p, dtype=np.float64)
+    return np.where(unpack_mask(mask, p.shape[1]), p, 0.0)
+
+
+def bias_grad(dz: np.ndarray, layout: str) -> np.ndarray:
+    """Gradient of a broadcast bias: a (1,n) bias ("col") collects the sum over
+    rows, an (m,1) bias ("row") the sum over columns."""
+    dz = np.asarray(dz, dtype=np.float64)
+    if layout == "col":
+        return dz.sum(axis=0)
+    if layout == "row":
+        return dz.sum(axis=1)
+    raise ValueError(f"unknown bias layout {layout!r}")
+
+
+def bias_grad_error_bound(a64: np.ndarray, b64: np.ndarray, mask: np.ndarray, layout: str) -> np.ndarray:
+    """Worst-case error of a bias gradient accumulated in fp32: every dZ value
+    carries at most K u (|A|.|B|)_ij from its K-term fp32 dot product, and the
+    L-term fp32 sum along the reduced axis adds at most L u sum|dZ|, so the
+    total stays below (K + L) u sum over the reduced axis of (|A|.|B|) (.) mask
+    (first-order bound, u = 2^-24)."""
+    absprod = product(np.abs(np.asarray(a64, dtype=np.float64)), np.abs(np.asarray(b64, dtype=np.float64)))
+    kept = np.where(unpack_mask(mask, absprod.shape[1]), absprod, 0.0)
+    k = np.asarray(a64).shape[1]
+    reduced_len = kept.shape[0] if layout == "col" else kept.shape[1]
+    return (k + reduced_len) * FP32_U * bias_grad(kept, layout)
+
+
+def backward_reference(a_bits, b_bits, dtype, epilog, mask, bias_layout=None):
+    """Unrounded dZ (fp64), and for DRELU_BGRAD the bias gradient (fp64) with
+    its fp32-accumulation error bound."""
+    if epilog not in BACKWARD_EPILOGS:
+        raise ValueError(f"unknown backward epilog {epilog!r}")
+    a64 = widen(a_bits, dtype)
+    b64 = widen(b_bits, dtype)
+    dz = drelu(product(a64, b64), mask)
+    if epilog == "DRELU":
+        return dz, None, None
+    if bias_layout is None:
+        raise ValueError("DRELU_BGRAD needs the bias layout")
+    return dz, bias_grad(dz, bias_layout), bias_grad_error_bound(a64, b64, mask, bias_layout)

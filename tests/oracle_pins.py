@@ -303,4 +303,131 @@ def pin_empty_k(o):
     assert list(mask[:, 0]) == [0, 0, 255, 255]
 
 
+# ---------------------------------------------------------------------------
+# backward: DRELU / DRELU_BGRAD
+# ---------------------------------------------------------------------------
+def _golden_backward():
+    rows = {}
+    with open(os.path.join(GOLDEN, "drelu_bgrad_small.txt")) as f:
+        for line in f:
+            if line.strip() and not line.startswith("#"):
+                key, *vals = line.split()
+                rows.setdefault(key, []).append([float(v) for v in vals])
+    return rows
+
+
+def pin_backward_golden(o):
+    """The hand-derived example in tests/golden/drelu_bgrad_small.txt, through
+    the whole backward path (A = dY, B = I)."""
+    g = _golden_backward()
+    a = o.round_to_bits(np.array(g["A"]), F16)
+    b = o.round_to_bits(np.eye(8), F16)
+    mask = np.array(g["MASK"], dtype=np.uint8).reshape(2, 1)
+    dz, dcol, _ = o.backward_reference(a, b, F16, "DRELU_BGRAD", mask, "col")
+    assert np.array_equal(dz, np.array(g["DZ"]))
+    assert np.array_equal(dcol, np.array(g["DBIAS_COL"][0]))
+    _, drow, _ = o.backward_reference(a, b, F16, "DRELU_BGRAD", mask, "row")
+    assert np.array_equal(drow, np.array(g["DBIAS_ROW"][0]))
+    dz2, none, _ = o.backward_reference(a, b, F16, "DRELU", mask)
+    assert none is None and np.array_equal(dz2, dz)
+
+
+def pin_backward_brute_force(o):
+    """Exact rational brute force: dZ[i][j] = (sum_t a b) if bit j of row i, and
+    the bias gradients as plain loops over Fractions."""
+    rng = np.random.default_rng(7)
+    for s, (m, n, k) in enumerate([(1, 8, 3), (3, 16, 5), (5, 24, 9), (9, 8, 2)]):
+        for dtype in (F16, BF16):
+            ops = gemm_operands(m, n, k, dtype, seed=300 + s, a_std=1.1, b_std=0.8, bias_layout="col")
+            mask = rng.integers(0, 256, size=(m, n // 8), dtype=np.uint8)
+            fa, fb = _frac_of_bits(ops.a, dtype, o), _frac_of_bits(ops.b, dtype, o)
+            dz_ex = [[Fraction(0)] * n for _ in range(m)]
+            for i in range(m):
+                for j in range(n):
+                    if (int(mask[i, j // 8]) >> (j % 8)) & 1:
+                        dz_ex[i][j] = sum((fa[i][t] * fb[t][j] for t in range(k)), Fraction(0))
+            dz, dcol, _ = o.backward_reference(ops.a, ops.b, dtype, "DRELU_BGRAD", mask, "col")
+            _, drow, _ = o.backward_reference(ops.a, ops.b, dtype, "DRELU_BGRAD", mask, "row")
+            for i in range(m):
+                for j in range(n):
+                    assert abs(dz[i, j] - float(dz_ex[i][j])) <= 1e-12
+            for j in range(n):
+                assert abs(dcol[j] - float(sum((dz_ex[i][j] for i in range(m)), Fraction(0)))) <= 1e-11
+            for i in range(m):
+                assert abs(drow[i] - float(sum(dz_ex[i], Fraction(0)))) <= 1e-11
+
+
+def pin_drelu_is_relu_derivative(o):
+    """With the mask the forward pass packed from Z, DRELU(dY) equals the
+    directional derivative of ReLU at Z along dY: (relu(Z + h dY) - relu(Z)) / h
+    for a step h too small to flip any sign (|Z| >= 1/8, |h dY| < 1/64)."""
+    rng = np.random.default_rng(11)
+    m, n = 6, 24
+    # dyadic values, so z + h dy and the difference quotient are exact in fp64
+    z = rng.choice([-1.0, 1.0], size=(m, n)) * rng.integers(1, 17, size=(m, n)) / 8.0
+    dy = rng.integers(-3, 4, size=(m, n)).astype(np.float64)
+    h = 2.0 ** -8
+    fd = (o.relu(z + h * dy) - o.relu(z)) / h
+    assert np.array_equal(o.drelu(dy, o.relu_mask(z)), fd)
+
+
+def pin_drelu_all_or_nothing(o):
+    """A full mask keeps the product (DRELU = DEFAULT); an empty one gives 0."""
+    ops = gemm_operands(40, 32, 24, BF16, seed=21, bias_layout="col")
+    p = o.product(o.widen(ops.a, BF16), o.widen(ops.b, BF16))
+    full = np.full((40, 4), 255, dtype=np.uint8)
+    dz, _, _ = o.backward_reference(ops.a, ops.b, BF16, "DRELU", full)
+    assert np.array_equal(dz, p)
+    dz0, dcol, _ = o.backward_reference(ops.a, ops.b, BF16, "DRELU_BGRAD", np.zeros_like(full), "col")
+    assert not dz0.any() and not dcol.any()
+
+
+def pin_bias_grad_invariants(o):
+    """Both gradients sum to the sum of dZ; the row and column gradients are
+    each other's transpose; integer inputs give integer sums exactly."""
+    ops = integer_operands(33, 40, 16, F16, seed=5)
+    rng = np.random.default_rng(3)
+    mask = rng.integers(0, 256, size=(33, 5), dtype=np.uint8)
+    dz, dcol, _ = o.backward_reference(ops.a, ops.b, F16, "DRELU_BGRAD", mask, "col")
+    _, drow, _ = o.backward_reference(ops.a, ops.b, F16, "DRELU_BGRAD", mask, "row")
+    assert dcol.sum() == drow.sum() == dz.sum()
+    assert np.array_equal(o.bias_grad(dz.T, "row"), dcol)
+    ai = o.widen(ops.a, F16).astype(np.int64)
+    bi = o.widen(ops.b, F16).astype(np.int64)
+    keep = np.unpackbits(mask, axis=1, bitorder="little").astype(bool)
+    want = np.where(keep, ai @ bi, 0)
+    assert np.array_equal(dz, want) and np.array_equal(dcol, want.sum(axis=0)) and np.array_equal(drow, want.sum(axis=1))
+
+
+def pin_bias_grad_error_bound(o):
+    """The bound covers an actual fp32 computation (fp32 dot products, then an
+    fp32 running sum) and is not vacuous (a small multiple of the error)."""
+    for dtype in (F16, BF16):
+        ops = gemm_operands(300, 64, 512, dtype, seed=9, a_std=1.0, b_std=1.0 / math.sqrt(512), bias_layout="col")
+        rng = np.random.default_rng(4)
+        mask = rng.integers(0, 256, size=(300, 8), dtype=np.uint8)
+        dz, dcol, bound = o.backward_reference(ops.a, ops.b, dtype, "DRELU_BGRAD", mask, "col")
+        p32 = np.zeros((300, 64), dtype=np.float32)
+        a32, b32 = o.widen(ops.a, dtype).astype(np.float32), o.widen(ops.b, dtype).astype(np.float32)
+        for t in range(512):  # one rounding per step, as a sequential fp32 dot product
+            p32 = (p32 + a32[:, t:t + 1] * b32[t:t + 1, :]).astype(np.float32)
+        keep = np.unpackbits(mask, axis=1, bitorder="little").astype(bool)
+        dz32 = np.where(keep, p32, np.float32(0))
+        s32 = np.zeros(64, dtype=np.float32)
+        for i in range(300):
+            s32 = (s32 + dz32[i]).astype(np.float32)
+        err = np.abs(s32.astype(np.float64) - dcol)
+        assert (err <= bound).all() and (bound > 0).all()
+    # closed form: A and B all ones, full mask: |A|.|B| = K everywhere, so the
+    # (1,n) gradient's bound is (K + M) u M K and the (m,1) one's (K + N) u N K
+    m, n, k = 24, 16, 40
+    ones_a = o.round_to_bits(np.ones((m, k)), F16)
+    ones_b = o.round_to_bits(np.ones((k, n)), F16)
+    full = np.full((m, n // 8), 255, dtype=np.uint8)
+    _, _, bcol = o.backward_reference(ones_a, ones_b, F16, "DRELU_BGRAD", full, "col")
+    _, _, brow = o.backward_reference(ones_a, ones_b, F16, "DRELU_BGRAD", full, "row")
+    assert np.allclose(bcol, (k + m) * 2.0 ** -24 * m * k, rtol=1e-15, atol=0)
+    assert np.allclose(brow, (k + n) * 2.0 ** -24 * n * k, rtol=1e-15, atol=0)
+
+
 PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_")]

@@ -86,6 +86,31 @@ def _widen_bf16_shift15(bits, dtype):
     return _orig["widen"](bits, dtype)
 
 
+def _unpack_msb(mask, n):
+    return np.unpackbits(np.asarray(mask, dtype=np.uint8), axis=1, bitorder="big").astype(bool)
+
+
+def _drelu_inverted(p, mask):
+    p = np.asarray(p, dtype=np.float64)
+    return np.where(_orig["unpack_mask"](mask, p.shape[1]), 0.0, p)
+
+
+def _bias_grad_wrong_axis(dz, layout):
+    return _orig["bias_grad"](dz, "row" if layout == "col" else "col")
+
+
+def _bias_grad_mean(dz, layout):
+    dz = np.asarray(dz, dtype=np.float64)
+    return dz.mean(axis=0) if layout == "col" else dz.mean(axis=1)
+
+
+def _bound_without_k(a64, b64, mask, layout):
+    full = _orig["bias_grad_error_bound"](a64, b64, mask, layout)
+    k = np.asarray(a64).shape[1]
+    n_red = np.asarray(a64).shape[0] if layout == "col" else np.asarray(b64).shape[1]
+    return full * n_red / (k + n_red)
+
+
 MUTANTS = {
     "bias_dropped": ("add_bias", _drop_bias),
     "bias_layout_swapped": ("add_bias", _swapped_layout),
@@ -102,6 +127,11 @@ MUTANTS = {
     "round_truncates": ("round_to_bits", _round_trunc),
     "round_twice_via_fp32": ("round_to_bits", _round_via_f32),
     "widen_bf16_wrong_shift": ("widen", _widen_bf16_shift15),
+    "mask_unpacked_msb_first": ("unpack_mask", _unpack_msb),
+    "drelu_mask_inverted": ("drelu", _drelu_inverted),
+    "bias_grad_wrong_axis": ("bias_grad", _bias_grad_wrong_axis),
+    "bias_grad_mean_not_sum": ("bias_grad", _bias_grad_mean),
+    "bias_grad_bound_drops_k_term": ("bias_grad_error_bound", _bound_without_k),
 }
 
 
