@@ -47,7 +47,10 @@ EPILOGS = {
     "GELU_BIAS": 3,
     "RELU_AUX_BIAS": 4,
     "BIAS_RESIDUAL": 5,
+    "DRELU": 6,
+    "DRELU_BGRAD": 7,
 }
+BACKWARD_EPILOGS = ("DRELU", "DRELU_BGRAD")
 
 # bias layouts (egm_bias_layout_t)
 EGM_BIAS_NONE = 0
@@ -70,7 +73,8 @@ class EgmError(RuntimeError):
 
 
 class EpilogInputs(ctypes.Structure):
-    _fields_ = [("bias", ctypes.c_void_p), ("bias_layout", ctypes.c_int32), ("residual", ctypes.c_void_p)]
+    _fields_ = [("bias", ctypes.c_void_p), ("bias_layout", ctypes.c_int32), ("residual", ctypes.c_void_p),
+                ("bias_grad", ctypes.c_void_p)]
 
 
 class PlanOptions(ctypes.Structure):
@@ -130,11 +134,11 @@ def _check(status: int, where: str) -> None:
 
 
 def egm_plan(m: int, n: int, k: int, dtype: int, epilog: int, bias: int = 0, bias_layout: int = EGM_BIAS_NONE,
-             residual: int = 0, *, fused: int = 1, force_config: int = -1, autotune: int = 0,
+             residual: int = 0, *, bias_grad: int = 0, fused: int = 1, force_config: int = -1, autotune: int = 0,
              group_m: int = 0, raw_status: bool = False):
     """Returns the plan handle (int), or (status, handle) with ``raw_status``."""
     h = ctypes.c_void_p()
-    ins = EpilogInputs(bias or None, bias_layout, residual or None)
+    ins = EpilogInputs(bias or None, bias_layout, residual or None, bias_grad or None)
     opt = PlanOptions(fused, force_config, autotune, group_m)
     st = LIB.egm_plan(ctypes.byref(h), int(m), int(n), int(k), int(dtype), int(epilog), ctypes.byref(ins),
                       ctypes.byref(opt))
@@ -210,6 +214,11 @@ class Matmul:
     BIAS_RESIDUAL.  ``execute()`` enqueues on torch's current stream and
     returns D (and the packed [m, n/8] uint8 mask for RELU_AUX_BIAS).
     ``a`` and ``b`` may be rebound per call: ``execute(a=..., b=...)``.
+
+    Backward: ``plan("DRELU")`` and ``plan("DRELU_BGRAD", {"bias_grad": g})``
+    with ``g`` a float32 tensor shaped (m,1) (gradient of an (m,1) bias: row
+    sums) or (1,n) (of a (1,n) bias: column sums); ``execute(aux=mask)`` takes
+    the forward RELU_AUX_BIAS mask as input and returns D (and ``g``).
     """
 
     def __init__(self, a, b):
@@ -240,11 +249,26 @@ class Matmul:
         if epilog not in EPILOGS:
             raise ValueError(f"unknown epilog {epilog!r}; one of {sorted(EPILOGS)}")
         ins = dict(epilog_inputs or {})
-        unknown = set(ins) - {"bias", "residual"}
+        unknown = set(ins) - {"bias", "residual", "bias_grad"}
         if unknown:
             raise ValueError(f"unknown epilog inputs {sorted(unknown)}")
-        bias_ptr, layout, res_ptr = 0, EGM_BIAS_NONE, 0
+        bias_ptr, layout, res_ptr, grad_ptr = 0, EGM_BIAS_NONE, 0, 0
         keep = []
+        self.bias_grad = None
+        if "bias_grad" in ins:
+            import torch
+            g = ins["bias_grad"]
+            if not g.is_cuda or not g.is_contiguous() or g.dtype != torch.float32:
+                raise ValueError("bias_grad must be a contiguous float32 GPU tensor")
+            if tuple(g.shape) == (self.m, 1):
+                layout = EGM_BIAS_ROW
+            elif tuple(g.shape) == (1, self.n):
+                layout = EGM_BIAS_COL
+            else:
+                raise ValueError(f"bias_grad shape {tuple(g.shape)} must be (m,1)=({self.m},1) or (1,n)=(1,{self.n})")
+            grad_ptr = g.data_ptr()
+            keep.append(g)
+            self.bias_grad = g
         if "bias" in ins:
             bias = ins["bias"]
             self._check_operand(bias, "bias")
@@ -267,8 +291,8 @@ class Matmul:
             keep.append(r)
         self.free()
         self._plan = egm_plan(self.m, self.n, self.k, _dtype_code(self.a), EPILOGS[epilog], bias_ptr, layout,
-                              res_ptr, fused=int(fused), force_config=force_config, autotune=int(autotune),
-                              group_m=group_m)
+                              res_ptr, bias_grad=grad_ptr, fused=int(fused), force_config=force_config,
+                              autotune=int(autotune), group_m=group_m)
         self._keep = tuple(keep)
         self.epilog = epilog
         self._ws = None
@@ -299,10 +323,19 @@ class Matmul:
         mask = None
         if self.epilog == "RELU_AUX_BIAS":
             mask = aux if aux is not None else torch.empty((self.m, self.n // 8), dtype=torch.uint8, device=a.device)
+        elif self.epilog in BACKWARD_EPILOGS:
+            if aux is None or aux.dtype != torch.uint8 or tuple(aux.shape) != (self.m, self.n // 8) \
+                    or not aux.is_cuda or not aux.is_contiguous():
+                raise ValueError("the backward epilogues take the forward mask: aux = uint8 [m, n/8] on the GPU")
+            mask = aux
         s = stream if stream is not None else torch.cuda.current_stream(a.device)
         ws = self._ws
         egm_execute(plan, a.data_ptr(), b.data_ptr(), d.data_ptr(), mask.data_ptr() if mask is not None else 0,
                     ws.data_ptr() if ws is not None else 0, ws.numel() if ws is not None else 0, s.cuda_stream)
+        if self.epilog == "DRELU_BGRAD":
+            return d, self.bias_grad
+        if self.epilog == "DRELU":
+            return d
         return (d, mask) if mask is not None else d
 
     def free(self):

@@ -32,7 +32,7 @@ using egm::GemmLaunch;
 
 constexpr uint32_t kPlanMagic = 0x45474d31u;  // "EGM1"
 constexpr uint32_t kFreedMagic = 0xdeadbeefu;
-constexpr int kNumEpi = 6;
+constexpr int kNumEpi = 8;
 // keeps every in-tile buffer offset (256 rows x n or k elements) below 2^30
 constexpr int64_t kMaxNK = int64_t(1) << 21;
 constexpr int kNumCUs = 256;
@@ -45,7 +45,8 @@ using egm::ConfigInfo;
 int epi_of(egm_epilog_t e) { return int(e); }
 
 const char* epilog_name(int e) {
-  static const char* names[kNumEpi] = {"DEFAULT", "BIAS", "RELU_BIAS", "GELU_BIAS", "RELU_AUX_BIAS", "BIAS_RESIDUAL"};
+  static const char* names[kNumEpi] = {"DEFAULT",       "BIAS",          "RELU_BIAS", "GELU_BIAS",
+                                       "RELU_AUX_BIAS", "BIAS_RESIDUAL", "DRELU",     "DRELU_BGRAD"};
   return (e >= 0 && e < kNumEpi) ? names[e] : "?";
 }
 
@@ -81,11 +82,15 @@ struct egm_plan_s {
   const void* bias;
   int32_t bias_layout;
   const void* residual;
+  void* bias_grad;           // DRELU_BGRAD output (fp32)
   int32_t fused;
   int32_t config;
   int32_t group_m;
   int32_t autotune_pending;
   size_t workspace_bytes;
+  size_t product_bytes;      // the two-kernel path's P at the start of the workspace
+  int64_t grad_chunks;       // DRELU_BGRAD: rows of partial sums (32-row or 32-column blocks)
+  int64_t grad_len;          // ... and their length (n or m)
 };
 
 namespace {
@@ -114,12 +119,15 @@ void describe(const egm_plan_s* p, char* buf, size_t len) {
 hipError_t launch_plan(const egm_plan_s* p, int cfg, const void* A, const void* B, void* D, void* aux,
                        void* ws, hipStream_t s) {
   const ConfigInfo& c = kConfigs[cfg];
+  const int dt = p->dtype == EGM_F16 ? egm::DT_F16 : egm::DT_BF16;
+  float* partial = p->grad_chunks > 0 ? reinterpret_cast<float*>(static_cast<uint8_t*>(ws) + p->product_bytes) : nullptr;
   GemmArgs g{};
   g.A = A;
   g.B = B;
   g.bias = p->bias;
   g.R = p->residual;
   g.aux = aux;
+  g.partial = partial;
   g.M = int32_t(p->m);
   g.N = int32_t(p->n);
   g.K = int32_t(p->k);
@@ -131,12 +139,20 @@ hipError_t launch_plan(const egm_plan_s* p, int cfg, const void* A, const void* 
   const int epi = epi_of(p->epilog);
   const bool two_kernels = !p->fused && epi != egm::EPI_NONE;
   g.D = two_kernels ? ws : D;
-  GemmLaunch gl = egm::gemm_launcher(p->dtype == EGM_F16 ? egm::DT_F16 : egm::DT_BF16,
-                                      two_kernels ? egm::EPI_NONE : epi, cfg);
+  GemmLaunch gl = egm::gemm_launcher(dt, two_kernels ? egm::EPI_NONE : epi, cfg);
   if (gl == nullptr) return hipErrorInvalidValue;
   gl(grid, s, g);
   hipError_t err = hipGetLastError();
-  if (err != hipSuccess || !two_kernels) return err;
+  if (err != hipSuccess) return err;
+  // the bias gradient's last step: sum the per-block partials in block order
+  auto finish_grad = [&]() {
+    int64_t blocks = cdiv(p->grad_len, 256);
+    if (blocks > 4096) blocks = 4096;
+    egm::launch_bias_grad_finish(dim3(uint32_t(blocks)), s, partial, p->grad_chunks, p->grad_len,
+                                 static_cast<float*>(p->bias_grad));
+    return hipGetLastError();
+  };
+  if (!two_kernels) return epi == egm::EPI_DRELU_BGRAD ? finish_grad() : err;
   EpiArgs e{};
   e.P = ws;
   e.bias = p->bias;
@@ -149,10 +165,20 @@ hipError_t launch_plan(const egm_plan_s* p, int cfg, const void* A, const void* 
   const int64_t units = p->m * (p->n / 8);
   int64_t blocks = cdiv(units, 256);
   if (blocks > 8 * 1024) blocks = 8 * 1024;
-  EpiLaunch el = egm::epi_launcher(p->dtype == EGM_F16 ? egm::DT_F16 : egm::DT_BF16, epi);
+  // the backward two-kernel path applies the mask with the DRELU epilogue
+  // kernel, then sums the bias gradient from D
+  EpiLaunch el = egm::epi_launcher(dt, epi == egm::EPI_DRELU_BGRAD ? egm::EPI_DRELU : epi);
   if (el == nullptr) return hipErrorInvalidValue;
   el(dim3(uint32_t(blocks)), s, e);
-  return hipGetLastError();
+  err = hipGetLastError();
+  if (err != hipSuccess || epi != egm::EPI_DRELU_BGRAD) return err;
+  const int64_t punits = p->bias_layout == EGM_BIAS_COL ? cdiv(p->m, 32) * (p->n / 8) : p->m * cdiv(p->n, 32);
+  int64_t pblocks = cdiv(punits, 256);
+  if (pblocks > 8 * 1024) pblocks = 8 * 1024;
+  egm::partials_launcher(dt)(dim3(uint32_t(pblocks)), s, D, p->m, int32_t(p->n), p->bias_layout, partial);
+  err = hipGetLastError();
+  if (err != hipSuccess) return err;
+  return finish_grad();
 }
 
 // Time every config once (after one warm-up launch each) on the caller's
@@ -207,10 +233,20 @@ egm_status_t egm_plan(egm_plan_t* out, int64_t m, int64_t n, int64_t k, egm_dtyp
 
   const void* bias = nullptr;
   const void* residual = nullptr;
+  void* bias_grad = nullptr;
   int32_t layout = EGM_BIAS_NONE;
-  if (epilog == EGM_EPILOG_DEFAULT) {
+  if (in != nullptr && in->bias_grad != nullptr && epilog != EGM_EPILOG_DRELU_BGRAD)
+    return EGM_ERR_INVALID_VALUE;  // a bias gradient only belongs to DRELU_BGRAD
+  if (epilog == EGM_EPILOG_DEFAULT || epilog == EGM_EPILOG_DRELU) {
     if (in != nullptr && (in->bias != nullptr || in->residual != nullptr || in->bias_layout != EGM_BIAS_NONE))
-      return EGM_ERR_INVALID_VALUE;  // DEFAULT takes no epilog inputs
+      return EGM_ERR_INVALID_VALUE;  // DEFAULT and DRELU take no epilog inputs
+  } else if (epilog == EGM_EPILOG_DRELU_BGRAD) {
+    if (in == nullptr || in->bias_grad == nullptr) return EGM_ERR_INVALID_VALUE;
+    if (in->bias != nullptr || in->residual != nullptr) return EGM_ERR_INVALID_VALUE;
+    if (in->bias_layout != EGM_BIAS_ROW && in->bias_layout != EGM_BIAS_COL) return EGM_ERR_SHAPE;
+    if (!aligned16(in->bias_grad)) return EGM_ERR_ALIGNMENT;
+    bias_grad = in->bias_grad;
+    layout = in->bias_layout;
   } else {
     if (in == nullptr || in->bias == nullptr) return EGM_ERR_INVALID_VALUE;
     if (in->bias_layout != EGM_BIAS_ROW && in->bias_layout != EGM_BIAS_COL) return EGM_ERR_SHAPE;
@@ -250,6 +286,7 @@ egm_status_t egm_plan(egm_plan_t* out, int64_t m, int64_t n, int64_t k, egm_dtyp
   p->bias = bias;
   p->bias_layout = layout;
   p->residual = residual;
+  p->bias_grad = bias_grad;
   p->fused = fused;
   p->config = force >= 0 ? force : choose_config(m, n, k);
   // the grid is one workgroup per output tile and tile ids are 32-bit
@@ -261,7 +298,17 @@ egm_status_t egm_plan(egm_plan_t* out, int64_t m, int64_t n, int64_t k, egm_dtyp
   }
   p->group_m = group_m;
   p->autotune_pending = tune;
-  p->workspace_bytes = (!fused && epilog != EGM_EPILOG_DEFAULT) ? size_t(m) * size_t(n) * 2u : 0u;
+  // workspace: the two-kernel path's product P, then (DRELU_BGRAD) the fp32
+  // partial sums: one row of n per 32-row block ((1,n) bias) or of m per
+  // 32-column block ((m,1) bias); the same layout on both paths
+  p->product_bytes = (!fused && epilog != EGM_EPILOG_DEFAULT) ? (size_t(m) * size_t(n) * 2u + 255u) & ~size_t(255) : 0u;
+  p->grad_chunks = 0;
+  p->grad_len = 0;
+  if (epilog == EGM_EPILOG_DRELU_BGRAD) {
+    p->grad_chunks = layout == EGM_BIAS_COL ? cdiv(m, 32) : cdiv(n, 32);
+    p->grad_len = layout == EGM_BIAS_COL ? n : m;
+  }
+  p->workspace_bytes = p->product_bytes + size_t(p->grad_chunks) * size_t(p->grad_len) * 4u;
   if (const char* log = std::getenv("EGM_LOG"); log != nullptr && log[0] == '1') {
     char buf[512];
     describe(p, buf, sizeof(buf));
@@ -275,11 +322,28 @@ egm_status_t egm_execute(egm_plan_t plan, const void* A, const void* B, void* D,
                          size_t workspace_bytes, void* stream) {
   if (!valid_plan(plan)) return EGM_ERR_INVALID_PLAN;
   egm_plan_s* p = plan;
-  const bool need_aux = p->epilog == EGM_EPILOG_RELU_AUX_BIAS;
-  if (need_aux != (aux != nullptr)) return EGM_ERR_INVALID_VALUE;
+  const bool need_aux = p->epilog == EGM_EPILOG_RELU_AUX_BIAS || p->epilog == EGM_EPILOG_DRELU ||
+                        p->epilog == EGM_EPILOG_DRELU_BGRAD;
+  const bool empty = p->m == 0 || p->n == 0;
+  // an empty problem has an empty mask, which may come as NULL
+  if (need_aux ? (aux == nullptr && !empty) : aux != nullptr) return EGM_ERR_INVALID_VALUE;
   if (p->workspace_bytes > 0 && (workspace == nullptr || workspace_bytes < p->workspace_bytes))
     return EGM_ERR_WORKSPACE;
-  if (p->m == 0 || p->n == 0) return EGM_OK;  // empty output: nothing to do
+  if (empty) {
+    // empty output: nothing to compute, but a bias gradient of a non-empty
+    // axis is a sum of nothing: zeros
+    // (written by the finish kernel over zero chunks, not a memset, so the
+    // call stays capturable in a graph)
+    if (p->bias_grad != nullptr && p->grad_len > 0) {
+      if (!aligned16(p->bias_grad)) return EGM_ERR_ALIGNMENT;
+      int64_t blocks = cdiv(p->grad_len, 256);
+      if (blocks > 4096) blocks = 4096;
+      egm::launch_bias_grad_finish(dim3(uint32_t(blocks)), reinterpret_cast<hipStream_t>(stream), nullptr, 0,
+                                   p->grad_len, static_cast<float*>(p->bias_grad));
+      return hipGetLastError() == hipSuccess ? EGM_OK : EGM_ERR_HIP;
+    }
+    return EGM_OK;
+  }
   if (D == nullptr) return EGM_ERR_INVALID_VALUE;
   if (p->k > 0 && (A == nullptr || B == nullptr)) return EGM_ERR_INVALID_VALUE;
   if ((A && !aligned16(A)) || (B && !aligned16(B)) || !aligned16(D) || (aux && !aligned16(aux)) ||

@@ -22,8 +22,22 @@ typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 enum DType { DT_F16 = 0, DT_BF16 = 1 };
 
 // Epilogue kinds (device side).  EPI_NONE stores the bare product (the DEFAULT
-// epilog, and the first kernel of the two-kernel path).
-enum Epi { EPI_NONE = 0, EPI_BIAS = 1, EPI_RELU = 2, EPI_GELU = 3, EPI_RELU_AUX = 4, EPI_RESID = 5 };
+// epilog, and the first kernel of the two-kernel path).  EPI_DRELU and
+// EPI_DRELU_BGRAD are the backward epilogues: the product is the gradient at
+// the ReLU output, kept where the forward mask bit is set (and, for BGRAD,
+// also summed along the forward bias's broadcast axis).
+enum Epi {
+  EPI_NONE = 0,
+  EPI_BIAS = 1,
+  EPI_RELU = 2,
+  EPI_GELU = 3,
+  EPI_RELU_AUX = 4,
+  EPI_RESID = 5,
+  EPI_DRELU = 6,
+  EPI_DRELU_BGRAD = 7
+};
+constexpr bool epi_adds_bias(int epi) { return epi >= EPI_BIAS && epi <= EPI_RESID; }
+constexpr bool epi_reads_mask(int epi) { return epi == EPI_DRELU || epi == EPI_DRELU_BGRAD; }
 enum BiasLayout { BIAS_NONE = 0, BIAS_ROW = 1, BIAS_COL = 2 };
 
 // ---------------------------------------------------------------------------
@@ -46,8 +60,14 @@ __device__ __forceinline__ u32x4 buf_load16(__amdgpu_buffer_rsrc_t r, uint32_t o
 __device__ __forceinline__ u32x2 buf_load8(__amdgpu_buffer_rsrc_t r, uint32_t off) {
   return __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, 0);
 }
+__device__ __forceinline__ uint32_t buf_load4(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  return __builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 0);
+}
 __device__ __forceinline__ uint16_t buf_load2(__amdgpu_buffer_rsrc_t r, uint32_t off) {
   return __builtin_amdgcn_raw_buffer_load_b16(r, off, 0, 0);
+}
+__device__ __forceinline__ uint8_t buf_load1(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  return __builtin_amdgcn_raw_buffer_load_b8(r, off, 0, 0);
 }
 __device__ __forceinline__ void buf_store16(u32x4 v, __amdgpu_buffer_rsrc_t r, uint32_t off) {
   __builtin_amdgcn_raw_buffer_store_b128(v, r, off, 0, 0);

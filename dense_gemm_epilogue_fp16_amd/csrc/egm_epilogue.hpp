@@ -7,7 +7,11 @@
 // Reads P = round(A.B) (16-bit, [M,N]), the bias and the residual; applies the
 // same fp32 epilogue as the fused kernel to fp32(P) + bias; writes D and the
 // packed ReLU mask.  Each thread handles runs of 8 columns of one row: one
-// 16-byte load of P (and of R), one 16-byte store of D and one mask byte.
+// 16-byte load of P (and of R), one 16-byte store of D and one mask byte.  The
+// backward DRELU reads the mask byte instead and keeps P where its bits are
+// set; the bias gradient of the two-kernel path is then summed from D by
+// axis_partials_kernel and bias_grad_finish_kernel (the latter also finishes
+// the fused kernel's per-block sums).
 //
 // Pages (cited by title):
 //   [bias-fusion] "通过 nvmath-python 的 cuBLASLt 绑定，在 PyTorch 中实现偏差融合以提升推理性能"
@@ -49,7 +53,7 @@ __global__ void __launch_bounds__(256) epilogue_kernel(EpiArgs p) {
       z[2 * e] = lo_f32<DT>(pv[e]);
       z[2 * e + 1] = hi_f32<DT>(pv[e]);
     }
-    if constexpr (EPI != EPI_NONE) {
+    if constexpr (epi_adds_bias(EPI)) {
       if (p.bias_layout == BIAS_ROW) {
         const float b = to_f32<DT>(bias[row]);
 #pragma unroll
@@ -71,6 +75,11 @@ __global__ void __launch_bounds__(256) epilogue_kernel(EpiArgs p) {
         z[2 * e + 1] += hi_f32<DT>(rv[e]);
       }
     }
+    if constexpr (epi_reads_mask(EPI)) {
+      const uint32_t keep = aux[u];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) z[e] = ((keep >> e) & 1u) ? z[e] : 0.0f;
+    }
     if constexpr (EPI == EPI_RELU_AUX) {
       uint32_t bits = 0;
 #pragma unroll
@@ -81,6 +90,68 @@ __global__ void __launch_bounds__(256) epilogue_kernel(EpiArgs p) {
 #pragma unroll
     for (int e = 0; e < 4; ++e) out[e] = pack2<DT>(activate<EPI>(z[2 * e]), activate<EPI>(z[2 * e + 1]));
     *(u32x4*)(D + idx) = out;
+  }
+}
+
+// Bias gradient of the two-kernel path, first step: partial sums of D
+// ([M,N], the operand dtype) in the same layout the fused kernel writes,
+//   (1,n) bias (BIAS_COL): partial[rb * N + c] = sum of D[32 rb .. 32 rb + 31, c]
+//   (m,1) bias (BIAS_ROW): partial[cb * M + r] = sum of D[r, 32 cb .. 32 cb + 31]
+// one thread per (32-row block, 8 columns) or (row, 32-column block).
+template <int DT>
+__global__ void __launch_bounds__(256) axis_partials_kernel(const void* Dp, int64_t M, int32_t N, int32_t layout,
+                                                            float* partial) {
+  const uint16_t* D = (const uint16_t*)Dp;
+  if (layout == BIAS_COL) {
+    const int64_t groups = N / 8, blocks = (M + 31) / 32;
+    for (int64_t u = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; u < blocks * groups;
+         u += (int64_t)gridDim.x * blockDim.x) {
+      const int64_t rb = u / groups, c = (u - rb * groups) * 8;
+      float s[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+      const int64_t r_end = rb * 32 + 32 < M ? rb * 32 + 32 : M;
+      for (int64_t r = rb * 32; r < r_end; ++r) {
+        const u32x4 v = *(const u32x4*)(D + r * N + c);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          s[2 * e] += lo_f32<DT>(v[e]);
+          s[2 * e + 1] += hi_f32<DT>(v[e]);
+        }
+      }
+      float* out = partial + rb * N + c;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) out[e] = s[e];
+    }
+  } else {
+    const int64_t cblocks = (N + 31) / 32;
+    for (int64_t u = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; u < M * cblocks;
+         u += (int64_t)gridDim.x * blockDim.x) {
+      const int64_t cb = u / M, r = u - cb * M;  // consecutive threads: consecutive rows
+      float s = 0.0f;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int64_t c = cb * 32 + 8 * q;
+        if (c < N) {
+          const u32x4 v = *(const u32x4*)(D + r * N + c);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) s += lo_f32<DT>(v[e]) + hi_f32<DT>(v[e]);
+        }
+      }
+      partial[cb * M + r] = s;
+    }
+  }
+}
+
+// Bias gradient, last step (both paths): out[x] = sum over c of
+// partial[c * len + x], c = 0 .. chunks-1 in order, so the result does not
+// depend on the launch.  (A template only so that every unit including this
+// header may see it; it is instantiated once, for float.)
+template <typename F>
+__global__ void __launch_bounds__(256) bias_grad_finish_kernel(const F* partial, int64_t chunks, int64_t len,
+                                                               F* out) {
+  for (int64_t x = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; x < len; x += (int64_t)gridDim.x * blockDim.x) {
+    F s = 0;
+    for (int64_t c = 0; c < chunks; ++c) s += partial[c * len + x];
+    out[x] = s;
   }
 }
 

@@ -48,7 +48,10 @@ struct GemmArgs {
   void* D;           // [M,N] (the workspace P for the first kernel of the two-kernel path)
   const void* bias;  // [M] or [N]
   const void* R;     // [M,N] residual
-  void* aux;         // [M,N/8] mask bytes
+  void* aux;         // [M,N/8] mask bytes (written by RELU_AUX, read by DRELU / DRELU_BGRAD)
+  float* partial;    // DRELU_BGRAD: fp32 partial sums of dZ, one row of them per 32-row
+                     // block ((1,n) bias: [ceil(M/32), N]) or per 32-column block
+                     // ((m,1) bias: [ceil(N/32), M])
   int32_t M, N, K;
   int32_t bias_layout;
   int32_t tiles_m, tiles_n;
@@ -214,7 +217,7 @@ __device__ __forceinline__ void epilogue_store(const GemmArgs& p, f32x16 (&acc)[
 
   // a (1,n) bias: the tile's BN values sit in LDS (bias_lds), by tile column
   float bcol[FN][4][4];
-  if constexpr (EPI != EPI_NONE) {
+  if constexpr (epi_adds_bias(EPI)) {
     if (p.bias_layout == BIAS_COL) {
 #pragma unroll
       for (int j = 0; j < FN; ++j)
@@ -241,14 +244,16 @@ __device__ __forceinline__ void epilogue_store(const GemmArgs& p, f32x16 (&acc)[
   const uint32_t mrow = (uint32_t)N / 8u;
   uint8_t* const mstage = stage + 32 * ROWB;
   const bool mask_rows = n0 + wn0 + 32 * FN <= N && mrow % (4u * FN) == 0;
-  const auto rM = make_rsrc(EPI == EPI_RELU_AUX ? (uint8_t*)p.aux + (size_t)m0 * mrow : (uint8_t*)p.D,
-                            EPI == EPI_RELU_AUX ? (uint64_t)(M - m0) * mrow : 0);
+  // the mask rows of this tile: written by RELU_AUX, read by the backward epilogues
+  constexpr bool kMask = EPI == EPI_RELU_AUX || epi_reads_mask(EPI);
+  const auto rM = make_rsrc(kMask ? (uint8_t*)p.aux + (size_t)m0 * mrow : (uint8_t*)p.D,
+                            kMask ? (uint64_t)(M - m0) * mrow : 0);
 
 #pragma unroll
   for (int i = 0; i < FM; ++i) {
     const uint32_t lrow = wm0 + 32 * i + lr;  // row within the tile
     float brow = 0.0f;
-    if constexpr (EPI != EPI_NONE) {
+    if constexpr (epi_adds_bias(EPI)) {
       if (p.bias_layout == BIAS_ROW) {
         const auto rbias = make_rsrc(p.bias, (uint64_t)M * 2);
         const int row = m0 + (int)lrow;
@@ -258,6 +263,25 @@ __device__ __forceinline__ void epilogue_store(const GemmArgs& p, f32x16 (&acc)[
 #pragma unroll
     for (int j = 0; j < FN; ++j) {
       uint32_t mword = 0;
+      // backward: the forward mask word of this row's 32 columns wn0+32j .. +31
+      // (bit 8g + 4lh + e belongs to this lane's column 8g + 4lh + e)
+      uint32_t keep = 0;
+      if constexpr (epi_reads_mask(EPI)) {
+        const int cb = n0 + wn0 + 32 * j;
+        const uint32_t mo = lrow * mrow + (uint32_t)cb / 8u;
+        if ((mrow & 3u) == 0) {
+          keep = buf_load4(rM, mo);  // 4-byte aligned: the word is one load
+        } else {
+#pragma unroll
+          for (int b = 0; b < 4; ++b)
+            keep |= (uint32_t)buf_load1(rM, cb + 8 * b < N ? mo + b : OOB_OFFSET) << (8 * b);
+        }
+      }
+      // bias gradient partial sums of this 32 x 32 block: per column (over the
+      // lane's row, reduced across rows below) or per row (over the lane's
+      // columns, reduced across the two half-waves below)
+      float csum[4][4];
+      float rsum = 0.0f;
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
         const int col = n0 + wn0 + 32 * j + 8 * g + 4 * lh;
@@ -266,7 +290,12 @@ __device__ __forceinline__ void epilogue_store(const GemmArgs& p, f32x16 (&acc)[
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           z[e] = acc[i][j][4 * g + e];
-          if constexpr (EPI != EPI_NONE) z[e] += brow + bcol[j][g][e];
+          if constexpr (epi_adds_bias(EPI)) z[e] += brow + bcol[j][g][e];
+          if constexpr (epi_reads_mask(EPI)) z[e] = ((keep >> (8 * g + 4 * lh + e)) & 1u) ? z[e] : 0.0f;
+          if constexpr (EPI == EPI_DRELU_BGRAD) {
+            csum[g][e] = z[e];
+            rsum += z[e];
+          }
         }
         if constexpr (EPI == EPI_RESID) {
           const u32x2 rv = buf_load8(rR, off);
@@ -284,6 +313,36 @@ __device__ __forceinline__ void epilogue_store(const GemmArgs& p, f32x16 (&acc)[
         for (int e = 0; e < 4; ++e) y[e] = activate<EPI>(z[e]);
         const uint32_t slot = (uint32_t)(8 * j + 2 * g + lh);
         *(u32x2*)(stage + lr * ROWB + ((slot ^ xr(lr)) << 3)) = u32x2{pack2<DT>(y[0], y[1]), pack2<DT>(y[2], y[3])};
+      }
+      if constexpr (EPI == EPI_DRELU_BGRAD) {
+        if (p.bias_layout == BIAS_COL) {
+          // sum the block's 32 rows: lanes lr and lr^s (s < 32) share columns
+#pragma unroll
+          for (int s = 1; s < 32; s <<= 1)
+#pragma unroll
+            for (int g = 0; g < 4; ++g)
+#pragma unroll
+              for (int e = 0; e < 4; ++e) csum[g][e] += __shfl_xor(csum[g][e], s);
+          const int rb = m0 + wm0 + 32 * i;  // first row of the block
+          if (lr == 0) {
+            const auto rP = make_rsrc(p.partial + (size_t)(rb / 32) * N, rb < M ? (uint64_t)N * 4 : 0);
+#pragma unroll
+            for (int g = 0; g < 4; ++g) {
+              const int col = n0 + wn0 + 32 * j + 8 * g + 4 * lh;
+              buf_store16(u32x4{__builtin_bit_cast(uint32_t, csum[g][0]), __builtin_bit_cast(uint32_t, csum[g][1]),
+                                __builtin_bit_cast(uint32_t, csum[g][2]), __builtin_bit_cast(uint32_t, csum[g][3])},
+                          rP, col < N ? (uint32_t)col * 4u : OOB_OFFSET);
+            }
+          }
+        } else {
+          // sum the block's 32 columns: the two half-waves hold the other 16
+          rsum += __shfl_xor(rsum, 32);
+          const int cb = n0 + wn0 + 32 * j;  // first column of the block
+          if (lh == 0) {
+            const auto rP = make_rsrc(p.partial + (size_t)(cb / 32) * M + m0, cb < N ? (uint64_t)(M - m0) * 4 : 0);
+            buf_store4(__builtin_bit_cast(uint32_t, rsum), rP, lrow * 4u);
+          }
+        }
       }
       if constexpr (EPI == EPI_RELU_AUX) {
         // lanes l and l+32 hold complementary nibbles of the same row's 32 columns
@@ -352,7 +411,7 @@ __global__ void __launch_bounds__(C::NT, 1) gemm_epilogue_kernel(GemmArgs p) {
   // A (1,n) bias: wave 0 copies the tile's BN values straight into LDS ahead
   // of the operand loads (its completion is covered by the prologue's wait;
   // lanes past BN/8 write zeros).  A (m,1) bias is read in the epilogue.
-  if constexpr (EPI != EPI_NONE) {
+  if constexpr (epi_adds_bias(EPI)) {
     if (p.bias_layout == BIAS_COL && wave == 0) {
       const uint32_t c = (uint32_t)n0 + 8u * (uint32_t)lane;  // n is a multiple of 8: whole 16-byte pieces
       dma16(make_srd(p.bias, (uint64_t)N * 2), smem_lds + C::LDS_BYTES,

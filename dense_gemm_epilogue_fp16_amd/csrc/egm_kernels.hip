@@ -26,6 +26,10 @@ void launch_epi(dim3 grid, hipStream_t s, const EpiArgs& a) {
   hipLaunchKernelGGL((epilogue_kernel<DT, EPI>), grid, dim3(256), 0, s, a);
 }
 
+void launch_partials(dim3 grid, hipStream_t s, const void* D, int64_t M, int32_t N, int32_t layout, float* partial) {
+  hipLaunchKernelGGL((axis_partials_kernel<DT>), grid, dim3(256), 0, s, D, M, N, layout, partial);
+}
+
 template <int EPI>
 GemmLaunch gemm_row(int cfg) {
   static_assert(kNumConfigs == 5, "update the launch table with the config table");
@@ -47,6 +51,8 @@ GemmLaunch gemm_table(int epi, int cfg) {
     case EPI_GELU: return gemm_row<EPI_GELU>(cfg);
     case EPI_RELU_AUX: return gemm_row<EPI_RELU_AUX>(cfg);
     case EPI_RESID: return gemm_row<EPI_RESID>(cfg);
+    case EPI_DRELU: return gemm_row<EPI_DRELU>(cfg);
+    case EPI_DRELU_BGRAD: return gemm_row<EPI_DRELU_BGRAD>(cfg);
     default: return nullptr;
   }
 }
@@ -58,6 +64,7 @@ EpiLaunch epi_table(int epi) {
     case EPI_GELU: return &launch_epi<EPI_GELU>;
     case EPI_RELU_AUX: return &launch_epi<EPI_RELU_AUX>;
     case EPI_RESID: return &launch_epi<EPI_RESID>;
+    case EPI_DRELU: return &launch_epi<EPI_DRELU>;
     default: return nullptr;
   }
 }
@@ -67,9 +74,15 @@ EpiLaunch epi_table(int epi) {
 #if EGM_DTYPE == 0
 GemmLaunch gemm_launcher_f16(int epi, int cfg) { return gemm_table(epi, cfg); }
 EpiLaunch epi_launcher_f16(int epi) { return epi_table(epi); }
+PartialsLaunch partials_launcher_f16() { return &launch_partials; }
+void launch_bias_grad_finish(dim3 grid, hipStream_t s, const float* partial, int64_t chunks, int64_t len,
+                             float* out) {
+  hipLaunchKernelGGL(bias_grad_finish_kernel<float>, grid, dim3(256), 0, s, partial, chunks, len, out);
+}
 #else
 GemmLaunch gemm_launcher_bf16(int epi, int cfg) { return gemm_table(epi, cfg); }
 EpiLaunch epi_launcher_bf16(int epi) { return epi_table(epi); }
+PartialsLaunch partials_launcher_bf16() { return &launch_partials; }
 #endif
 
 }  // namespace egm

@@ -36,16 +36,25 @@ inline constexpr int kNumConfigs = int(sizeof(kConfigs) / sizeof(kConfigs[0]));
 
 using GemmLaunch = void (*)(dim3 grid, hipStream_t stream, const GemmArgs& args);
 using EpiLaunch = void (*)(dim3 grid, hipStream_t stream, const EpiArgs& args);
+// bias gradient of the two-kernel path: partial sums of D (see axis_partials_kernel)
+using PartialsLaunch = void (*)(dim3 grid, hipStream_t stream, const void* D, int64_t M, int32_t N,
+                                int32_t layout, float* partial);
 
 // Defined in egm_kernels.hip (compiled once per dtype).
 GemmLaunch gemm_launcher_f16(int epi, int cfg);
 GemmLaunch gemm_launcher_bf16(int epi, int cfg);
 EpiLaunch epi_launcher_f16(int epi);
 EpiLaunch epi_launcher_bf16(int epi);
+PartialsLaunch partials_launcher_f16();
+PartialsLaunch partials_launcher_bf16();
+// the last step of every bias gradient (dtype-independent; in the fp16 unit)
+void launch_bias_grad_finish(dim3 grid, hipStream_t stream, const float* partial, int64_t chunks, int64_t len,
+                             float* out);
 
 inline GemmLaunch gemm_launcher(int dt, int epi, int cfg) {
   return dt == DT_F16 ? gemm_launcher_f16(epi, cfg) : gemm_launcher_bf16(epi, cfg);
 }
 inline EpiLaunch epi_launcher(int dt, int epi) { return dt == DT_F16 ? epi_launcher_f16(epi) : epi_launcher_bf16(epi); }
+inline PartialsLaunch partials_launcher(int dt) { return dt == DT_F16 ? partials_launcher_f16() : partials_launcher_bf16(); }
 
 }  // namespace egm

@@ -49,7 +49,7 @@
 extern "C" {
 #endif
 
-#define EGM_ABI_VERSION 1
+#define EGM_ABI_VERSION 2
 
 typedef enum egm_status_t {
   EGM_OK = 0,
@@ -81,6 +81,19 @@ typedef enum egm_dtype_t {
  *                                             [bias-fusion] body, limitations
  *                                             paragraph (mask for backward)
  *   BIAS_RESIDUAL  D = Z + R, R [m,n] row-major   [op-fusion] §三
+ *
+ * Backward epilogues (consumers of the RELU_AUX_BIAS mask; [bias-fusion] body:
+ * the training paragraph (the forward must leave the mask backward needs) and
+ * the closing paragraph (dBias as an epilogue to come)).  Here A.B is the
+ * gradient reaching the ReLU output, dZ its part that passes the ReLU:
+ *   DRELU          D = dZ = (A.B) where the mask bit is 1, else 0
+ *                  (aux at execute is the INPUT mask, as RELU_AUX_BIAS wrote it)
+ *   DRELU_BGRAD    D as DRELU, and the bias gradient of the forward bias:
+ *                  bias_layout COL ((1,n) bias): grad[j] = sum_i dZ[i,j], n values;
+ *                  bias_layout ROW ((m,1) bias): grad[i] = sum_j dZ[i,j], m values;
+ *                  summed in fp32 from the unrounded dZ, written as fp32 to
+ *                  egm_epilog_inputs_t.bias_grad
+ * No bias is added in either backward epilogue.
  */
 typedef enum egm_epilog_t {
   EGM_EPILOG_DEFAULT = 0,
@@ -88,7 +101,9 @@ typedef enum egm_epilog_t {
   EGM_EPILOG_RELU_BIAS = 2,
   EGM_EPILOG_GELU_BIAS = 3,
   EGM_EPILOG_RELU_AUX_BIAS = 4,
-  EGM_EPILOG_BIAS_RESIDUAL = 5
+  EGM_EPILOG_BIAS_RESIDUAL = 5,
+  EGM_EPILOG_DRELU = 6,
+  EGM_EPILOG_DRELU_BGRAD = 7
 } egm_epilog_t;
 
 /* Bias shapes accepted by the pages ([bias-fusion] body, shape item of the
@@ -100,11 +115,15 @@ typedef enum egm_bias_layout_t {
 } egm_bias_layout_t;
 
 /* Named epilog operands (the pages' epilog_inputs dict).  Device pointers,
- * caller-owned, 16-byte aligned, in the plan's dtype. */
+ * caller-owned, 16-byte aligned, in the plan's dtype unless stated. */
 typedef struct egm_epilog_inputs_t {
-  const void* bias;      /* required for every epilog except DEFAULT */
-  int32_t bias_layout;   /* egm_bias_layout_t */
+  const void* bias;      /* required for BIAS .. BIAS_RESIDUAL; NULL for DEFAULT and
+                            the backward epilogues */
+  int32_t bias_layout;   /* egm_bias_layout_t; for DRELU_BGRAD it selects the
+                            gradient's axis (ROW: m values, COL: n values) */
   const void* residual;  /* [m,n] row-major; required iff BIAS_RESIDUAL, else NULL */
+  void* bias_grad;       /* OUTPUT, fp32 (not the plan's dtype), m or n values;
+                            required iff DRELU_BGRAD, else NULL */
 } egm_epilog_inputs_t;
 
 /* Plan options ([bias-fusion] checklist: autotuning through options). */
@@ -131,8 +150,9 @@ typedef struct egm_plan_s* egm_plan_t;
  *           empty problem (execute does nothing); k == 0 gives D = epilogue(bias).
  *   dtype   EGM_F16 or EGM_BF16, shared by every operand and the output.
  *   epilog  egm_epilog_t.
- *   in      epilog inputs (may be NULL only for DEFAULT).  RELU_AUX_BIAS needs
- *           n % 8 == 0 (already required) for whole mask bytes.
+ *   in      epilog inputs (may be NULL for DEFAULT and DRELU).  RELU_AUX_BIAS
+ *           and the backward epilogues need n % 8 == 0 (already required) for
+ *           whole mask bytes.
  *   opt     NULL for defaults.
  * No device work and no HIP call.
  */
@@ -144,14 +164,20 @@ egm_status_t egm_plan(egm_plan_t* out, int64_t m, int64_t n, int64_t k, egm_dtyp
  * egm_execute - enqueue the plan on a HIP stream (asynchronous).
  *   A     [m,k] device, row-major.          B [k,n] device, row-major.
  *   D     [m,n] device, row-major output.
- *   aux   [m, n/8] uint8 device output, required iff RELU_AUX_BIAS, else NULL.
+ *   aux   [m, n/8] uint8 device mask: the OUTPUT of RELU_AUX_BIAS and the INPUT
+ *         of DRELU / DRELU_BGRAD; required for those three, else NULL.
  *         Bit (j%8) of byte aux[i*(n/8) + j/8] is 1 iff Z[i,j] > 0 (strict;
  *         least-significant bit = lowest column).
  *   workspace, workspace_bytes: scratch of at least egm_plan_workspace_bytes()
- *         (0 for a fused plan, m*n*2 for the two-kernel path); may be NULL when
- *         that is 0.
+ *         (0 for a fused forward plan; per-tile fp32 partial sums for
+ *         DRELU_BGRAD; plus m*n*2 bytes for the product on the two-kernel
+ *         path); may be NULL when that is 0.  Its contents need no
+ *         initialisation and are garbage afterwards.
  *   stream  a hipStream_t (NULL = the null stream).
- * All pointers 16-byte aligned.  A, B, bias, residual must not alias D or aux.
+ * All pointers 16-byte aligned.  A, B, bias, residual must not alias D or aux;
+ * the bias gradient must not alias anything else.  DRELU_BGRAD is two
+ * launches on the stream (the GEMM with its per-tile sums, then their
+ * reduction); the result is deterministic for a given plan.
  */
 egm_status_t egm_execute(egm_plan_t plan, const void* A, const void* B, void* D, void* aux,
                          void* workspace, size_t workspace_bytes, void* stream);

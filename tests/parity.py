@@ -87,3 +87,42 @@ def compare(d_bits, y, dtype, *, z=None, mask=None, mask_ref=None, unfused=False
 def exact_bits(y, dtype):
     """The single correct rounding of an exact oracle result (integer tests)."""
     return eo.round_to_bits(y, dtype)
+
+
+def run_backward(ops, epilog, mask, layout=None, *, fused=True, force_config=-1):
+    """Run DRELU / DRELU_BGRAD on Operands (A.B is the incoming gradient) with
+    a host mask [m, n/8]; returns (D bits, bias gradient as float64 or None)."""
+    import torch
+    import dense_gemm_epilogue_fp16_amd as egm
+    a, b = to_device(ops.a, ops.dtype), to_device(ops.b, ops.dtype)
+    aux = torch.from_numpy(np.ascontiguousarray(mask, dtype=np.uint8)).cuda()
+    ins = {}
+    if epilog == "DRELU_BGRAD":
+        shape = (ops.m, 1) if layout == "row" else (1, ops.n)
+        # poisoned: every value must be written by the library
+        ins["bias_grad"] = torch.full(shape, float("nan"), dtype=torch.float32, device="cuda")
+    with egm.Matmul(a, b) as mm:
+        mm.plan(epilog=epilog, epilog_inputs=ins, fused=fused, force_config=force_config)
+        out = mm.execute(aux=aux)
+        torch.cuda.synchronize()
+    if isinstance(out, tuple):
+        return to_host_bits(out[0]), out[1].double().cpu().numpy().reshape(-1)
+    return to_host_bits(out), None
+
+
+def compare_bias_grad(got, want, bound, *, d_ref=None, dtype=None, layout=None):
+    """The bias gradient against the oracle within its fp32 error bound; for
+    the two-kernel path (sums of the rounded D) pass the oracle dZ so the
+    rounding of each summed value (half an ulp) widens the bound."""
+    assert got.shape == want.shape, (got.shape, want.shape)
+    assert np.isfinite(got).all(), "non-finite bias gradient"
+    b = bound.copy()
+    if d_ref is not None:
+        b = b + eo.bias_grad(0.5 * eo.ulp(d_ref, dtype) * (d_ref != 0), layout)
+    err = np.abs(got - want)
+    bad = err > b
+    if bad.any():
+        i = int(np.argwhere(bad)[0][0])
+        raise AssertionError(f"{int(bad.sum())} of {err.size} bias-gradient values exceed the bound; first at {i}: "
+                             f"got={got[i]!r} want={want[i]!r} bound={b[i]:.3g}")
+    return {"max_abs_err": float(err.max()) if err.size else 0.0}

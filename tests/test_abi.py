@@ -32,7 +32,7 @@ def test_every_declared_symbol_is_exported():
 
 
 def test_abi_version_and_status_strings():
-    assert egm.egm_abi_version() == 1
+    assert egm.egm_abi_version() == 2
     for s in range(10):
         assert egm.status_string(s).startswith("EGM_")
     assert "unknown" in egm.status_string(12345)
@@ -56,7 +56,17 @@ def plan_status(m=64, n=64, k=64, dtype=F16, epilog="BIAS", bias=FAKE, layout=RO
     (dict(n=1 << 21, k=1 << 21), egm.EGM_OK),
     (dict(m=1 << 31), egm.EGM_ERR_SHAPE),
     (dict(dtype=2), egm.EGM_ERR_DTYPE),
-    (dict(epilog=6), egm.EGM_ERR_INVALID_VALUE),
+    (dict(epilog=8), egm.EGM_ERR_INVALID_VALUE),
+    (dict(epilog="DRELU", bias=0, layout=0), egm.EGM_OK),
+    (dict(epilog="DRELU"), egm.EGM_ERR_INVALID_VALUE),            # no bias in the backward epilogues
+    (dict(epilog="DRELU", bias=0, layout=0, bias_grad=FAKE), egm.EGM_ERR_INVALID_VALUE),
+    (dict(epilog="DRELU_BGRAD", bias=0, bias_grad=FAKE), egm.EGM_OK),
+    (dict(epilog="DRELU_BGRAD", bias=0, layout=COL, bias_grad=FAKE), egm.EGM_OK),
+    (dict(epilog="DRELU_BGRAD", bias=0, bias_grad=0), egm.EGM_ERR_INVALID_VALUE),
+    (dict(epilog="DRELU_BGRAD", bias=0, layout=0, bias_grad=FAKE), egm.EGM_ERR_SHAPE),
+    (dict(epilog="DRELU_BGRAD", bias=0, bias_grad=FAKE + 4), egm.EGM_ERR_ALIGNMENT),
+    (dict(epilog="DRELU_BGRAD", bias_grad=FAKE), egm.EGM_ERR_INVALID_VALUE),   # a bias as well
+    (dict(epilog="BIAS", bias_grad=FAKE), egm.EGM_ERR_INVALID_VALUE),
     (dict(epilog=-1), egm.EGM_ERR_INVALID_VALUE),
     (dict(bias=0), egm.EGM_ERR_INVALID_VALUE),
     (dict(layout=0), egm.EGM_ERR_SHAPE),
@@ -197,3 +207,29 @@ def test_matmul_wrapper_rejects_without_gpu():
     a = torch.zeros(8, 8, dtype=torch.float16)
     with pytest.raises(ValueError):
         egm.Matmul(a, a)  # CPU tensors are not device memory
+
+
+def test_backward_workspace_and_execute_validation():
+    # fused DRELU_BGRAD: fp32 partial sums, one row per 32-row block of a (1,n) bias
+    h = egm.egm_plan(100, 64, 32, BF16, E["DRELU_BGRAD"], 0, COL, bias_grad=FAKE)
+    try:
+        assert egm.egm_plan_workspace_bytes(h) == 4 * 64 * 4  # ceil(100/32) = 4 blocks x n x fp32
+        assert "DRELU_BGRAD" in egm.egm_plan_describe(h)
+        # the forward mask is an input here: required
+        assert egm.egm_execute(h, FAKE, FAKE, FAKE, 0, FAKE, 4096, raw_status=True) == egm.EGM_ERR_INVALID_VALUE
+        assert egm.egm_execute(h, FAKE, FAKE, FAKE, FAKE, 0, 0, raw_status=True) == egm.EGM_ERR_WORKSPACE
+    finally:
+        egm.egm_free(h)
+    # (m,1) gradient: one row of m per 32-column block; the two-kernel path adds P in front
+    h = egm.egm_plan(100, 72, 32, F16, E["DRELU_BGRAD"], 0, ROW, bias_grad=FAKE, fused=0)
+    try:
+        p_bytes = (100 * 72 * 2 + 255) // 256 * 256
+        assert egm.egm_plan_workspace_bytes(h) == p_bytes + 3 * 100 * 4  # ceil(72/32) = 3 blocks x m
+    finally:
+        egm.egm_free(h)
+    h = egm.egm_plan(64, 64, 64, F16, E["DRELU"], 0, 0)
+    try:
+        assert egm.egm_plan_workspace_bytes(h) == 0
+        assert egm.egm_execute(h, FAKE, FAKE, FAKE, 0, raw_status=True) == egm.EGM_ERR_INVALID_VALUE
+    finally:
+        egm.egm_free(h)

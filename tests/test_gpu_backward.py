@@ -1,0 +1,122 @@
+"""Backward epilogues on the GPU against the CPU oracle, through the C ABI:
+DRELU (the forward ReLU mask applied to the incoming gradient A.B) and
+DRELU_BGRAD (plus the bias gradient).  The mask comes from the seeded
+generator or from the GPU's own forward RELU_AUX_BIAS."""
+import numpy as np
+import pytest
+
+import egm_workloads as W
+from oracle import egm_oracle as eo
+from parity import compare, compare_bias_grad, exact_bits, run, run_backward, to_host_bits
+
+pytestmark = pytest.mark.gpu
+
+CONFIGS = (0, 1, 2, 3, 4)
+RAGGED = (300, 264, 136)
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    import torch
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import dense_gemm_epilogue_fp16_amd  # noqa: F401  (fails loudly without libegm.so)
+
+
+def random_mask(m, n, seed):
+    return np.random.default_rng(seed).integers(0, 256, size=(m, n // 8), dtype=np.uint8)
+
+
+@pytest.mark.parametrize("fused", [True, False])
+@pytest.mark.parametrize("cfg", CONFIGS)
+@pytest.mark.parametrize("dtype", ["fp16", "bf16"])
+def test_integer_exact(dtype, cfg, fused):
+    """Integer gradients: D and both bias gradients exact, bit for bit."""
+    m, n, k = RAGGED
+    ops = W.integer_operands(m, n, k, dtype, seed=cfg + 40)
+    mask = random_mask(m, n, cfg)
+    dz, _, _ = eo.backward_reference(ops.a, ops.b, dtype, "DRELU", mask)
+    d, none = run_backward(ops, "DRELU", mask, force_config=cfg, fused=fused)
+    assert none is None and np.array_equal(d, exact_bits(dz, dtype))
+    for layout in ("row", "col"):
+        _, grad_ref, _ = eo.backward_reference(ops.a, ops.b, dtype, "DRELU_BGRAD", mask, layout)
+        d, grad = run_backward(ops, "DRELU_BGRAD", mask, layout, force_config=cfg, fused=fused)
+        assert np.array_equal(d, exact_bits(dz, dtype))
+        assert np.array_equal(grad, grad_ref), layout
+
+
+@pytest.mark.parametrize("cfg", CONFIGS)
+@pytest.mark.parametrize("dtype", ["fp16", "bf16"])
+def test_normal_within_bounds(dtype, cfg):
+    m, n, k = 520, 392, 328
+    ops = W.gemm_operands(m, n, k, dtype, seed=60 + cfg, a_std=0.7, b_std=1.0 / np.sqrt(k), bias_layout="col")
+    mask = random_mask(m, n, 100 + cfg)
+    for layout in ("row", "col"):
+        dz, grad_ref, bound = eo.backward_reference(ops.a, ops.b, dtype, "DRELU_BGRAD", mask, layout)
+        d, grad = run_backward(ops, "DRELU_BGRAD", mask, layout, force_config=cfg)
+        compare(d, dz, dtype)
+        compare_bias_grad(grad, grad_ref, bound)
+        d2, grad2 = run_backward(ops, "DRELU_BGRAD", mask, layout, force_config=cfg, fused=False)
+        compare(d2, dz, dtype, unfused=True)
+        compare_bias_grad(grad2, grad_ref, bound, d_ref=dz, dtype=dtype, layout=layout)
+
+
+@pytest.mark.parametrize("dtype", ["fp16", "bf16"])
+def test_mask_from_gpu_forward(dtype):
+    """The chain a training step runs: forward RELU_AUX_BIAS on the GPU, then
+    the backward epilogue consuming that mask; checked against the oracle fed
+    the GPU's mask (and that mask against the forward oracle)."""
+    m, n, k = 264, 136, 200
+    fwd = W.gemm_operands(m, n, k, dtype, seed=77, a_std=1.0, b_std=1.0 / np.sqrt(k), bias_layout="col",
+                          bias_std=0.5)
+    d_fwd, mask = run(fwd, "RELU_AUX_BIAS")
+    y, z, mref = eo.reference(fwd.a, fwd.b, dtype, "RELU_AUX_BIAS", fwd.bias, "col")
+    compare(d_fwd, y, dtype, z=z, mask=mask, mask_ref=mref)
+    grad_ops = W.gemm_operands(m, n, 96, dtype, seed=78, a_std=0.7, b_std=1.0 / np.sqrt(96), bias_layout="col")
+    dz, grad_ref, bound = eo.backward_reference(grad_ops.a, grad_ops.b, dtype, "DRELU_BGRAD", mask, "col")
+    d, grad = run_backward(grad_ops, "DRELU_BGRAD", mask, "col")
+    compare(d, dz, dtype)
+    compare_bias_grad(grad, grad_ref, bound)
+    # the gradient is zero exactly where the forward ReLU cut
+    assert not eo.widen(d, dtype)[~eo.unpack_mask(mask, n)].any()
+
+
+def test_edges_and_empty():
+    import torch
+    import dense_gemm_epilogue_fp16_amd as egm
+    for (m, n, k) in [(1, 8, 8), (33, 8, 16), (7, 24, 520), (40, 72, 0)]:
+        for dtype in ("fp16", "bf16"):
+            ops = W.gemm_operands(m, n, k, dtype, seed=m + n + k, a_std=1.0, bias_layout="col")
+            mask = random_mask(m, n, m * n)
+            for layout in ("row", "col"):
+                dz, grad_ref, bound = eo.backward_reference(ops.a, ops.b, dtype, "DRELU_BGRAD", mask, layout)
+                if k == 0:
+                    a = torch.empty((m, 0), dtype=torch.float16 if dtype == "fp16" else torch.bfloat16, device="cuda")
+                    b = torch.empty((0, n), dtype=a.dtype, device="cuda")
+                    g = torch.full((m, 1) if layout == "row" else (1, n), float("nan"), device="cuda")
+                    with egm.Matmul(a, b) as mm:
+                        mm.plan("DRELU_BGRAD", {"bias_grad": g})
+                        d, grad = mm.execute(aux=torch.from_numpy(mask).cuda())
+                    torch.cuda.synchronize()
+                    assert not eo.widen(to_host_bits(d), dtype).any() and not grad.cpu().numpy().any()
+                    continue
+                d, grad = run_backward(ops, "DRELU_BGRAD", mask, layout)
+                compare(d, dz, dtype)
+                compare_bias_grad(grad, grad_ref, bound)
+    # an empty m: the (1,n) gradient is a sum over no rows, all zeros
+    a = torch.empty((0, 64), dtype=torch.float16, device="cuda")
+    b = torch.zeros((64, 16), dtype=torch.float16, device="cuda")
+    g = torch.full((1, 16), float("nan"), device="cuda")
+    with egm.Matmul(a, b) as mm:
+        mm.plan("DRELU_BGRAD", {"bias_grad": g})
+        d, grad = mm.execute(aux=torch.empty((0, 2), dtype=torch.uint8, device="cuda"))
+    torch.cuda.synchronize()
+    assert d.shape == (0, 16) and not grad.cpu().numpy().any()
+
+
+def test_deterministic_gradient():
+    ops = W.gemm_operands(1000, 520, 264, "bf16", seed=9, bias_layout="col")
+    mask = random_mask(1000, 520, 5)
+    _, g1 = run_backward(ops, "DRELU_BGRAD", mask, "col")
+    _, g2 = run_backward(ops, "DRELU_BGRAD", mask, "col")
+    assert np.array_equal(g1, g2)
