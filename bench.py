@@ -61,8 +61,15 @@ def traffic_from_profile(workload: str):
 
 
 def algorithmic_bytes(m, n, k, epilog, bias_layout):
-    """Fused path: read A, B, bias (+R) once, write D (+mask) once."""
+    """Fused path: read A, B, bias (+R) once, write D (+mask) once; the
+    backward epilogues read the mask instead of a bias and (BGRAD) write the
+    fp32 bias gradient."""
     b = 2 * (m * k + k * n + m * n)
+    if epilog in ("DRELU", "DRELU_BGRAD"):
+        b += m * n // 8
+        if epilog == "DRELU_BGRAD":
+            b += 4 * (m if bias_layout == "row" else n)
+        return b
     b += 2 * (m if bias_layout == "row" else n)
     if epilog == "BIAS_RESIDUAL":
         b += 2 * m * n
@@ -87,6 +94,9 @@ def main():
     ap.add_argument("--cold", action="store_true",
                     help="also time single steps with the caches flushed (a 512 MiB write between steps, outside "
                          "the events), and the host-side latency of one launch plus synchronize")
+    ap.add_argument("--torch-context", action="store_true",
+                    help="also time torch.matmul (the vendor GEMM, no epilogue) and torch's eager "
+                         "matmul + bias + activation on the same operands, with the same warm-up and step counts")
     ap.add_argument("--sustain", type=float, default=0.0,
                     help="instead of the bench line: run the fused step back to back for this many seconds and "
                          "print one JSON line per second with its throughput and the board power and clocks "
@@ -120,9 +130,21 @@ def main():
 
     t_setup = time.time()
     name = args.workload
-    wl = W.WORKLOADS[name]
+    wl = W.WORKLOADS[name] if name in W.WORKLOADS else W.BACKWARD_WORKLOADS[name]
     keep = []
-    if name.startswith("ffn_"):
+    if name in W.BACKWARD_WORKLOADS:
+        ops, mask = W.backward_operands(name)
+        a = to_dev(ops.a, ops.dtype, (ops.m, ops.k))
+        b = to_dev(ops.b, ops.dtype, (ops.k, ops.n))
+        aux = torch.from_numpy(mask).to(dev)
+        grad = torch.empty((1, ops.n) if wl.bias_layout == "col" else (ops.m, 1), dtype=torch.float32, device=dev)
+        d = torch.empty((ops.m, ops.n), dtype=a.dtype, device=dev)
+        specs = [((a, b), wl.epilogs[-1], {"bias_grad": grad}, dict(out=d, aux=aux), (ops.m, ops.n, ops.k),
+                  wl.bias_layout)]
+        keep += [a, b, d, aux, grad]
+        host_ops = ops
+        host_ops.meta["mask"] = mask
+    elif name.startswith("ffn_"):
         f = W.ffn_operands()
         x = to_dev(f.x, "bf16", (f.tokens, f.hidden))
         w1 = to_dev(f.w1, "bf16", (f.hidden, f.ffn))
@@ -227,7 +249,8 @@ def main():
 
     value = flops / (fused_ms * 1e-3) / 1e12
     alg = sum(algorithmic_bytes(m, n, k, ep, lay) for _, _, (m, n, k), ep, lay in fused_plans)
-    extra = sum(4 * m * n for _, _, (m, n, k), _, _ in fused_plans)  # P written and read back
+    # P written and read back (+ D read again for the two-kernel bias gradient)
+    extra = sum((6 if ep == "DRELU_BGRAD" else 4) * m * n for _, _, (m, n, k), ep, _ in fused_plans)
     result = {
         "metric": "fused GEMM+epilogue TFLOP/s (fp16/bf16 MFMA, fp32 accumulate)",
         "value": round(value, 2),
@@ -258,6 +281,9 @@ def main():
         "timed_wall_s": round(fused_wall, 3),
     }
 
+    if args.torch_context:
+        result["torch_context"] = torch_context(specs, timed, steps, warmup, flops)
+
     if args.cold:
         result["cold_cache"] = cold_and_latency(lambda: step(fused_plans), lambda: step(unfused_plans),
                                                 flops, alg, dev, stream)
@@ -268,6 +294,60 @@ def main():
     for mm, *_ in fused_plans + unfused_plans:
         mm.free()
     print(json.dumps(result), flush=True)
+
+
+def torch_context(specs, timed, steps, warmup, flops):
+    """torch.matmul alone, and torch's eager matmul + bias + activation (+ residual),
+    timed like the fused step: context for the fused kernel, not a code path of
+    the library."""
+    import torch
+
+    keep_cache = {}
+
+    def eager(spec, with_epilogue):
+        (aa, bb), ep, ins, out, _, _ = spec
+        y = torch.matmul(aa, bb)
+        if with_epilogue and ep in ("DRELU", "DRELU_BGRAD"):
+            # eager backward: the mask as a bool tensor (unpacked once, outside
+            # the timing), the product masked, then the bias gradient
+            aux = out["aux"]
+            if id(aux) not in keep_cache:
+                bits = torch.arange(8, device=aux.device, dtype=torch.uint8)
+                keep_cache[id(aux)] = ((aux.unsqueeze(-1) >> bits) & 1).bool().reshape(aa.shape[0], -1)
+            dz = y * keep_cache[id(aux)]
+            if ep == "DRELU_BGRAD":
+                dz.sum(dim=0 if ins["bias_grad"].shape[0] == 1 else 1, dtype=torch.float32)
+            return dz
+        if with_epilogue:
+            y = y + ins["bias"]
+            if ep in ("RELU_BIAS", "RELU_AUX_BIAS"):
+                y = torch.relu(y)
+                if ep == "RELU_AUX_BIAS":
+                    (y > 0)  # the predicate pass a backward mask needs (unpacked)
+            elif ep == "GELU_BIAS":
+                y = torch.nn.functional.gelu(y, approximate="tanh")
+            elif ep == "BIAS_RESIDUAL":
+                y = y + ins["residual"]
+        return y
+
+    res = {}
+    for label, with_epi in (("matmul_ms", False), ("matmul_bias_act_ms", True)):
+        runner = [lambda sp=spec, w=with_epi: eager(sp, w) for spec in specs]
+        ms, _ = _timed_callables(runner, timed, steps, warmup)
+        res[label] = round(ms, 5)
+    res["matmul_tflops"] = round(flops / (res["matmul_ms"] * 1e-3) / 1e12, 2)
+    res["note"] = "torch.matmul is the vendor GEMM (hipBLASLt); the second figure is the eager op sequence"
+    return res
+
+
+def _timed_callables(runner, timed, steps, warmup):
+    class _Plan:
+        def __init__(self, fn):
+            self.fn = fn
+
+        def execute(self, **_):
+            self.fn()
+    return timed([(_Plan(fn), {}, None, None, None) for fn in runner], steps, warmup)
 
 
 def cold_and_latency(run_fused, run_unfused, flops, alg_bytes, dev, stream, reps=30):
@@ -422,6 +502,39 @@ def ingest_pmc(workload, fetch_dir, write_dir, copy_mib):
     print(json.dumps(out, indent=1))
 
 
+def _cpu_baseline_backward(name, ops, keep, target_s, cores):
+    """The backward oracle (DRELU part) on a row sample; checks the GPU's D on
+    those rows.  The bias gradient needs every row and is not sampled."""
+    import numpy as np
+    import torch
+
+    import egm_workloads as W
+    from oracle import egm_oracle as eo
+    mask = ops.meta["mask"]
+    times = {}
+    for cnt in (64, 192):
+        rows = W.sample_rows(ops.m, min(ops.m, cnt), seed=2)
+        t0 = time.perf_counter()
+        eo.backward_reference(ops.a[rows], ops.b, ops.dtype, "DRELU", mask[rows])
+        times[cnt] = time.perf_counter() - t0
+    per_row = max((times[192] - times[64]) / 128.0, 1e-6)
+    fixed = max(times[64] - 64 * per_row, 0.0)
+    count = int(min(ops.m, 32768, max(64, (target_s - fixed) / per_row)))
+    rows = W.sample_rows(ops.m, count, seed=2)
+    t0 = time.perf_counter()
+    dz, _, _ = eo.backward_reference(ops.a[rows], ops.b, ops.dtype, "DRELU", mask[rows])
+    secs = time.perf_counter() - t0
+    gpu_d = keep[2]
+    sel = gpu_d.index_select(0, torch.from_numpy(rows).to(gpu_d.device)).cpu()
+    d = eo.widen(sel.view(torch.int16).numpy().view(np.uint16), ops.dtype)
+    flops = 2.0 * len(rows) * ops.n * ops.k
+    return {"value": round(flops / secs / 1e12, 4), "unit": "TFLOP/s", "cores": int(cores), "kind": "oracle",
+            "sample": f"{len(rows)} of {ops.m} output rows x all {ops.n} columns (k={ops.k}), DRELU part of "
+                      f"{W.BACKWARD_WORKLOADS[name].epilogs[-1]}, fp64 numpy oracle; {secs:.1f} s",
+            "seconds": round(secs, 2), "parity_max_abs_err": float(np.abs(d - dz).max()),
+            "parity_tol": eo.TOLERANCE[ops.dtype]}
+
+
 def cpu_baseline(name, ops, keep, target_s):
     """The CPU fp64 oracle on a row sample of the same workload; also checks
     the GPU's D on those rows (a bench-time parity spot check)."""
@@ -436,6 +549,8 @@ def cpu_baseline(name, ops, keep, target_s):
         cores = max([i.get("num_threads", 1) for i in threadpool_info() if i.get("user_api") == "blas"] or [1])
     except Exception:  # pragma: no cover
         cores = len(os.sched_getaffinity(0))
+    if ops is not None and "mask" in ops.meta:  # backward: the DRELU part on a row sample
+        return _cpu_baseline_backward(name, ops, keep, target_s, cores)
     if ops is None:  # FFN chain: time the up-projection oracle on a row sample
         f = W.ffn_operands()
         a, b, bias, layout, epilog, dtype = f.x, f.w1, f.b1, "col", "GELU_BIAS", "bf16"

@@ -89,13 +89,21 @@ struct egm_plan_s {
   int32_t autotune_pending;
   size_t workspace_bytes;
   size_t product_bytes;      // the two-kernel path's P at the start of the workspace
-  int64_t grad_chunks;       // DRELU_BGRAD: rows of partial sums (32-row or 32-column blocks)
-  int64_t grad_len;          // ... and their length (n or m)
+  int64_t grad_len;          // DRELU_BGRAD: length of the gradient (n or m)
 };
 
 namespace {
 
 bool valid_plan(egm_plan_t p) { return p != nullptr && p->magic == kPlanMagic; }
+
+// DRELU_BGRAD partial-sum rows a launch writes: one per tile row ((1,n)
+// bias) or tile column ((m,1) bias) on the fused path, one per 32-row or
+// 32-column block of D on the two-kernel path
+int64_t grad_chunks(const egm_plan_s* p, int cfg) {
+  if (p->epilog != EGM_EPILOG_DRELU_BGRAD) return 0;
+  if (p->bias_layout == EGM_BIAS_COL) return cdiv(p->m, p->fused ? kConfigs[cfg].bm : 32);
+  return cdiv(p->n, p->fused ? kConfigs[cfg].bn : 32);
+}
 
 // tile rows per L2-sharing group actually launched
 int32_t effective_group_m(const egm_plan_s* p, int cfg) {
@@ -120,7 +128,8 @@ hipError_t launch_plan(const egm_plan_s* p, int cfg, const void* A, const void* 
                        void* ws, hipStream_t s) {
   const ConfigInfo& c = kConfigs[cfg];
   const int dt = p->dtype == EGM_F16 ? egm::DT_F16 : egm::DT_BF16;
-  float* partial = p->grad_chunks > 0 ? reinterpret_cast<float*>(static_cast<uint8_t*>(ws) + p->product_bytes) : nullptr;
+  const int64_t chunks = grad_chunks(p, cfg);
+  float* partial = chunks > 0 ? reinterpret_cast<float*>(static_cast<uint8_t*>(ws) + p->product_bytes) : nullptr;
   GemmArgs g{};
   g.A = A;
   g.B = B;
@@ -146,9 +155,9 @@ hipError_t launch_plan(const egm_plan_s* p, int cfg, const void* A, const void* 
   if (err != hipSuccess) return err;
   // the bias gradient's last step: sum the per-block partials in block order
   auto finish_grad = [&]() {
-    int64_t blocks = cdiv(p->grad_len, 256);
+    int64_t blocks = cdiv(p->grad_len, 64);
     if (blocks > 4096) blocks = 4096;
-    egm::launch_bias_grad_finish(dim3(uint32_t(blocks)), s, partial, p->grad_chunks, p->grad_len,
+    egm::launch_bias_grad_finish(dim3(uint32_t(blocks)), s, partial, chunks, p->grad_len,
                                  static_cast<float*>(p->bias_grad));
     return hipGetLastError();
   };
@@ -299,16 +308,18 @@ egm_status_t egm_plan(egm_plan_t* out, int64_t m, int64_t n, int64_t k, egm_dtyp
   p->group_m = group_m;
   p->autotune_pending = tune;
   // workspace: the two-kernel path's product P, then (DRELU_BGRAD) the fp32
-  // partial sums: one row of n per 32-row block ((1,n) bias) or of m per
-  // 32-column block ((m,1) bias); the same layout on both paths
+  // partial sums, sized for every config the plan may launch (all of them
+  // while autotuning is pending)
   p->product_bytes = (!fused && epilog != EGM_EPILOG_DEFAULT) ? (size_t(m) * size_t(n) * 2u + 255u) & ~size_t(255) : 0u;
-  p->grad_chunks = 0;
-  p->grad_len = 0;
-  if (epilog == EGM_EPILOG_DRELU_BGRAD) {
-    p->grad_chunks = layout == EGM_BIAS_COL ? cdiv(m, 32) : cdiv(n, 32);
-    p->grad_len = layout == EGM_BIAS_COL ? n : m;
+  p->grad_len = epilog == EGM_EPILOG_DRELU_BGRAD ? (layout == EGM_BIAS_COL ? n : m) : 0;
+  int64_t max_chunks = 0;
+  for (int c = 0; c < kNumConfigs; ++c) {
+    if (tune || c == p->config) {
+      const int64_t ch = grad_chunks(p, c);
+      if (ch > max_chunks) max_chunks = ch;
+    }
   }
-  p->workspace_bytes = p->product_bytes + size_t(p->grad_chunks) * size_t(p->grad_len) * 4u;
+  p->workspace_bytes = p->product_bytes + size_t(max_chunks) * size_t(p->grad_len) * 4u;
   if (const char* log = std::getenv("EGM_LOG"); log != nullptr && log[0] == '1') {
     char buf[512];
     describe(p, buf, sizeof(buf));
@@ -336,7 +347,7 @@ egm_status_t egm_execute(egm_plan_t plan, const void* A, const void* B, void* D,
     // call stays capturable in a graph)
     if (p->bias_grad != nullptr && p->grad_len > 0) {
       if (!aligned16(p->bias_grad)) return EGM_ERR_ALIGNMENT;
-      int64_t blocks = cdiv(p->grad_len, 256);
+      int64_t blocks = cdiv(p->grad_len, 64);
       if (blocks > 4096) blocks = 4096;
       egm::launch_bias_grad_finish(dim3(uint32_t(blocks)), reinterpret_cast<hipStream_t>(stream), nullptr, 0,
                                    p->grad_len, static_cast<float*>(p->bias_grad));

@@ -94,7 +94,8 @@ __global__ void __launch_bounds__(256) epilogue_kernel(EpiArgs p) {
 }
 
 // Bias gradient of the two-kernel path, first step: partial sums of D
-// ([M,N], the operand dtype) in the same layout the fused kernel writes,
+// ([M,N], the operand dtype) over 32-row or 32-column blocks (the fused kernel
+// writes the same layout with whole tiles as the blocks),
 //   (1,n) bias (BIAS_COL): partial[rb * N + c] = sum of D[32 rb .. 32 rb + 31, c]
 //   (m,1) bias (BIAS_ROW): partial[cb * M + r] = sum of D[r, 32 cb .. 32 cb + 31]
 // one thread per (32-row block, 8 columns) or (row, 32-column block).
@@ -142,16 +143,27 @@ __global__ void __launch_bounds__(256) axis_partials_kernel(const void* Dp, int6
 }
 
 // Bias gradient, last step (both paths): out[x] = sum over c of
-// partial[c * len + x], c = 0 .. chunks-1 in order, so the result does not
-// depend on the launch.  (A template only so that every unit including this
-// header may see it; it is instantiated once, for float.)
+// partial[c * len + x].  A workgroup takes 64 consecutive x; its four waves
+// each add every fourth chunk (wave q: chunks q, q + 4, ...) in order, and the
+// four sums are joined in a fixed order, so the result does not depend on the
+// launch.  (A template only so that every unit including this header may see
+// it; it is instantiated once, for float.)
 template <typename F>
 __global__ void __launch_bounds__(256) bias_grad_finish_kernel(const F* partial, int64_t chunks, int64_t len,
                                                                F* out) {
-  for (int64_t x = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; x < len; x += (int64_t)gridDim.x * blockDim.x) {
+  __shared__ F sums[4][64];
+  const int xl = threadIdx.x & 63, q = threadIdx.x >> 6;
+  for (int64_t x0 = (int64_t)blockIdx.x * 64; x0 < len; x0 += (int64_t)gridDim.x * 64) {
+    const int64_t x = x0 + xl;
     F s = 0;
-    for (int64_t c = 0; c < chunks; ++c) s += partial[c * len + x];
-    out[x] = s;
+    if (x < len) {
+#pragma unroll 8
+      for (int64_t c = q; c < chunks; c += 4) s += partial[c * len + x];
+    }
+    sums[q][xl] = s;
+    __syncthreads();
+    if (q == 0 && x < len) out[x] = (sums[0][xl] + sums[1][xl]) + (sums[2][xl] + sums[3][xl]);
+    __syncthreads();
   }
 }
 

@@ -49,9 +49,9 @@ struct GemmArgs {
   const void* bias;  // [M] or [N]
   const void* R;     // [M,N] residual
   void* aux;         // [M,N/8] mask bytes (written by RELU_AUX, read by DRELU / DRELU_BGRAD)
-  float* partial;    // DRELU_BGRAD: fp32 partial sums of dZ, one row of them per 32-row
-                     // block ((1,n) bias: [ceil(M/32), N]) or per 32-column block
-                     // ((m,1) bias: [ceil(N/32), M])
+  float* partial;    // DRELU_BGRAD: fp32 partial sums of dZ, one row of them per tile row
+                     // ((1,n) bias: [ceil(M/BM), N]) or per tile column ((m,1) bias:
+                     // [ceil(N/BN), M])
   int32_t M, N, K;
   int32_t bias_layout;
   int32_t tiles_m, tiles_n;
@@ -87,6 +87,11 @@ struct TileCfg {
   // per-wave epilogue stage: 32 rows of the wave tile in T, then 32 mask rows
   static constexpr int EPI_STAGE = 32 * WTN * 2 + 512;
   static_assert(NW * EPI_STAGE <= LDS_BYTES, "epilogue stages must fit in the ring");
+  // bias-gradient sums of the waves, combined after the stages: WM rows of BN
+  // column sums or WN rows of BM row sums (fp32)
+  static constexpr int RED_OFF = NW * EPI_STAGE;
+  static_assert(RED_OFF + 4 * (WM * BN > WN * BM ? WM * BN : WN * BM) <= LDS_BYTES, "gradient sums must fit");
+  static_assert(BM <= NT && BN <= NT, "one thread per tile row / column for the gradient sums");
   static_assert(STAGES >= 2, "the ring needs a buffer being filled besides the one being read");
   static_assert(LDS_BYTES + 1024 <= 160 * 1024, "LDS ring exceeds 160 KiB");
 };
@@ -190,14 +195,71 @@ __device__ __forceinline__ void wait_vmcnt() {
   __builtin_amdgcn_s_waitcnt((N & 0xf) | ((N >> 4) << 14) | (0x7 << 4) | (0xf << 8));
 }
 
+// Cross-lane moves for the bias-gradient sums (VALU only, no LDS traffic).
+// swap16(x, y): for each pair of 16-lane rows (0,1), (2,3), the odd row of x
+// trades places with the even row of y (v_permlane16_swap); swap32 does the
+// same with the two 32-lane halves (v_permlane32_swap).
+__device__ __forceinline__ void swap16(float& x, float& y) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__builtin_bit_cast(uint32_t, x), __builtin_bit_cast(uint32_t, y),
+                                                  false, false);
+  x = __builtin_bit_cast(float, (uint32_t)r[0]);
+  y = __builtin_bit_cast(float, (uint32_t)r[1]);
+}
+__device__ __forceinline__ void swap32(float& x, float& y) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__builtin_bit_cast(uint32_t, x), __builtin_bit_cast(uint32_t, y),
+                                                  false, false);
+  x = __builtin_bit_cast(float, (uint32_t)r[0]);
+  y = __builtin_bit_cast(float, (uint32_t)r[1]);
+}
+// DPP lane moves inside a 16-lane row: lane i reads lane i ^ 8 (row_ror:8),
+// (i & ~7) | (7 - (i & 7)) (row_half_mirror), i ^ 2 and i ^ 1 (quad_perm)
+enum : int { DPP_XOR8 = 0x128, DPP_HALF_MIRROR = 0x141, DPP_XOR2 = 0x4E, DPP_XOR1 = 0xB1 };
+template <int CTRL>
+__device__ __forceinline__ float dpp(float v) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL, 0xf, 0xf, false));
+}
+
+// Column sums of a 32 x 32 block over its 32 rows.  Lane l holds row l % 32
+// and, in v[4g + e], column 8g + 4(l / 32) + e.  Each step pairs every lane
+// with a partner that holds the same value indices over other rows; the lane
+// keeps one half of its values (chosen by a bit of l that differs from the
+// partner's) and adds the partner's copy of that half: 16 -> 8 values over
+// rows l, l^16 (row swap), -> 4 over 4 rows (partner l^8), -> 2 (partner in
+// the mirrored half-row), -> 1 (partner l^2), then a last add with lane l^1.
+// Lane l ends with the sum of v[k], k = (l >> 1) & 15, over all 32 rows.
+__device__ __forceinline__ float block_column_sum(float (&v)[16], int lane) {
+#pragma unroll
+  for (int t = 0; t < 8; ++t) {
+    float x = v[t], y = v[t + 8];
+    swap16(x, y);  // even rows now hold (own v[t], partner v[t]), odd rows (partner v[t+8], own v[t+8])
+    v[t] = x + y;
+  }
+  const bool b3 = (lane & 8) != 0, b2 = (lane & 4) != 0, b1 = (lane & 2) != 0;
+#pragma unroll
+  for (int t = 0; t < 4; ++t) {
+    const float give = b3 ? v[t] : v[t + 4], mine = b3 ? v[t + 4] : v[t];
+    v[t] = mine + dpp<DPP_XOR8>(give);
+  }
+#pragma unroll
+  for (int t = 0; t < 2; ++t) {
+    const float give = b2 ? v[t] : v[t + 2], mine = b2 ? v[t + 2] : v[t];
+    v[t] = mine + dpp<DPP_HALF_MIRROR>(give);
+  }
+  {
+    const float give = b1 ? v[0] : v[1], mine = b1 ? v[1] : v[0];
+    v[0] = mine + dpp<DPP_XOR2>(give);
+  }
+  return v[0] + dpp<DPP_XOR1>(v[0]);
+}
+
 // ---------------------------------------------------------------------------
 // Epilogue on the fp32 accumulators of one wave, then the store.
 // lane holds D[m0 + wm0 + 32i + lr][n0 + wn0 + 32j + 8g + 4lh + e] = acc[i][j][4g + e]
 // ---------------------------------------------------------------------------
-template <int DT, int EPI, int FM, int FN>
+template <int DT, int EPI, int WM, int WN, int FM, int FN>
 __device__ __forceinline__ void epilogue_store(const GemmArgs& p, f32x16 (&acc)[FM][FN], int m0, int n0, int wm0,
                                                int wn0, int lane, uint8_t* stage,
-                                               const uint8_t* bias_lds) {
+                                               const uint8_t* bias_lds, float* red) {
   const int M = p.M, N = p.N;
   // The packed outputs of one 32-row block-row go through this wave's private
   // LDS stage so that D leaves as 16-byte row chunks, 4 full rows of the wave
@@ -249,6 +311,37 @@ __device__ __forceinline__ void epilogue_store(const GemmArgs& p, f32x16 (&acc)[
   const auto rM = make_rsrc(kMask ? (uint8_t*)p.aux + (size_t)m0 * mrow : (uint8_t*)p.D,
                             kMask ? (uint64_t)(M - m0) * mrow : 0);
 
+  // backward: the forward mask words of the wave tile, all loads issued at
+  // once; word (i, j) covers row wm0+32i+lr, columns wn0+32j .. +31 (bit
+  // 8g + 4lh + e belongs to this lane's column 8g + 4lh + e)
+  uint32_t keep[FM][FN];
+  if constexpr (epi_reads_mask(EPI)) {
+#pragma unroll
+    for (int i = 0; i < FM; ++i)
+#pragma unroll
+      for (int j = 0; j < FN; ++j) {
+        const int cb = n0 + wn0 + 32 * j;
+        const uint32_t mo = (uint32_t)(wm0 + 32 * i + lr) * mrow + (uint32_t)cb / 8u;
+        if ((mrow & 3u) == 0) {
+          keep[i][j] = buf_load4(rM, mo);  // 4-byte aligned: the word is one load
+        } else {
+          uint32_t w = 0;
+#pragma unroll
+          for (int b = 0; b < 4; ++b)
+            w |= (uint32_t)buf_load1(rM, cb + 8 * b < N ? mo + b : OOB_OFFSET) << (8 * b);
+          keep[i][j] = w;
+        }
+      }
+  }
+  // bias gradient: this wave's sums of dZ over its rows, one per column of
+  // block j and lane (colacc, (1,n) bias), or over its columns, one per row of
+  // block i (rowacc, (m,1) bias); added up in a fixed order
+  float colacc[FN], rowacc[FM];
+#pragma unroll
+  for (int j = 0; j < FN; ++j) colacc[j] = 0.0f;
+#pragma unroll
+  for (int i = 0; i < FM; ++i) rowacc[i] = 0.0f;
+
 #pragma unroll
   for (int i = 0; i < FM; ++i) {
     const uint32_t lrow = wm0 + 32 * i + lr;  // row within the tile
@@ -263,23 +356,9 @@ __device__ __forceinline__ void epilogue_store(const GemmArgs& p, f32x16 (&acc)[
 #pragma unroll
     for (int j = 0; j < FN; ++j) {
       uint32_t mword = 0;
-      // backward: the forward mask word of this row's 32 columns wn0+32j .. +31
-      // (bit 8g + 4lh + e belongs to this lane's column 8g + 4lh + e)
-      uint32_t keep = 0;
-      if constexpr (epi_reads_mask(EPI)) {
-        const int cb = n0 + wn0 + 32 * j;
-        const uint32_t mo = lrow * mrow + (uint32_t)cb / 8u;
-        if ((mrow & 3u) == 0) {
-          keep = buf_load4(rM, mo);  // 4-byte aligned: the word is one load
-        } else {
-#pragma unroll
-          for (int b = 0; b < 4; ++b)
-            keep |= (uint32_t)buf_load1(rM, cb + 8 * b < N ? mo + b : OOB_OFFSET) << (8 * b);
-        }
-      }
-      // bias gradient partial sums of this 32 x 32 block: per column (over the
-      // lane's row, reduced across rows below) or per row (over the lane's
-      // columns, reduced across the two half-waves below)
+      // bias gradient sums of this 32 x 32 block: per column (the lane's row
+      // only, reduced across the rows below) or per row (the lane's columns,
+      // reduced across the two half-waves below)
       float csum[4][4];
       float rsum = 0.0f;
 #pragma unroll
@@ -291,7 +370,7 @@ __device__ __forceinline__ void epilogue_store(const GemmArgs& p, f32x16 (&acc)[
         for (int e = 0; e < 4; ++e) {
           z[e] = acc[i][j][4 * g + e];
           if constexpr (epi_adds_bias(EPI)) z[e] += brow + bcol[j][g][e];
-          if constexpr (epi_reads_mask(EPI)) z[e] = ((keep >> (8 * g + 4 * lh + e)) & 1u) ? z[e] : 0.0f;
+          if constexpr (epi_reads_mask(EPI)) z[e] = ((keep[i][j] >> (8 * g + 4 * lh + e)) & 1u) ? z[e] : 0.0f;
           if constexpr (EPI == EPI_DRELU_BGRAD) {
             csum[g][e] = z[e];
             rsum += z[e];
@@ -316,32 +395,17 @@ __device__ __forceinline__ void epilogue_store(const GemmArgs& p, f32x16 (&acc)[
       }
       if constexpr (EPI == EPI_DRELU_BGRAD) {
         if (p.bias_layout == BIAS_COL) {
-          // sum the block's 32 rows: lanes lr and lr^s (s < 32) share columns
+          float v[16];
 #pragma unroll
-          for (int s = 1; s < 32; s <<= 1)
+          for (int g = 0; g < 4; ++g)
 #pragma unroll
-            for (int g = 0; g < 4; ++g)
-#pragma unroll
-              for (int e = 0; e < 4; ++e) csum[g][e] += __shfl_xor(csum[g][e], s);
-          const int rb = m0 + wm0 + 32 * i;  // first row of the block
-          if (lr == 0) {
-            const auto rP = make_rsrc(p.partial + (size_t)(rb / 32) * N, rb < M ? (uint64_t)N * 4 : 0);
-#pragma unroll
-            for (int g = 0; g < 4; ++g) {
-              const int col = n0 + wn0 + 32 * j + 8 * g + 4 * lh;
-              buf_store16(u32x4{__builtin_bit_cast(uint32_t, csum[g][0]), __builtin_bit_cast(uint32_t, csum[g][1]),
-                                __builtin_bit_cast(uint32_t, csum[g][2]), __builtin_bit_cast(uint32_t, csum[g][3])},
-                          rP, col < N ? (uint32_t)col * 4u : OOB_OFFSET);
-            }
-          }
+            for (int e = 0; e < 4; ++e) v[4 * g + e] = csum[g][e];
+          colacc[j] += block_column_sum(v, lane);
         } else {
-          // sum the block's 32 columns: the two half-waves hold the other 16
-          rsum += __shfl_xor(rsum, 32);
-          const int cb = n0 + wn0 + 32 * j;  // first column of the block
-          if (lh == 0) {
-            const auto rP = make_rsrc(p.partial + (size_t)(cb / 32) * M + m0, cb < N ? (uint64_t)(M - m0) * 4 : 0);
-            buf_store4(__builtin_bit_cast(uint32_t, rsum), rP, lrow * 4u);
-          }
+          // sum the block's 32 columns: the two half-waves hold 16 each
+          float x = rsum, y = rsum;
+          swap32(x, y);  // x: the low half's sum in every lane, y: the high half's
+          rowacc[i] += x + y;
         }
       }
       if constexpr (EPI == EPI_RELU_AUX) {
@@ -386,6 +450,43 @@ __device__ __forceinline__ void epilogue_store(const GemmArgs& p, f32x16 (&acc)[
       if (x & 1) v = u32x4{v[2], v[3], v[0], v[1]};
       const int col = n0 + wn0 + 8 * (int)m;
       buf_store16(v, rD, col < N ? (wm0 + 32 * i + r) * rowbytes + (uint32_t)col * 2u : OOB_OFFSET);
+    }
+  }
+  if constexpr (EPI == EPI_DRELU_BGRAD) {
+    // the tile's sums: the waves that share columns (or rows) leave theirs in
+    // LDS, then one thread per tile column (row) adds them in wave order and
+    // writes the tile's partial; rows and columns past the matrix hold zeros
+    // (their mask bits read as 0) and are not written
+    constexpr int BM = WM * 32 * FM, BN = WN * 32 * FN;
+    const int tid = (int)threadIdx.x;
+    if (p.bias_layout == BIAS_COL) {
+      const int wave_m = wm0 / (32 * FM);
+      if ((lr & 1) == 0) {
+        const int k = (lr >> 1) & 15;
+        const int c = 8 * (k >> 2) + 4 * lh + (k & 3);
+#pragma unroll
+        for (int j = 0; j < FN; ++j) red[wave_m * BN + wn0 + 32 * j + c] = colacc[j];
+      }
+      __syncthreads();
+      if (tid < BN && n0 + tid < N) {
+        float t = red[tid];
+#pragma unroll
+        for (int w = 1; w < WM; ++w) t += red[w * BN + tid];
+        p.partial[(size_t)(m0 / BM) * N + n0 + tid] = t;
+      }
+    } else {
+      const int wave_n = wn0 / (32 * FN);
+      if (lh == 0) {
+#pragma unroll
+        for (int i = 0; i < FM; ++i) red[wave_n * BM + wm0 + 32 * i + lr] = rowacc[i];
+      }
+      __syncthreads();
+      if (tid < BM && m0 + tid < M) {
+        float t = red[tid];
+#pragma unroll
+        for (int w = 1; w < WN; ++w) t += red[w * BM + tid];
+        p.partial[(size_t)(n0 / BN) * M + m0 + tid] = t;
+      }
     }
   }
 }
@@ -631,7 +732,8 @@ __global__ void __launch_bounds__(C::NT, 1) gemm_epilogue_kernel(GemmArgs p) {
   wait_vmcnt<0>();
   // the ring is free once every wave is past its last fragment read
   __syncthreads();
-  epilogue_store<DT, EPI>(p, acc, m0, n0, wm0, wn0, lane, smem + wave * C::EPI_STAGE, bias_lds);
+  epilogue_store<DT, EPI, C::WM, C::WN>(p, acc, m0, n0, wm0, wn0, lane, smem + wave * C::EPI_STAGE, bias_lds,
+                                        (float*)(smem + C::RED_OFF));
 }
 
 }  // namespace egm

@@ -208,6 +208,49 @@ WORKLOADS = {
 #: workload names in table order (small -> large)
 WORKLOAD_ORDER = tuple(WORKLOADS)
 
+#: the backward of the square workload: the gradient reaching its ReLU output
+#: (A.B with A ~ N(0,1), B ~ N(0,1)/sqrt(K)) through its mask, with the
+#: gradient of its (1,n) bias.  The mask is drawn (uniform bytes, each bit 1
+#: with probability 1/2, as for a ReLU over a zero-mean pre-activation) rather
+#: than taken from a forward run, so that every oracle input is a draw.
+BACKWARD_WORKLOADS = {
+    "drelu_bgrad_bf16_8192x8192x8192": Workload(
+        "drelu_bgrad_bf16_8192x8192x8192", 8192, 8192, 8192, BF16, ("DRELU_BGRAD",), "col",
+        "backward of the square workload; bias gradient of its (1,n) bias"),
+}
+
+
+def mask_bits(m: int, n: int, seed: int, tensor_index: int) -> np.ndarray:
+    """A packed [m, n/8] uint8 mask of independent fair bits."""
+    if n % 8:
+        raise ValueError("n must be a multiple of 8")
+    return _uniform_bytes((m, n // 8), seed, tensor_index)
+
+
+def _uniform_bytes(shape, seed: int, tensor_index: int) -> np.ndarray:
+    total = int(np.prod(shape))
+    out = np.empty(total, dtype=np.uint8)
+
+    def fill(c: int) -> None:
+        lo = c * CHUNK
+        hi = min(total, lo + CHUNK)
+        out[lo:hi] = _chunk_generator(seed, tensor_index, c).integers(0, 256, size=hi - lo, dtype=np.uint8)
+
+    nchunks = (total + CHUNK - 1) // CHUNK
+    with ThreadPoolExecutor(_THREADS) as ex:
+        list(ex.map(fill, range(nchunks)))
+    return out.reshape(shape)
+
+
+def backward_operands(name: str, seed: int = 0):
+    """(Operands of the gradient GEMM, packed mask) of a backward workload;
+    tensor indices 0, 1 for A, B and 2 for the mask."""
+    w = BACKWARD_WORKLOADS[name]
+    a = normal_bits((w.m, w.k), 1.0, w.dtype, seed, 0)
+    b = normal_bits((w.k, w.n), 1.0 / math.sqrt(w.k), w.dtype, seed, 1)
+    ops = Operands(w.m, w.n, w.k, w.dtype, a, b, None, w.bias_layout)
+    return ops, mask_bits(w.m, w.n, seed, 2)
+
 
 def workload_operands(name: str, seed: int = 0) -> Operands:
     """Operands of a plain GEMM workload (all but the FFN chain)."""

@@ -210,17 +210,24 @@ def test_matmul_wrapper_rejects_without_gpu():
 
 
 def test_backward_workspace_and_execute_validation():
-    # fused DRELU_BGRAD: fp32 partial sums, one row per 32-row block of a (1,n) bias
+    # fused DRELU_BGRAD: fp32 partial sums, one row of n per tile row of a (1,n) bias
     h = egm.egm_plan(100, 64, 32, BF16, E["DRELU_BGRAD"], 0, COL, bias_grad=FAKE)
     try:
-        assert egm.egm_plan_workspace_bytes(h) == 4 * 64 * 4  # ceil(100/32) = 4 blocks x n x fp32
+        bm = int(re.search(r"tile=(\d+)x(\d+)", egm.egm_plan_describe(h)).group(1))
+        assert egm.egm_plan_workspace_bytes(h) == -(-100 // bm) * 64 * 4  # ceil(m/BM) rows x n x fp32
         assert "DRELU_BGRAD" in egm.egm_plan_describe(h)
         # the forward mask is an input here: required
         assert egm.egm_execute(h, FAKE, FAKE, FAKE, 0, FAKE, 4096, raw_status=True) == egm.EGM_ERR_INVALID_VALUE
         assert egm.egm_execute(h, FAKE, FAKE, FAKE, FAKE, 0, 0, raw_status=True) == egm.EGM_ERR_WORKSPACE
     finally:
         egm.egm_free(h)
-    # (m,1) gradient: one row of m per 32-column block; the two-kernel path adds P in front
+    # autotuning may pick any tile: room for the smallest (64 x 64)
+    h = egm.egm_plan(100, 64, 32, BF16, E["DRELU_BGRAD"], 0, COL, bias_grad=FAKE, autotune=1)
+    try:
+        assert egm.egm_plan_workspace_bytes(h) == 2 * 64 * 4
+    finally:
+        egm.egm_free(h)
+    # (m,1) gradient, two-kernel path: one row of m per 32-column block of D, after P
     h = egm.egm_plan(100, 72, 32, F16, E["DRELU_BGRAD"], 0, ROW, bias_grad=FAKE, fused=0)
     try:
         p_bytes = (100 * 72 * 2 + 255) // 256 * 256

@@ -1,7 +1,7 @@
 """Backward epilogues on the GPU against the CPU oracle, through the C ABI:
 DRELU (the forward ReLU mask applied to the incoming gradient A.B) and
-DRELU_BGRAD (plus the bias gradient).  The mask comes from the seeded
-generator or from the GPU's own forward RELU_AUX_BIAS."""
+DRELU_BGRAD (plus the bias gradient).  The masks given to the oracle come from
+the seeded generator or from the oracle's own forward pass."""
 import numpy as np
 import pytest
 
@@ -62,23 +62,29 @@ def test_normal_within_bounds(dtype, cfg):
 
 
 @pytest.mark.parametrize("dtype", ["fp16", "bf16"])
-def test_mask_from_gpu_forward(dtype):
-    """The chain a training step runs: forward RELU_AUX_BIAS on the GPU, then
-    the backward epilogue consuming that mask; checked against the oracle fed
-    the GPU's mask (and that mask against the forward oracle)."""
+def test_forward_then_backward(dtype):
+    """The chain a training step runs: forward RELU_AUX_BIAS, then the backward
+    epilogue on its mask.  The oracle's own forward mask is the oracle input
+    (and the backward's, checked against the oracle); the GPU's forward mask
+    feeds a second backward run, which must agree with the first wherever the
+    two masks agree and be zero wherever the GPU mask is 0.  No GPU output is
+    ever an oracle input."""
     m, n, k = 264, 136, 200
     fwd = W.gemm_operands(m, n, k, dtype, seed=77, a_std=1.0, b_std=1.0 / np.sqrt(k), bias_layout="col",
                           bias_std=0.5)
-    d_fwd, mask = run(fwd, "RELU_AUX_BIAS")
-    y, z, mref = eo.reference(fwd.a, fwd.b, dtype, "RELU_AUX_BIAS", fwd.bias, "col")
-    compare(d_fwd, y, dtype, z=z, mask=mask, mask_ref=mref)
+    d_fwd, mask_gpu = run(fwd, "RELU_AUX_BIAS")
+    y, z, mask_ref = eo.reference(fwd.a, fwd.b, dtype, "RELU_AUX_BIAS", fwd.bias, "col")
+    compare(d_fwd, y, dtype, z=z, mask=mask_gpu, mask_ref=mask_ref)
     grad_ops = W.gemm_operands(m, n, 96, dtype, seed=78, a_std=0.7, b_std=1.0 / np.sqrt(96), bias_layout="col")
-    dz, grad_ref, bound = eo.backward_reference(grad_ops.a, grad_ops.b, dtype, "DRELU_BGRAD", mask, "col")
-    d, grad = run_backward(grad_ops, "DRELU_BGRAD", mask, "col")
-    compare(d, dz, dtype)
+    dz, grad_ref, bound = eo.backward_reference(grad_ops.a, grad_ops.b, dtype, "DRELU_BGRAD", mask_ref, "col")
+    d_ref_mask, grad = run_backward(grad_ops, "DRELU_BGRAD", mask_ref, "col")
+    compare(d_ref_mask, dz, dtype)
     compare_bias_grad(grad, grad_ref, bound)
-    # the gradient is zero exactly where the forward ReLU cut
-    assert not eo.widen(d, dtype)[~eo.unpack_mask(mask, n)].any()
+    d_gpu_mask, _ = run_backward(grad_ops, "DRELU_BGRAD", mask_gpu, "col")
+    keep_gpu, keep_ref = eo.unpack_mask(mask_gpu, n), eo.unpack_mask(mask_ref, n)
+    same = keep_gpu == keep_ref
+    assert np.array_equal(d_gpu_mask[same], d_ref_mask[same])
+    assert not eo.widen(d_gpu_mask, dtype)[~keep_gpu].any()
 
 
 def test_edges_and_empty():

@@ -45,29 +45,30 @@ def test_worked_example_shape(epilog, fused):
 @pytest.mark.slow
 def test_ffn_chain():
     """Up-projection GELU_BIAS then down-projection BIAS_RESIDUAL (R = X).
-    (i) each GEMM against the oracle fed the GPU's own H; (ii) the chain against
-    the oracle's own rounded H."""
+    (i) the up-projection against the oracle; (ii) the down-projection run on
+    the oracle's own rounded H (uploaded), against the oracle on that H; (iii)
+    the GPU chain (down-projection on the GPU's H) against the oracle's chain.
+    No GPU output is ever an oracle input."""
     import torch
     import dense_gemm_epilogue_fp16_amd as egm
     f = W.ffn_operands()
     x, w1, w2 = to_device(f.x, "bf16"), to_device(f.w1, "bf16"), to_device(f.w2, "bf16")
     b1 = to_device(f.b1, "bf16").reshape(1, -1)
     b2 = to_device(f.b2, "bf16").reshape(1, -1)
+    y_up, _, _ = eo.reference(f.x, f.w1, "bf16", "GELU_BIAS", f.b1, "col")
+    h_ref = eo.round_to_bits(y_up, "bf16")
     with egm.Matmul(x, w1) as up, egm.Matmul(torch.empty((f.tokens, f.ffn), dtype=torch.bfloat16, device="cuda"),
                                              w2) as down:
         up.plan("GELU_BIAS", {"bias": b1})
         h = up.execute()
         down.plan("BIAS_RESIDUAL", {"bias": b2, "residual": x})
-        d = down.execute(a=h)
+        d_chain = down.execute(a=h)
+        d_on_ref_h = down.execute(a=to_device(h_ref, "bf16"))
         torch.cuda.synchronize()
-    h_bits, d_bits = to_host_bits(h), to_host_bits(d)
-    y_up, _, _ = eo.reference(f.x, f.w1, "bf16", "GELU_BIAS", f.b1, "col")
-    print("[ffn up]", compare(h_bits, y_up, "bf16"), flush=True)
-    y_dn, _, _ = eo.reference(h_bits, f.w2, "bf16", "BIAS_RESIDUAL", f.b2, "col", f.x)
-    print("[ffn down, GPU H]", compare(d_bits, y_dn, "bf16"), flush=True)
-    h_ref = eo.round_to_bits(y_up, "bf16")
-    y_chain, _, _ = eo.reference(h_ref, f.w2, "bf16", "BIAS_RESIDUAL", f.b2, "col", f.x)
-    print("[ffn chain, oracle H]", compare(d_bits, y_chain, "bf16"), flush=True)
+    print("[ffn up]", compare(to_host_bits(h), y_up, "bf16"), flush=True)
+    y_dn, _, _ = eo.reference(h_ref, f.w2, "bf16", "BIAS_RESIDUAL", f.b2, "col", f.x)
+    print("[ffn down, oracle H]", compare(to_host_bits(d_on_ref_h), y_dn, "bf16"), flush=True)
+    print("[ffn chain, GPU H]", compare(to_host_bits(d_chain), y_dn, "bf16"), flush=True)
 
 
 @pytest.mark.slow
