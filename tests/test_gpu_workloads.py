@@ -1,4 +1,4 @@
-"""The five named workloads on the HIP path vs the CPU oracle (GPU).
+"""The named workloads on the HIP path vs the CPU oracle (GPU).
 
 Inputs are the seeded synthetic operands of ``egm_workloads`` at the full
 sizes; the launch configuration is the per-shape default that bench.py times.
@@ -74,6 +74,22 @@ def test_ffn_chain():
 @pytest.mark.slow
 def test_square_relu_aux_bias():
     _check_gemm("gemm_relu_aux_bias_bf16_8192x8192x8192", "RELU_AUX_BIAS")
+
+
+@pytest.mark.slow
+@pytest.mark.parametrize("fused", [True, False])
+def test_backward_workload(fused):
+    """The 8192^3 DRELU_BGRAD workload at full size, in the launch
+    configuration bench.py times: every output of D and the whole (1,n)
+    gradient against the oracle."""
+    from parity import compare_bias_grad, run_backward
+    name = "drelu_bgrad_bf16_8192x8192x8192"
+    ops, mask = W.backward_operands(name)
+    d, grad = run_backward(ops, "DRELU_BGRAD", mask, ops.bias_layout, fused=fused)
+    dz, g_ref, bound = eo.backward_reference(ops.a, ops.b, ops.dtype, "DRELU_BGRAD", mask, ops.bias_layout)
+    st = compare(d, dz, ops.dtype, unfused=not fused)
+    gs = compare_bias_grad(grad, g_ref, bound, d_ref=None if fused else dz, dtype=ops.dtype, layout=ops.bias_layout)
+    print(f"[{name} fused={fused}] D {st} grad {gs}", flush=True)
 
 
 @pytest.mark.slow

@@ -66,3 +66,17 @@ def test_workload_table():
         W.workload_operands("ffn_bf16_4096x1024x4096")
     ops = W.workload_operands("gemm_bias_fp16_256x256x512")
     assert ops.a.shape == (256, 512) and ops.b.shape == (512, 256) and ops.bias.shape == (256,)
+
+
+def test_backward_workload_and_mask_recipe():
+    # the mask is uniform bytes from the same chunked streams (tensor index 2)
+    m = W.mask_bits(64, 1024, seed=5, tensor_index=2)
+    g = np.random.Generator(np.random.PCG64(np.random.SeedSequence(5, spawn_key=(2, 0))))
+    assert m.shape == (64, 128) and m.dtype == np.uint8
+    assert np.array_equal(m.reshape(-1), g.integers(0, 256, size=64 * 128, dtype=np.uint8))
+    bits = np.unpackbits(W.mask_bits(512, 4096, seed=0, tensor_index=2))
+    assert abs(float(bits.mean()) - 0.5) < 0.005  # ReLU-like density: half the pre-activations positive
+    with pytest.raises(ValueError):
+        W.mask_bits(4, 12, seed=0, tensor_index=2)
+    w = W.BACKWARD_WORKLOADS["drelu_bgrad_bf16_8192x8192x8192"]
+    assert (w.m, w.n, w.k, w.dtype, w.bias_layout) == (8192, 8192, 8192, W.BF16, "col")
