@@ -31,6 +31,11 @@ up/down-projection weights and biases as N(0, v) and v is read as a variance):
                                     up = GELU_BIAS, down = BIAS_RESIDUAL (R = X)
   gemm_relu_aux_bias_bf16_8192x8192x8192  A,B ~ N(0,1)/sqrt(K), bias (1,n) ~ N(0,1)
   gemm_relu_bias_fp16_65536x16384x16384   A,B ~ N(0,1)/sqrt(K), bias (m,1) ~ N(0,1)
+
+fp8 operands (OCP E4M3 / E5M2) are made the way an fp8 producer makes them:
+the fp32 draw gets a per-tensor scale amax / (largest finite fp8 value), is
+divided by it in fp32 and rounded once, to nearest-even, to fp8 (torch's
+conversion); the bits and the fp32 scale are the operand.
 """
 from __future__ import annotations
 
@@ -113,6 +118,56 @@ def normal_bits(shape, std: float, dtype: str, seed: int, tensor_index: int) -> 
     return out.reshape(shape)
 
 
+def normal_f32(shape, std: float, seed: int, tensor_index: int) -> np.ndarray:
+    """The same draws as ``normal_bits``, kept in fp32 (scaled by std in fp32)."""
+    shape = tuple(int(s) for s in shape)
+    total = int(np.prod(shape, dtype=np.int64)) if shape else 1
+    out = np.empty(total, dtype=np.float32)
+    nchunks = (total + CHUNK - 1) // CHUNK
+    s32 = np.float32(std)
+
+    def fill(c: int) -> None:
+        lo = c * CHUNK
+        hi = min(total, lo + CHUNK)
+        v = _chunk_generator(seed, tensor_index, c).standard_normal(hi - lo, dtype=np.float32)
+        v *= s32
+        out[lo:hi] = v
+
+    with ThreadPoolExecutor(_THREADS) as ex:
+        list(ex.map(fill, range(nchunks)))
+    return out.reshape(shape)
+
+
+# --------------------------------------------------------------------------
+# fp8 operands
+# --------------------------------------------------------------------------
+E4M3 = "e4m3"
+E5M2 = "e5m2"
+FP8 = (E4M3, E5M2)
+#: largest finite value of each fp8 format
+FP8_MAX = {E4M3: 448.0, E5M2: 57344.0}
+
+
+def f32_to_fp8_bits(x: np.ndarray, fmt: str) -> np.ndarray:
+    """Round float32 values once (nearest-even, torch's conversion) to fp8,
+    saturating at the largest finite value; return uint8 bits."""
+    import torch
+    if fmt not in FP8_MAX:
+        raise ValueError(f"unknown fp8 format {fmt!r}")
+    x = np.clip(np.ascontiguousarray(x, dtype=np.float32), -FP8_MAX[fmt], FP8_MAX[fmt])
+    t = torch.from_numpy(x).to(torch.float8_e4m3fn if fmt == E4M3 else torch.float8_e5m2)
+    return t.view(torch.uint8).numpy().copy()
+
+
+def fp8_quantize(x: np.ndarray, fmt: str):
+    """Per-tensor scaling: scale = amax / FP8_MAX (fp32; 1 for an all-zero
+    tensor), q = fp8(x / scale).  Returns (uint8 bits, float32 scale)."""
+    x = np.asarray(x, dtype=np.float32)
+    amax = float(np.abs(x).max()) if x.size else 0.0
+    scale = np.float32(amax / FP8_MAX[fmt]) if amax > 0 else np.float32(1.0)
+    return f32_to_fp8_bits(x / scale, fmt), scale
+
+
 def integer_bits(shape, lo: int, hi: int, dtype: str, seed: int, tensor_index: int) -> np.ndarray:
     """Uniform integers in [lo, hi] as exact fp16/bf16 patterns (|v| <= 256)."""
     assert -256 <= lo <= hi <= 256
@@ -172,6 +227,55 @@ def integer_operands(m, n, k, dtype, seed=0, *, lo=-2, hi=2, bias_layout="row",
     return Operands(m, n, k, dtype, a, b, bias, bias_layout, r)
 
 
+@dataclass
+class Fp8Operands:
+    """Bit patterns of one fp8 GEMM + epilogue problem (row-major)."""
+
+    m: int
+    n: int
+    k: int
+    a_fmt: str
+    b_fmt: str
+    out_dtype: str            # fp16 / bf16: the bias, residual and output type
+    a: np.ndarray             # [m, k] uint8
+    b: np.ndarray             # [k, n] uint8
+    scale_a: np.float32
+    scale_b: np.float32
+    bias: np.ndarray | None   # [m] or [n] uint16 (out_dtype)
+    bias_layout: str | None
+    residual: np.ndarray | None = None  # [m, n] uint16 (out_dtype)
+    meta: dict = field(default_factory=dict)
+
+
+def fp8_operands(m, n, k, a_fmt, b_fmt, out_dtype, seed=0, *, a_std=1.0, b_std=None,
+                 bias_layout="col", bias_std=1.0, residual_std=None) -> Fp8Operands:
+    """Normal draws quantised per tensor (A ~ N(0, a_std^2), B ~ N(0, b_std^2),
+    b_std = 1/sqrt(K) by default, so A.B is O(1)); bias and residual in out_dtype."""
+    b_std = 1.0 / math.sqrt(max(int(k), 1)) if b_std is None else b_std
+    a, sa = fp8_quantize(normal_f32((m, k), a_std, seed, 0), a_fmt)
+    b, sb = fp8_quantize(normal_f32((k, n), b_std, seed, 1), b_fmt)
+    bias = None
+    if bias_layout is not None:
+        bias = normal_bits((m if bias_layout == "row" else n,), bias_std, out_dtype, seed, 2)
+    r = normal_bits((m, n), residual_std, out_dtype, seed, 3) if residual_std is not None else None
+    return Fp8Operands(m, n, k, a_fmt, b_fmt, out_dtype, a, b, sa, sb, bias, bias_layout, r)
+
+
+def fp8_integer_operands(m, n, k, a_fmt, b_fmt, out_dtype, seed=0, *, lo=-2, hi=2, bias_layout="col",
+                         scale_a=1.0, scale_b=1.0, residual=False) -> Fp8Operands:
+    """Small integers (exact in both fp8 formats) with power-of-two scales:
+    every product, sum, scaling and bias add is exact in fp32."""
+    g = _chunk_generator(seed, 0, 0)
+    a = f32_to_fp8_bits(g.integers(lo, hi + 1, size=(m, k)).astype(np.float32), a_fmt)
+    b = f32_to_fp8_bits(_chunk_generator(seed, 1, 0).integers(lo, hi + 1, size=(k, n)).astype(np.float32), b_fmt)
+    bias = None
+    if bias_layout is not None:
+        bias = integer_bits((m if bias_layout == "row" else n,), -4, 4, out_dtype, seed, 2)
+    r = integer_bits((m, n), -4, 4, out_dtype, seed, 3) if residual else None
+    return Fp8Operands(m, n, k, a_fmt, b_fmt, out_dtype, a, b, np.float32(scale_a), np.float32(scale_b), bias,
+                       bias_layout, r)
+
+
 # --------------------------------------------------------------------------
 # the five named workloads
 # --------------------------------------------------------------------------
@@ -218,6 +322,20 @@ BACKWARD_WORKLOADS = {
         "drelu_bgrad_bf16_8192x8192x8192", 8192, 8192, 8192, BF16, ("DRELU_BGRAD",), "col",
         "backward of the square workload; bias gradient of its (1,n) bias"),
 }
+
+
+#: fp8 operands on the square workload: A ~ N(0,1), B ~ N(0,1/K), both
+#: quantised per tensor to E4M3, bias (1,n) ~ N(0,1) and output in bf16
+FP8_WORKLOADS = {
+    "gemm_relu_aux_bias_fp8e4m3_8192x8192x8192": Workload(
+        "gemm_relu_aux_bias_fp8e4m3_8192x8192x8192", 8192, 8192, 8192, BF16, ("RELU_AUX_BIAS",), "col",
+        "square, E4M3 x E4M3 with per-tensor scales; bf16 bias and output, packed ReLU mask"),
+}
+
+
+def fp8_workload_operands(name: str, seed: int = 0) -> Fp8Operands:
+    w = FP8_WORKLOADS[name]
+    return fp8_operands(w.m, w.n, w.k, E4M3, E4M3, w.dtype, seed, bias_layout=w.bias_layout)
 
 
 def mask_bits(m: int, n: int, seed: int, tensor_index: int) -> np.ndarray:

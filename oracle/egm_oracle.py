@@ -43,6 +43,18 @@ needs, and the closing paragraph names dBias as an epilogue to come):
                values; (m,1) bias: over columns, m values), from the unrounded
                dZ, returned in fp32.
 
+FP8 operands ([bias-fusion], body: the data-type item of the checklist lists
+FP8 among the supported types; the closing paragraph names FP8 among the
+features to come).  The operands are OCP 8-bit floats, E4M3 (4 exponent bits,
+bias 7, 3 mantissa bits, no infinities, S.1111.111 is NaN) or E5M2 (5
+exponent bits, bias 15, 2 mantissa bits, IEEE-style infinities and NaNs), each
+with a per-tensor fp32 dequantisation scale: A = scale_a * A8, B = scale_b *
+B8.  The page's same-type rule is read as covering the two operands; the bias,
+the residual and the output are 16-bit (fp16 or bf16), since an fp8 bias or
+output would lose the precision the epilogue exists to keep.  Then
+  Z = scale_a * scale_b * (A8 . B8) + bias,  Y = epilogue(Z)
+with the same epilogues as above.
+
 Every function here is pinned by ``tests/test_oracle_pins.py`` against brute
 force, closed forms, invariants and library routines.
 """
@@ -213,6 +225,70 @@ def reference(a_bits, b_bits, dtype, epilog, bias_bits=None, bias_layout=None,
             raise ValueError(f"{epilog} needs a bias")
         z = add_bias(z, widen(row_bias, dtype), bias_layout)
     r64 = widen(r_bits, dtype) if r_bits is not None else None
+    y = apply_epilog(z, epilog, r64)
+    mask = relu_mask(z) if epilog == "RELU_AUX_BIAS" else None
+    return y, z, mask
+
+
+# ---------------------------------------------------------------------------
+# fp8 operands: exact decoding and the scaled product
+# ---------------------------------------------------------------------------
+E4M3 = "e4m3"
+E5M2 = "e5m2"
+# exponent bits, mantissa bits, exponent bias
+FP8_FORMATS = {E4M3: (4, 3, 7), E5M2: (5, 2, 15)}
+
+
+def decode_fp8(bits: np.ndarray, fmt: str) -> np.ndarray:
+    """fp8 bit patterns (uint8) -> float64, exactly, from the bit fields:
+    a normal number (exponent field e > 0) is (-1)^s 2^(e - bias) (1 + m 2^-M),
+    a subnormal one (e = 0) is (-1)^s 2^(1 - bias) m 2^-M.  E4M3 spends only
+    its all-ones pattern (e and m all ones) on NaN and has no infinities; E5M2
+    keeps the IEEE convention for an all-ones exponent (m = 0: infinity, else
+    NaN)."""
+    if fmt not in FP8_FORMATS:
+        raise ValueError(f"unknown fp8 format {fmt!r}")
+    ebits, mbits, bias = FP8_FORMATS[fmt]
+    b = np.asarray(bits, dtype=np.uint8).astype(np.int64)
+    sign = b >> 7
+    e = (b >> mbits) & ((1 << ebits) - 1)
+    m = b & ((1 << mbits) - 1)
+    normal = np.ldexp((m + (1 << mbits)).astype(np.float64), e - bias - mbits)
+    subnormal = np.ldexp(m.astype(np.float64), 1 - bias - mbits)
+    mag = np.where(e == 0, subnormal, normal)
+    top = (1 << ebits) - 1
+    if fmt == E4M3:
+        mag = np.where((e == top) & (m == (1 << mbits) - 1), np.nan, mag)
+    else:
+        mag = np.where(e == top, np.where(m == 0, np.inf, np.nan), mag)
+    return np.where(sign == 1, -mag, mag)
+
+
+def reference_fp8(a_bits, b_bits, a_fmt, b_fmt, scale_a, scale_b, out_dtype, epilog, bias_bits=None,
+                  bias_layout=None, residual_bits=None, rows=None):
+    """Y, Z and the mask (as ``reference``) for fp8 operands with per-tensor
+    fp32 scales: Z = scale_a scale_b (A8 . B8) + bias.  Products of two fp8
+    values are exact in fp64; the two fp32 scales multiply exactly in fp64.
+    bias_bits and residual_bits are in the 16-bit out_dtype."""
+    if epilog not in EPILOGS:
+        raise ValueError(f"unknown epilog {epilog!r}")
+    a_bits = np.asarray(a_bits, dtype=np.uint8)
+    r_bits = None if residual_bits is None else np.asarray(residual_bits, dtype=np.uint16)
+    row_bias = bias_bits
+    if rows is not None:
+        rows = np.asarray(rows, dtype=np.int64)
+        a_bits = a_bits[rows]
+        if r_bits is not None:
+            r_bits = r_bits[rows]
+        if bias_layout == "row" and bias_bits is not None:
+            row_bias = np.asarray(bias_bits, dtype=np.uint16).reshape(-1)[rows]
+    scale = float(np.float32(scale_a)) * float(np.float32(scale_b))
+    z = product(decode_fp8(a_bits, a_fmt), decode_fp8(b_bits, b_fmt)) * scale
+    if epilog != "DEFAULT":
+        if bias_bits is None or bias_layout is None:
+            raise ValueError(f"{epilog} needs a bias")
+        z = add_bias(z, widen(row_bias, out_dtype), bias_layout)
+    r64 = widen(r_bits, out_dtype) if r_bits is not None else None
     y = apply_epilog(z, epilog, r64)
     mask = relu_mask(z) if epilog == "RELU_AUX_BIAS" else None
     return y, z, mask

@@ -14,7 +14,8 @@ from fractions import Fraction
 
 import numpy as np
 
-from egm_workloads import BF16, F16, gemm_operands, integer_operands
+from egm_workloads import (BF16, E4M3, E5M2, F16, f32_to_fp8_bits, fp8_integer_operands, fp8_operands,
+                           gemm_operands, integer_operands)
 
 GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
 
@@ -428,6 +429,133 @@ def pin_bias_grad_error_bound(o):
     _, _, brow = o.backward_reference(ones_a, ones_b, F16, "DRELU_BGRAD", full, "row")
     assert np.allclose(bcol, (k + m) * 2.0 ** -24 * m * k, rtol=1e-15, atol=0)
     assert np.allclose(brow, (k + n) * 2.0 ** -24 * n * k, rtol=1e-15, atol=0)
+
+
+# ---------------------------------------------------------------------------
+# fp8 operands
+# ---------------------------------------------------------------------------
+def _parse_hexfloat(t):
+    if t in ("inf", "-inf", "nan"):
+        return float(t)
+    return float.fromhex(t)
+
+
+def pin_fp8_decode_golden(o):
+    """Hand-derived values of selected patterns (tests/golden/fp8_values.txt)."""
+    n = 0
+    with open(os.path.join(GOLDEN, "fp8_values.txt")) as f:
+        for line in f:
+            if not line.strip() or line.startswith("#"):
+                continue
+            fmt, bits, val = line.split()[:3]
+            got = float(o.decode_fp8(np.array([int(bits, 16)], dtype=np.uint8), fmt)[0])
+            want = _parse_hexfloat(val)
+            if math.isnan(want):
+                assert math.isnan(got), (fmt, bits, got)
+            else:
+                assert got == want and math.copysign(1.0, got) == math.copysign(1.0, want), (fmt, bits, got, want)
+            n += 1
+    assert n >= 20
+
+
+def pin_fp8_decode_library(o):
+    """All 256 patterns of both formats against torch's fp8 -> fp32 conversion."""
+    import torch
+    bits = np.arange(256, dtype=np.uint8)
+    for fmt, tdt in ((E4M3, torch.float8_e4m3fn), (E5M2, torch.float8_e5m2)):
+        mine = o.decode_fp8(bits, fmt)
+        ref = torch.from_numpy(bits).view(tdt).float().double().numpy()
+        assert np.array_equal(np.isnan(mine), np.isnan(ref)), fmt
+        ok = ~np.isnan(ref)
+        assert np.array_equal(mine[ok], ref[ok]), fmt
+        assert np.array_equal(np.signbit(mine[ok]), np.signbit(ref[ok])), fmt
+
+
+def pin_fp8_e5m2_is_fp16_high_byte(o):
+    """E5M2 has fp16's sign and exponent fields and its two top mantissa bits,
+    so a pattern followed by a zero byte is the same number in fp16."""
+    bits = np.arange(256, dtype=np.uint8)
+    as_f16 = (bits.astype(np.uint16) << np.uint16(8)).view(np.float16).astype(np.float64)
+    mine = o.decode_fp8(bits, E5M2)
+    ok = ~np.isnan(as_f16)
+    assert np.array_equal(np.isnan(mine), ~ok) and np.array_equal(mine[ok], as_f16[ok])
+
+
+def pin_fp8_brute_force(o):
+    """Exact rational brute force, every format pair and epilog but GELU, with
+    non-trivial fp32 scales: Z = sa sb sum(a b) + bias."""
+    shapes = [(1, 8, 1), (3, 16, 5), (5, 8, 9), (9, 24, 4)]
+    pairs = [(E4M3, E4M3), (E4M3, E5M2), (E5M2, E4M3), (E5M2, E5M2)]
+    for s, (m, n, k) in enumerate(shapes):
+        for pi, (fa, fb) in enumerate(pairs):
+            out = BF16 if (s + pi) % 2 else F16
+            layout = "row" if pi % 2 else "col"
+            ops = fp8_operands(m, n, k, fa, fb, out, seed=500 + 4 * s + pi, a_std=1.2, b_std=0.9,
+                               bias_layout=layout, bias_std=0.5, residual_std=0.7)
+            scale = Fraction(*float(ops.scale_a).as_integer_ratio()) * Fraction(*float(ops.scale_b).as_integer_ratio())
+            fa_ = [[Fraction(*float(v).as_integer_ratio()) * scale for v in row] for row in o.decode_fp8(ops.a, fa)]
+            fb_ = [[Fraction(*float(v).as_integer_ratio()) for v in row] for row in o.decode_fp8(ops.b, fb)]
+            bias = [Fraction(*float(v).as_integer_ratio()) for v in o.widen(ops.bias, out)]
+            r = _frac_of_bits(ops.residual, out, o)
+            for epilog in ("DEFAULT", "BIAS", "RELU_BIAS", "RELU_AUX_BIAS", "BIAS_RESIDUAL"):
+                y_ex, z_ex = _brute(fa_, fb_, bias, layout, r, epilog)
+                y, z, mask = o.reference_fp8(ops.a, ops.b, fa, fb, ops.scale_a, ops.scale_b, out, epilog,
+                                             ops.bias, layout, ops.residual)
+                for i in range(m):
+                    for j in range(n):
+                        assert abs(y[i, j] - float(y_ex[i][j])) <= 1e-12 * (1 + abs(float(y_ex[i][j]))), (epilog, i, j)
+                if epilog == "RELU_AUX_BIAS":
+                    want = np.packbits(np.array([[zz > 0 for zz in row] for row in z_ex]), axis=1, bitorder="little")
+                    assert np.array_equal(mask, want)
+
+
+def pin_fp8_matches_16bit_path(o):
+    """With unit scales, fp8 operands give the 16-bit path's result on the
+    same values: every E4M3 / E5M2 value is exact in fp16 and bf16 (the 16-bit
+    patterns come from torch's conversion, or from the E5M2 byte shifted into
+    fp16's high byte)."""
+    import torch
+    for fmt in (E4M3, E5M2):
+        for out in (F16, BF16):
+            ops = fp8_operands(12, 24, 40, fmt, fmt, out, seed=77, a_std=1.0, b_std=0.3, bias_layout="col")
+            one = np.float32(1.0)
+            tdt = torch.float8_e4m3fn if fmt == E4M3 else torch.float8_e5m2
+            to16 = torch.float16 if out == F16 else torch.bfloat16
+            if fmt == E5M2 and out == F16:
+                a16 = ops.a.astype(np.uint16) << np.uint16(8)
+                b16 = ops.b.astype(np.uint16) << np.uint16(8)
+            else:
+                a16 = torch.from_numpy(ops.a).view(tdt).to(to16).view(torch.int16).numpy().view(np.uint16)
+                b16 = torch.from_numpy(ops.b).view(tdt).to(to16).view(torch.int16).numpy().view(np.uint16)
+            for epilog in ("DEFAULT", "BIAS", "GELU_BIAS", "RELU_AUX_BIAS"):
+                y8, z8, m8 = o.reference_fp8(ops.a, ops.b, fmt, fmt, one, one, out, epilog, ops.bias, "col")
+                y16, z16, m16 = o.reference(a16, b16, out, epilog, ops.bias, "col")
+                assert np.array_equal(y8, y16) and np.array_equal(z8, z16), (fmt, out, epilog)
+                assert (m8 is None and m16 is None) or np.array_equal(m8, m16)
+
+
+def pin_fp8_scales(o):
+    """Power-of-two scales scale the product exactly and never the bias; the
+    two scales enter only through their product; integer operands give exact
+    integers."""
+    ops = fp8_integer_operands(16, 32, 24, E4M3, E5M2, BF16, seed=3, bias_layout="row")
+    one = np.float32(1.0)
+    y1, _, _ = o.reference_fp8(ops.a, ops.b, E4M3, E5M2, one, one, BF16, "DEFAULT")
+    ai = o.decode_fp8(ops.a, E4M3).astype(np.int64)
+    bi = o.decode_fp8(ops.b, E5M2).astype(np.int64)
+    assert np.array_equal(y1, ai @ bi)
+    y2, _, _ = o.reference_fp8(ops.a, ops.b, E4M3, E5M2, np.float32(8.0), np.float32(0.25), BF16, "DEFAULT")
+    assert np.array_equal(y2, 2.0 * y1)
+    sa, sb = np.float32(0.3), np.float32(1.7)
+    y3, _, _ = o.reference_fp8(ops.a, ops.b, E4M3, E5M2, sa, sb, BF16, "DEFAULT")
+    y4, _, _ = o.reference_fp8(ops.a, ops.b, E4M3, E5M2, sb, sa, BF16, "DEFAULT")
+    assert np.array_equal(y3, y4)
+    assert np.allclose(y3, y1 * (float(sa) * float(sb)), rtol=1e-15, atol=0)
+    # a zero B leaves the bias alone, whatever the scales
+    zb = f32_to_fp8_bits(np.zeros((24, 32), dtype=np.float32), E5M2)
+    y5, _, _ = o.reference_fp8(ops.a, zb, E4M3, E5M2, np.float32(3.0), np.float32(5.0), BF16, "BIAS",
+                               ops.bias, "row")
+    assert np.array_equal(y5, np.repeat(o.widen(ops.bias, BF16)[:, None], 32, axis=1))
 
 
 PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_")]

@@ -111,7 +111,52 @@ def _bound_without_k(a64, b64, mask, layout):
     return full * n_red / (k + n_red)
 
 
+def _fp8_subnormal_as_normal(bits, fmt):
+    ebits, mbits, bias = eo.FP8_FORMATS[fmt]
+    v = _orig["decode_fp8"](bits, fmt)
+    b = np.asarray(bits, dtype=np.uint8).astype(np.int64)
+    e, m = (b >> mbits) & ((1 << ebits) - 1), b & ((1 << mbits) - 1)
+    implicit = np.ldexp((m + (1 << mbits)).astype(np.float64), -bias - mbits)
+    return np.where(e == 0, np.where(b >> 7 == 1, -implicit, implicit), v)
+
+
+def _fp8_e5m2_no_infinity(bits, fmt):
+    v = _orig["decode_fp8"](bits, fmt)
+    if fmt != "e5m2":
+        return v
+    b = np.asarray(bits, dtype=np.uint8).astype(np.int64)
+    e, m = (b >> 2) & 31, b & 3
+    big = np.ldexp((m + 4).astype(np.float64), 31 - 15 - 2)
+    return np.where(e == 31, np.where(b >> 7 == 1, -big, big), v)
+
+
+def _fp8_scale_ignored(a, b, fa, fb, sa, sb, *args, **kw):
+    return _orig["reference_fp8"](a, b, fa, fb, np.float32(1), np.float32(1), *args, **kw)
+
+
+def _fp8_only_scale_a(a, b, fa, fb, sa, sb, *args, **kw):
+    return _orig["reference_fp8"](a, b, fa, fb, sa, np.float32(1), *args, **kw)
+
+
+def _fp8_scale_on_bias(a, b, fa, fb, sa, sb, out, epilog, bias_bits=None, bias_layout=None,
+                       residual_bits=None, rows=None):
+    s = float(np.float32(sa)) * float(np.float32(sb))
+    z = eo.product(eo.decode_fp8(a, fa), eo.decode_fp8(b, fb))
+    if epilog != "DEFAULT":
+        z = eo.add_bias(z, eo.widen(bias_bits, out), bias_layout)
+    z = z * s
+    r64 = eo.widen(residual_bits, out) if residual_bits is not None else None
+    y = eo.apply_epilog(z, epilog, r64)
+    return y, z, (eo.relu_mask(z) if epilog == "RELU_AUX_BIAS" else None)
+
+
 MUTANTS = {
+    "fp8_e4m3_bias_8": ("FP8_FORMATS", {"e4m3": (4, 3, 8), "e5m2": (5, 2, 15)}),
+    "fp8_subnormal_as_normal": ("decode_fp8", _fp8_subnormal_as_normal),
+    "fp8_e5m2_no_infinity": ("decode_fp8", _fp8_e5m2_no_infinity),
+    "fp8_scale_ignored": ("reference_fp8", _fp8_scale_ignored),
+    "fp8_only_scale_a": ("reference_fp8", _fp8_only_scale_a),
+    "fp8_scale_on_bias": ("reference_fp8", _fp8_scale_on_bias),
     "bias_dropped": ("add_bias", _drop_bias),
     "bias_layout_swapped": ("add_bias", _swapped_layout),
     "product_drops_last_k": ("product", _drop_last_k),

@@ -80,3 +80,23 @@ def test_backward_workload_and_mask_recipe():
         W.mask_bits(4, 12, seed=0, tensor_index=2)
     w = W.BACKWARD_WORKLOADS["drelu_bgrad_bf16_8192x8192x8192"]
     assert (w.m, w.n, w.k, w.dtype, w.bias_layout) == (8192, 8192, 8192, W.BF16, "col")
+
+
+def test_fp8_quantize_recipe():
+    x = W.normal_f32((300, 70), 0.5, seed=4, tensor_index=0)
+    assert np.array_equal(W.bits_to_f32(W.normal_bits((300, 70), 0.5, W.BF16, 4, 0), W.BF16),
+                          W.bits_to_f32(W.f32_to_bits(x, W.BF16), W.BF16))  # the same draws
+    for fmt in W.FP8:
+        q, s = W.fp8_quantize(x, fmt)
+        assert q.dtype == np.uint8 and q.shape == x.shape and s.dtype == np.float32
+        assert s == np.float32(float(np.abs(x).max()) / W.FP8_MAX[fmt])
+        import torch
+        back = torch.from_numpy(q).view(torch.float8_e4m3fn if fmt == W.E4M3 else torch.float8_e5m2).float().numpy()
+        assert np.abs(back).max() == W.FP8_MAX[fmt]  # amax maps to the largest finite value
+        rel = np.abs(back * s - x) / np.maximum(np.abs(x), 1e-3)
+        assert np.median(rel) < (2.0 ** -4 if fmt == W.E4M3 else 2.0 ** -3)
+    # saturation instead of NaN beyond the largest finite value
+    big = W.f32_to_fp8_bits(np.array([1e6, -1e6], dtype=np.float32), W.E4M3)
+    assert list(big) == [0x7E, 0xFE]
+    w = W.FP8_WORKLOADS["gemm_relu_aux_bias_fp8e4m3_8192x8192x8192"]
+    assert (w.m, w.n, w.k, w.dtype, w.bias_layout) == (8192, 8192, 8192, W.BF16, "col")
