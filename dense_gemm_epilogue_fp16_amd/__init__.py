@@ -39,6 +39,10 @@ EGM_ERR_WORKSPACE = 9
 EGM_F16 = 0
 EGM_BF16 = 1
 
+# fp8 operand formats (egm_fp8_format_t)
+EGM_E4M3 = 0
+EGM_E5M2 = 1
+
 # epilogues (egm_epilog_t)
 EPILOGS = {
     "DEFAULT": 0,
@@ -59,7 +63,7 @@ EGM_BIAS_COL = 2  # shape (1, n)
 
 #: every symbol include/egm.h declares
 EXPORTS = (
-    "egm_plan", "egm_execute", "egm_free", "egm_plan_workspace_bytes", "egm_plan_describe",
+    "egm_plan", "egm_plan_fp8", "egm_execute", "egm_free", "egm_plan_workspace_bytes", "egm_plan_describe",
     "egm_plan_config", "egm_num_configs", "egm_config_describe", "egm_status_string", "egm_abi_version",
 )
 
@@ -97,6 +101,9 @@ def _load() -> ctypes.CDLL:
     lib.egm_plan.argtypes = [ctypes.POINTER(vp), i64, i64, i64, i32, i32, ctypes.POINTER(EpilogInputs),
                              ctypes.POINTER(PlanOptions)]
     lib.egm_plan.restype = i32
+    lib.egm_plan_fp8.argtypes = [ctypes.POINTER(vp), i64, i64, i64, i32, i32, i32, vp, vp, i32,
+                                 ctypes.POINTER(EpilogInputs), ctypes.POINTER(PlanOptions)]
+    lib.egm_plan_fp8.restype = i32
     lib.egm_execute.argtypes = [vp, vp, vp, vp, vp, vp, sz, vp]
     lib.egm_execute.restype = i32
     lib.egm_free.argtypes = [vp]
@@ -145,6 +152,22 @@ def egm_plan(m: int, n: int, k: int, dtype: int, epilog: int, bias: int = 0, bia
     if raw_status:
         return st, h.value
     _check(st, "egm_plan")
+    return h.value
+
+
+def egm_plan_fp8(m: int, n: int, k: int, a_format: int, b_format: int, out_dtype: int, scale_a: int, scale_b: int,
+                 epilog: int, bias: int = 0, bias_layout: int = EGM_BIAS_NONE, residual: int = 0, *, fused: int = 1,
+                 force_config: int = -1, autotune: int = 0, group_m: int = 0, raw_status: bool = False):
+    """fp8 operands with per-tensor scales (device pointers to one fp32 each,
+    0 = NULL = 1); returns the plan handle, or (status, handle) with ``raw_status``."""
+    h = ctypes.c_void_p()
+    ins = EpilogInputs(bias or None, bias_layout, residual or None, None)
+    opt = PlanOptions(fused, force_config, autotune, group_m)
+    st = LIB.egm_plan_fp8(ctypes.byref(h), int(m), int(n), int(k), int(a_format), int(b_format), int(out_dtype),
+                          scale_a or None, scale_b or None, int(epilog), ctypes.byref(ins), ctypes.byref(opt))
+    if raw_status:
+        return st, h.value
+    _check(st, "egm_plan_fp8")
     return h.value
 
 
@@ -199,11 +222,22 @@ def egm_abi_version() -> int:
 # ---------------------------------------------------------------------------
 def _dtype_code(t) -> int:
     import torch
-    if t.dtype == torch.float16:
+    dt = t if isinstance(t, torch.dtype) else t.dtype
+    if dt == torch.float16:
         return EGM_F16
-    if t.dtype == torch.bfloat16:
+    if dt == torch.bfloat16:
         return EGM_BF16
-    raise TypeError(f"dtype {t.dtype} not supported: fp16 or bf16 only")
+    raise TypeError(f"dtype {dt} not supported: fp16 or bf16 only")
+
+
+def _fp8_code(t):
+    """egm_fp8_format_t of an fp8 tensor (OCP float8_e4m3fn / float8_e5m2), else None."""
+    import torch
+    if t.dtype == torch.float8_e4m3fn:
+        return EGM_E4M3
+    if t.dtype == torch.float8_e5m2:
+        return EGM_E5M2
+    return None
 
 
 class Matmul:
@@ -219,30 +253,57 @@ class Matmul:
     with ``g`` a float32 tensor shaped (m,1) (gradient of an (m,1) bias: row
     sums) or (1,n) (of a (1,n) bias: column sums); ``execute(aux=mask)`` takes
     the forward RELU_AUX_BIAS mask as input and returns D (and ``g``).
+
+    fp8: ``a`` and ``b`` of dtype float8_e4m3fn / float8_e5m2 (any pairing),
+    ``scale_a`` / ``scale_b`` one-element float32 GPU tensors (None = 1),
+    ``out_dtype`` fp16 or bf16 (default bf16) for D, the bias and the residual.
     """
 
-    def __init__(self, a, b):
-        self._check_operand(a, "a")
-        self._check_operand(b, "b")
+    def __init__(self, a, b, *, scale_a=None, scale_b=None, out_dtype=None):
+        import torch
+        fa, fb = _fp8_code(a), _fp8_code(b)
+        self.fp8 = None
+        if fa is not None or fb is not None:
+            if fa is None or fb is None:
+                raise TypeError("fp8 operands come in pairs (no implicit conversion)")
+            self.fp8 = (fa, fb)
+            out_dtype = torch.bfloat16 if out_dtype is None else out_dtype
+            _dtype_code(out_dtype)
+            for t, name in ((scale_a, "scale_a"), (scale_b, "scale_b")):
+                if t is not None and (not t.is_cuda or t.dtype != torch.float32 or t.numel() != 1):
+                    raise ValueError(f"{name} must be a one-element float32 GPU tensor")
+        else:
+            if scale_a is not None or scale_b is not None:
+                raise ValueError("scales belong to fp8 operands")
+            if out_dtype is not None and out_dtype != a.dtype:
+                raise TypeError("16-bit operands produce their own dtype (no implicit conversion)")
+            out_dtype = a.dtype
+        self._check_operand(a, "a", fp8=self.fp8 is not None)
+        self._check_operand(b, "b", fp8=self.fp8 is not None)
         if a.dim() != 2 or b.dim() != 2 or a.shape[1] != b.shape[0]:
             raise ValueError(f"shapes {tuple(a.shape)} and {tuple(b.shape)} do not multiply")
-        if a.dtype != b.dtype:
+        if self.fp8 is None and a.dtype != b.dtype:
             raise TypeError("a and b must share one dtype (no implicit conversion)")
         self.a, self.b = a, b
+        self.scale_a, self.scale_b = scale_a, scale_b
         self.m, self.k = a.shape
         self.n = b.shape[1]
-        self.dtype = a.dtype
+        self.dtype = out_dtype
         self._plan = None
         self._keep = ()
         self.epilog = None
 
     @staticmethod
-    def _check_operand(t, name):
+    def _check_operand(t, name, fp8=False):
         if not t.is_cuda:
             raise ValueError(f"{name} must be a GPU tensor")
         if not t.is_contiguous():
             raise ValueError(f"{name} must be contiguous row-major")
-        _dtype_code(t)
+        if fp8:
+            if _fp8_code(t) is None:
+                raise TypeError(f"{name}: dtype {t.dtype} is not an fp8 operand type")
+        else:
+            _dtype_code(t)
 
     def plan(self, epilog: str = "DEFAULT", epilog_inputs: dict | None = None, *, fused: bool = True,
              force_config: int = -1, autotune: bool = False, group_m: int = 0):
@@ -290,9 +351,19 @@ class Matmul:
             res_ptr = r.data_ptr()
             keep.append(r)
         self.free()
-        self._plan = egm_plan(self.m, self.n, self.k, _dtype_code(self.a), EPILOGS[epilog], bias_ptr, layout,
-                              res_ptr, bias_grad=grad_ptr, fused=int(fused), force_config=force_config,
-                              autotune=int(autotune), group_m=group_m)
+        if self.fp8 is not None:
+            if grad_ptr:
+                raise ValueError("the backward epilogues take 16-bit operands")
+            sa = self.scale_a.data_ptr() if self.scale_a is not None else 0
+            sb = self.scale_b.data_ptr() if self.scale_b is not None else 0
+            keep += [t for t in (self.scale_a, self.scale_b) if t is not None]
+            self._plan = egm_plan_fp8(self.m, self.n, self.k, self.fp8[0], self.fp8[1], _dtype_code(self.dtype), sa,
+                                      sb, EPILOGS[epilog], bias_ptr, layout, res_ptr, fused=int(fused),
+                                      force_config=force_config, autotune=int(autotune), group_m=group_m)
+        else:
+            self._plan = egm_plan(self.m, self.n, self.k, _dtype_code(self.a), EPILOGS[epilog], bias_ptr, layout,
+                                  res_ptr, bias_grad=grad_ptr, fused=int(fused), force_config=force_config,
+                                  autotune=int(autotune), group_m=group_m)
         self._keep = tuple(keep)
         self.epilog = epilog
         self._ws = None
@@ -315,9 +386,9 @@ class Matmul:
         plan = self._require()
         a = self.a if a is None else a
         b = self.b if b is None else b
-        for t, shape in ((a, (self.m, self.k)), (b, (self.k, self.n))):
-            self._check_operand(t, "operand")
-            if tuple(t.shape) != shape or t.dtype != self.dtype:
+        for t, shape, dt in ((a, (self.m, self.k), self.a.dtype), (b, (self.k, self.n), self.b.dtype)):
+            self._check_operand(t, "operand", fp8=self.fp8 is not None)
+            if tuple(t.shape) != shape or t.dtype != dt:
                 raise ValueError("rebound operand must keep the planned shape and dtype")
         d = out if out is not None else torch.empty((self.m, self.n), dtype=self.dtype, device=a.device)
         mask = None

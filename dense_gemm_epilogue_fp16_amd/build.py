@@ -2,9 +2,9 @@
 
     python -m dense_gemm_epilogue_fp16_amd.build      # or build() from Python
 
-Translation units: egm_kernels.hip once per dtype (fp16, bf16) and the host
-API egm_api.hip, compiled in parallel, then linked into one shared library
-next to this file.
+Translation units: egm_kernels.hip once per 16-bit dtype (fp16, bf16) and
+once per (fp8 format pair, output dtype), and the host API egm_api.hip,
+compiled in parallel, then linked into one shared library next to this file.
 """
 from __future__ import annotations
 
@@ -35,11 +35,18 @@ def hipcc() -> str:
 
 
 def _units(obj_dir: str):
-    return [
-        (os.path.join(CSRC, "egm_kernels.hip"), os.path.join(obj_dir, "egm_kernels_f16.o"), ["-DEGM_DTYPE=0"]),
-        (os.path.join(CSRC, "egm_kernels.hip"), os.path.join(obj_dir, "egm_kernels_bf16.o"), ["-DEGM_DTYPE=1"]),
+    kernels = os.path.join(CSRC, "egm_kernels.hip")
+    units = [
+        (kernels, os.path.join(obj_dir, "egm_kernels_f16.o"), ["-DEGM_DTYPE=0"]),
+        (kernels, os.path.join(obj_dir, "egm_kernels_bf16.o"), ["-DEGM_DTYPE=1"]),
         (os.path.join(CSRC, "egm_api.hip"), os.path.join(obj_dir, "egm_api.o"), []),
     ]
+    # fp8 operands: one unit per (output dtype, format pair)
+    for dt in (0, 1):
+        for f8 in (1, 2, 3, 4):
+            units.append((kernels, os.path.join(obj_dir, f"egm_kernels_fp8_{dt}_{f8}.o"),
+                          [f"-DEGM_DTYPE={dt}", f"-DEGM_F8={f8}"]))
+    return units
 
 
 def _run(cmd, verbose):
@@ -60,7 +67,7 @@ def build(verbose: bool = False, extra_flags=None) -> str:
     with tempfile.TemporaryDirectory(prefix="egm_build_") as obj_dir:
         units = _units(obj_dir)
         cmds = [[cc, *COMMON, *DEVICE_FLAGS, *defs, *extra, "-c", src, "-o", obj] for src, obj, defs in units]
-        with ThreadPoolExecutor(len(cmds)) as ex:
+        with ThreadPoolExecutor(min(len(cmds), max(1, os.cpu_count() or 1))) as ex:
             list(ex.map(lambda c: _run(c, verbose), cmds))
         tmp = LIB + ".tmp"
         _run([cc, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *[o for _, o, _ in units]], verbose)

@@ -90,6 +90,9 @@ struct egm_plan_s {
   size_t workspace_bytes;
   size_t product_bytes;      // the two-kernel path's P at the start of the workspace
   int64_t grad_len;          // DRELU_BGRAD: length of the gradient (n or m)
+  int32_t f8;                // 0: 16-bit operands; 1 + fa + 2 fb: fp8 operands (formats of A, B)
+  const float* scale_a;      // fp8: per-tensor scales (device, may be NULL)
+  const float* scale_b;
 };
 
 namespace {
@@ -114,12 +117,19 @@ int32_t effective_group_m(const egm_plan_s* p, int cfg) {
 
 void describe(const egm_plan_s* p, char* buf, size_t len) {
   const ConfigInfo& c = kConfigs[p->config];
+  static const char* fmt8[2] = {"e4m3", "e5m2"};
+  char operands[40];
+  if (p->f8 != 0)
+    snprintf(operands, sizeof(operands), "%sx%s", fmt8[(p->f8 - 1) & 1], fmt8[(p->f8 - 1) >> 1]);
+  else
+    snprintf(operands, sizeof(operands), "%s", p->dtype == EGM_F16 ? "fp16" : "bf16");
   snprintf(buf, len,
-           "egm m=%lld n=%lld k=%lld dtype=%s epilog=%s bias=%s path=%s tile=%dx%d kslab=%d waves=%dx%d "
-           "mfma=32x32x16 lds_ring=%d group_m=%d tiles=%lld workspace=%zu%s",
-           (long long)p->m, (long long)p->n, (long long)p->k, p->dtype == EGM_F16 ? "fp16" : "bf16",
+           "egm m=%lld n=%lld k=%lld operands=%s dtype=%s epilog=%s bias=%s path=%s tile=%dx%d kslab=%d waves=%dx%d "
+           "mfma=%s lds_ring=%d group_m=%d tiles=%lld workspace=%zu%s",
+           (long long)p->m, (long long)p->n, (long long)p->k, operands, p->dtype == EGM_F16 ? "fp16" : "bf16",
            epilog_name(p->epilog), p->bias_layout == EGM_BIAS_ROW ? "row(m,1)" : p->bias_layout == EGM_BIAS_COL ? "col(1,n)" : "none",
-           p->fused ? "fused" : "unfused(gemm+epilogue)", c.bm, c.bn, c.bk, c.wm, c.wn, c.stages, effective_group_m(p, p->config),
+           p->fused ? "fused" : "unfused(gemm+epilogue)", c.bm, c.bn, p->f8 != 0 ? 2 * c.bk : c.bk, c.wm, c.wn,
+           p->f8 != 0 ? "32x32x64" : "32x32x16", c.stages, effective_group_m(p, p->config),
            (long long)(cdiv(p->m, c.bm) * cdiv(p->n, c.bn)), p->workspace_bytes,
            p->autotune_pending ? " autotune=pending" : "");
 }
@@ -137,6 +147,8 @@ hipError_t launch_plan(const egm_plan_s* p, int cfg, const void* A, const void* 
   g.R = p->residual;
   g.aux = aux;
   g.partial = partial;
+  g.scale_a = p->scale_a;
+  g.scale_b = p->scale_b;
   g.M = int32_t(p->m);
   g.N = int32_t(p->n);
   g.K = int32_t(p->k);
@@ -148,7 +160,8 @@ hipError_t launch_plan(const egm_plan_s* p, int cfg, const void* A, const void* 
   const int epi = epi_of(p->epilog);
   const bool two_kernels = !p->fused && epi != egm::EPI_NONE;
   g.D = two_kernels ? ws : D;
-  GemmLaunch gl = egm::gemm_launcher(dt, two_kernels ? egm::EPI_NONE : epi, cfg);
+  const int gemm_epi = two_kernels ? egm::EPI_NONE : epi;
+  GemmLaunch gl = p->f8 != 0 ? egm::gemm_launcher_fp8(dt, p->f8, gemm_epi, cfg) : egm::gemm_launcher(dt, gemm_epi, cfg);
   if (gl == nullptr) return hipErrorInvalidValue;
   gl(grid, s, g);
   hipError_t err = hipGetLastError();
@@ -226,19 +239,21 @@ hipError_t autotune(egm_plan_s* p, const void* A, const void* B, void* D, void* 
   return err;
 }
 
-}  // namespace
-
-extern "C" {
-
-egm_status_t egm_plan(egm_plan_t* out, int64_t m, int64_t n, int64_t k, egm_dtype_t dtype,
-                      egm_epilog_t epilog, const egm_epilog_inputs_t* in, const egm_plan_options_t* opt) {
+// Validation and construction shared by egm_plan (f8 = 0) and egm_plan_fp8.
+egm_status_t plan_impl(egm_plan_t* out, int64_t m, int64_t n, int64_t k, egm_dtype_t dtype, int32_t f8,
+                       const float* scale_a, const float* scale_b, egm_epilog_t epilog,
+                       const egm_epilog_inputs_t* in, const egm_plan_options_t* opt) {
   if (out == nullptr) return EGM_ERR_INVALID_VALUE;
   *out = nullptr;
   if (m < 0 || n < 0 || k < 0) return EGM_ERR_SHAPE;
-  if ((n % 8) != 0 || (k % 8) != 0) return EGM_ERR_SHAPE;
+  const int64_t row_elems = f8 != 0 ? 16 : 8;  // elements per 16-byte operand row piece
+  if ((n % row_elems) != 0 || (k % row_elems) != 0) return EGM_ERR_SHAPE;
   if (n > kMaxNK || k > kMaxNK || m > int64_t(0x7fffffff)) return EGM_ERR_SHAPE;
   if (dtype != EGM_F16 && dtype != EGM_BF16) return EGM_ERR_DTYPE;
   if (int(epilog) < 0 || int(epilog) >= kNumEpi) return EGM_ERR_INVALID_VALUE;
+  if (f8 != 0 && (epilog == EGM_EPILOG_DRELU || epilog == EGM_EPILOG_DRELU_BGRAD)) return EGM_ERR_NOT_SUPPORTED;
+  if ((reinterpret_cast<uintptr_t>(scale_a) & 3u) != 0 || (reinterpret_cast<uintptr_t>(scale_b) & 3u) != 0)
+    return EGM_ERR_ALIGNMENT;
 
   const void* bias = nullptr;
   const void* residual = nullptr;
@@ -296,6 +311,9 @@ egm_status_t egm_plan(egm_plan_t* out, int64_t m, int64_t n, int64_t k, egm_dtyp
   p->bias_layout = layout;
   p->residual = residual;
   p->bias_grad = bias_grad;
+  p->f8 = f8;
+  p->scale_a = scale_a;
+  p->scale_b = scale_b;
   p->fused = fused;
   p->config = force >= 0 ? force : choose_config(m, n, k);
   // the grid is one workgroup per output tile and tile ids are 32-bit
@@ -327,6 +345,27 @@ egm_status_t egm_plan(egm_plan_t* out, int64_t m, int64_t n, int64_t k, egm_dtyp
   }
   *out = p;
   return EGM_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+egm_status_t egm_plan(egm_plan_t* out, int64_t m, int64_t n, int64_t k, egm_dtype_t dtype,
+                      egm_epilog_t epilog, const egm_epilog_inputs_t* in, const egm_plan_options_t* opt) {
+  return plan_impl(out, m, n, k, dtype, 0, nullptr, nullptr, epilog, in, opt);
+}
+
+egm_status_t egm_plan_fp8(egm_plan_t* out, int64_t m, int64_t n, int64_t k, egm_fp8_format_t a_format,
+                          egm_fp8_format_t b_format, egm_dtype_t out_dtype, const float* scale_a,
+                          const float* scale_b, egm_epilog_t epilog, const egm_epilog_inputs_t* in,
+                          const egm_plan_options_t* opt) {
+  if (out == nullptr) return EGM_ERR_INVALID_VALUE;
+  *out = nullptr;
+  const bool known = (a_format == EGM_E4M3 || a_format == EGM_E5M2) && (b_format == EGM_E4M3 || b_format == EGM_E5M2);
+  if (!known) return EGM_ERR_DTYPE;
+  const int32_t f8 = 1 + int32_t(a_format) + 2 * int32_t(b_format);
+  return plan_impl(out, m, n, k, out_dtype, f8, scale_a, scale_b, epilog, in, opt);
 }
 
 egm_status_t egm_execute(egm_plan_t plan, const void* A, const void* B, void* D, void* aux, void* workspace,

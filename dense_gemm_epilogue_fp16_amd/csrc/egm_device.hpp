@@ -18,6 +18,8 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x8 __attribute__((ext_vector_type(8)));
+typedef int i32x8 __attribute__((ext_vector_type(8)));
 
 enum DType { DT_F16 = 0, DT_BF16 = 1 };
 
@@ -127,6 +129,19 @@ __device__ __forceinline__ f32x16 mfma32(u32x4 a, u32x4 b, f32x16 c) {
     return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a),
                                                    __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
   }
+}
+
+// fp8 operands: v_mfma_f32_32x32x64_f8f6f4, 64 k-values per instruction.
+// Each operand is 32 bytes per lane: lane l holds row (column) l % 32 and the
+// k-values 32 (l / 32) .. +31 in byte order (checked on the GPU with an
+// in-bounds probe against a host product, all four format pairs).  FA / FB
+// select the format of the first / second operand: 0 E4M3, 1 E5M2.  The
+// scaled form of the builtin with zero scale operands is the plain
+// instruction (no block scaling).
+template <int FA, int FB>
+__device__ __forceinline__ f32x16 mfma32_f8(u32x8 a, u32x8 b, f32x16 c) {
+  return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(__builtin_bit_cast(i32x8, a), __builtin_bit_cast(i32x8, b),
+                                                         c, FA, FB, 0, 0, 0, 0);
 }
 
 // ---------------------------------------------------------------------------

@@ -52,23 +52,28 @@ struct GemmArgs {
   float* partial;    // DRELU_BGRAD: fp32 partial sums of dZ, one row of them per tile row
                      // ((1,n) bias: [ceil(M/BM), N]) or per tile column ((m,1) bias:
                      // [ceil(N/BN), M])
+  const float* scale_a;  // fp8 operands: per-tensor dequantisation scales (one fp32 each;
+  const float* scale_b;  // NULL = 1), read once per workgroup
   int32_t M, N, K;
   int32_t bias_layout;
   int32_t tiles_m, tiles_n;
   int32_t group_m;
 };
 
-template <int BM_, int BN_, int STAGES_ = 4, int WM_ = 2, int WN_ = 2, int BK_ = 32>
+template <int BM_, int BN_, int STAGES_ = 4, int WM_ = 2, int WN_ = 2, int BK_ = 32, int ES_ = 2>
 struct TileCfg {
   static constexpr int BM = BM_, BN = BN_, BK = BK_, STAGES = STAGES_;
+  static constexpr int ES = ES_;                      // operand element bytes: 2 (fp16/bf16) or 1 (fp8)
   static constexpr int WM = WM_, WN = WN_;            // WM x WN waves
   static constexpr int NW = WM * WN, NT = 64 * NW;
   static constexpr int WTM = BM / WM, WTN = BN / WN;  // wave sub-tile
   static constexpr int FM = WTM / 32, FN = WTN / 32;  // 32x32 blocks per wave
-  static constexpr int NS = BK / 16;                  // 16-deep k-slices per slab
-  static constexpr int A_ROW = BK * 2;                // bytes per A row in LDS
+  static constexpr int KI = ES == 2 ? 16 : 64;        // k per MFMA instruction
+  static constexpr int NS = BK / KI;                  // k-slices per slab
+  static constexpr int CE = 16 / ES;                  // elements per 16-byte chunk
+  static constexpr int A_ROW = BK * ES;               // bytes per A row in LDS
   static constexpr int A_CHUNKS = A_ROW / 16;         // 16-byte chunks per A row
-  static constexpr int B_ROW = BN * 2;                // bytes per B k-row in LDS
+  static constexpr int B_ROW = BN * ES;               // bytes per B k-row in LDS
   static constexpr int A_BYTES = BM * A_ROW;
   static constexpr int B_BYTES = BK * B_ROW;
   static constexpr int STAGE_BYTES = A_BYTES + B_BYTES;
@@ -78,10 +83,10 @@ struct TileCfg {
   static constexpr int A_PW = A_DMA / NW, B_PW = B_DMA / NW;  // per wave
   static constexpr int PW = A_PW + B_PW;
   static constexpr int A_ROWS_PER_DMA = 1024 / A_ROW;
-  static constexpr int B_CHUNKS = BN / 8;                   // 16-byte chunks per B row
+  static constexpr int B_CHUNKS = B_ROW / 16;               // 16-byte chunks per B row
   static constexpr int B_ROWS_PER_DMA = 1024 / B_ROW;
   static_assert(FM >= 1 && FN >= 1, "tile too small for the wave grid of 32x32 blocks");
-  static_assert(BK == 32 || BK == 64, "slabs are 32 or 64 deep");
+  static_assert(ES == 2 ? (BK == 32 || BK == 64) : (ES == 1 && BK == 128), "slabs are 32 or 64 (16-bit) or 128 (fp8) deep");
   static_assert(A_DMA % NW == 0 && B_DMA % NW == 0, "slab must split into whole loads per wave");
   static_assert((STAGES - 1) * PW < 64, "outstanding loads must fit the 6-bit vmcnt");
   // per-wave epilogue stage: 32 rows of the wave tile in T, then 32 mask rows
@@ -109,10 +114,21 @@ __device__ __forceinline__ uint32_t a_swz(uint32_t row) {
   else return (row >> 1) & 7u;
 }
 
-// B: chunk index bits 2..3 are XOR-ed with k mod 4, so the four k-rows a
-// transposing read touches at once land on different 64-byte bank groups.
-template <int B_CHUNKS>
-__device__ __forceinline__ uint32_t b_swz(uint32_t krow) { return ((krow & 3u) << 2) & (B_CHUNKS - 1); }
+// B, 16-bit: chunk index bits 2..3 are XOR-ed with k mod 4, so the four
+// k-rows a transposing read touches at once land on different 64-byte bank
+// groups.  fp8: one 8-bit transposing read takes a 16-byte chunk pair from 8
+// consecutive k-rows per half-wave; the pair index is XOR-ed with the k-row's
+// position among the rows that share a 256-byte bank window, so the 8 pairs
+// cover all 64 banks (rows of 256, 128 or 64 bytes).
+template <int B_CHUNKS, int ES = 2>
+__device__ __forceinline__ uint32_t b_swz(uint32_t krow) {
+  if constexpr (ES == 2) {
+    return ((krow & 3u) << 2) & (B_CHUNKS - 1);
+  } else {
+    constexpr uint32_t RPW = B_CHUNKS >= 16 ? 1 : 16 / B_CHUNKS;  // k-rows per 256-byte window
+    return ((krow / RPW) & (B_CHUNKS / 2 - 1)) << 1;
+  }
+}
 
 // Workgroup -> output tile.  Workgroups are handed to the 8 XCDs round-robin
 // (bid % 8), and each XCD has its own L2: give each XCD one contiguous run of
@@ -179,6 +195,16 @@ __device__ __forceinline__ u32x2 lds_read_tr(const uint8_t* p) {
     typedef __attribute__((address_space(3))) b4* bp;
     return __builtin_bit_cast(u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4bf16((bp)(lds_ptr)p));
   }
+}
+
+// 8-bit transposing LDS read: within each 16-lane group, lane i receives byte
+// (i mod 8) of the 8-byte rows addressed by lanes i/8, 2 + i/8, .., 14 + i/8,
+// in that order (checked on the GPU with an in-bounds probe).
+__device__ __forceinline__ u32x2 lds_read_tr8(const uint8_t* p) {
+  typedef int i2 __attribute__((ext_vector_type(2)));
+  typedef __attribute__((address_space(3))) i2* lp;
+  typedef __attribute__((address_space(3))) void* lds_ptr;
+  return __builtin_bit_cast(u32x2, __builtin_amdgcn_ds_read_tr8_b64_v2i32((lp)(lds_ptr)p));
 }
 
 // s_waitcnt lgkmcnt(n) with the other counters left alone (gfx9 encoding).
@@ -256,10 +282,10 @@ __device__ __forceinline__ float block_column_sum(float (&v)[16], int lane) {
 // Epilogue on the fp32 accumulators of one wave, then the store.
 // lane holds D[m0 + wm0 + 32i + lr][n0 + wn0 + 32j + 8g + 4lh + e] = acc[i][j][4g + e]
 // ---------------------------------------------------------------------------
-template <int DT, int EPI, int WM, int WN, int FM, int FN>
+template <int DT, int EPI, int WM, int WN, bool SCALED, int FM, int FN>
 __device__ __forceinline__ void epilogue_store(const GemmArgs& p, f32x16 (&acc)[FM][FN], int m0, int n0, int wm0,
                                                int wn0, int lane, uint8_t* stage,
-                                               const uint8_t* bias_lds, float* red) {
+                                               const uint8_t* bias_lds, float* red, float scale) {
   const int M = p.M, N = p.N;
   // The packed outputs of one 32-row block-row go through this wave's private
   // LDS stage so that D leaves as 16-byte row chunks, 4 full rows of the wave
@@ -369,6 +395,7 @@ __device__ __forceinline__ void epilogue_store(const GemmArgs& p, f32x16 (&acc)[
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           z[e] = acc[i][j][4 * g + e];
+          if constexpr (SCALED) z[e] *= scale;  // fp8: the two per-tensor scales, before the bias
           if constexpr (epi_adds_bias(EPI)) z[e] += brow + bcol[j][g][e];
           if constexpr (epi_reads_mask(EPI)) z[e] = ((keep[i][j] >> (8 * g + 4 * lh + e)) & 1u) ? z[e] : 0.0f;
           if constexpr (EPI == EPI_DRELU_BGRAD) {
@@ -491,8 +518,12 @@ __device__ __forceinline__ void epilogue_store(const GemmArgs& p, f32x16 (&acc)[
   }
 }
 
-template <int DT, int EPI, class C>
+// DT: the output (and bias / residual) type, and the operand type when F8 is 0.
+// F8 = 1 + fa + 2 fb for fp8 operands (fa, fb: 0 E4M3, 1 E5M2 for A and B),
+// with C::ES == 1.
+template <int DT, int EPI, class C, int F8 = 0>
 __global__ void __launch_bounds__(C::NT, 1) gemm_epilogue_kernel(GemmArgs p) {
+  static_assert((F8 == 0) == (C::ES == 2), "fp8 kernels use one-byte tiles");
   // the k-slab ring, then the tile's bias slice
   __shared__ __attribute__((aligned(1024))) uint8_t smem[C::LDS_BYTES + 1024];
   uint8_t* const bias_lds = smem + C::LDS_BYTES;
@@ -508,6 +539,13 @@ __global__ void __launch_bounds__(C::NT, 1) gemm_epilogue_kernel(GemmArgs p) {
   const int m0 = tm * C::BM;
   const int n0 = tn * C::BN;
   const int KT = (K + C::BK - 1) / C::BK;
+  // fp8: the product of the two per-tensor scales (uniform; NULL reads as 1)
+  float scale = 1.0f;
+  if constexpr (F8 != 0) {
+    const float sa = p.scale_a != nullptr ? *p.scale_a : 1.0f;
+    const float sb = p.scale_b != nullptr ? *p.scale_b : 1.0f;
+    scale = sa * sb;
+  }
 
   // A (1,n) bias: wave 0 copies the tile's BN values straight into LDS ahead
   // of the operand loads (its completion is covered by the prologue's wait;
@@ -531,8 +569,8 @@ __global__ void __launch_bounds__(C::NT, 1) gemm_epilogue_kernel(GemmArgs p) {
     const uint32_t q = wave * C::A_PW + u;
     const uint32_t row = C::A_ROWS_PER_DMA * q + lane / C::A_CHUNKS;
     const uint32_t lc = (lane % C::A_CHUNKS) ^ a_swz<C::A_CHUNKS>(row);
-    a_k8[u] = lc * 8;
-    a_off[u] = (row * (uint32_t)K + lc * 8) * 2u;
+    a_k8[u] = lc * C::CE;
+    a_off[u] = (row * (uint32_t)K + lc * C::CE) * C::ES;
   }
   // B load q fills k-rows q*R .. q*R+R-1 (R = B_ROWS_PER_DMA): lane L -> k-row
   // q*R + L/B_CHUNKS, physical chunk L%B_CHUNKS holding logical chunk
@@ -543,8 +581,8 @@ __global__ void __launch_bounds__(C::NT, 1) gemm_epilogue_kernel(GemmArgs p) {
   for (int u = 0; u < C::B_PW; ++u) {
     const uint32_t q = wave * C::B_PW + u;
     const uint32_t krow = q * C::B_ROWS_PER_DMA + lane / C::B_CHUNKS;
-    const uint32_t lc = (lane % C::B_CHUNKS) ^ b_swz<C::B_CHUNKS>(krow);
-    b_off[u] = (n0 + (int)lc * 8 < N) ? (krow * (uint32_t)N + lc * 8) * 2u : OOB_OFFSET;
+    const uint32_t lc = (lane % C::B_CHUNKS) ^ b_swz<C::B_CHUNKS, C::ES>(krow);
+    b_off[u] = (n0 + (int)lc * C::CE < N) ? (krow * (uint32_t)N + lc * C::CE) * C::ES : OOB_OFFSET;
   }
 
   // Buffer ranges of slab kt (uniform: computed once per slab): A from
@@ -559,11 +597,11 @@ __global__ void __launch_bounds__(C::NT, 1) gemm_epilogue_kernel(GemmArgs p) {
     SlabSrd r;
     r.kbase = (uint32_t)kt * C::BK;
     const uint64_t a_start = (uint64_t)m0 * K + r.kbase, a_size = (uint64_t)M * K;
-    r.a = make_srd((const uint8_t*)p.A + (a_start < a_size ? a_start : 0) * 2,
-                   a_start < a_size && r.kbase < (uint32_t)K ? (a_size - a_start) * 2 : 0);
+    r.a = make_srd((const uint8_t*)p.A + (a_start < a_size ? a_start : 0) * C::ES,
+                   a_start < a_size && r.kbase < (uint32_t)K ? (a_size - a_start) * C::ES : 0);
     const uint64_t b_start = (uint64_t)r.kbase * N + n0, b_size = (uint64_t)K * N;
-    r.b = make_srd((const uint8_t*)p.B + (b_start < b_size ? b_start : 0) * 2,
-                   b_start < b_size ? (b_size - b_start) * 2 : 0);
+    r.b = make_srd((const uint8_t*)p.B + (b_start < b_size ? b_start : 0) * C::ES,
+                   b_start < b_size ? (b_size - b_start) * C::ES : 0);
     return r;
   };
   // Load q (0 .. PW-1) of this wave for a slab into ring buffer `stage`: the
@@ -584,9 +622,9 @@ __global__ void __launch_bounds__(C::NT, 1) gemm_epilogue_kernel(GemmArgs p) {
   const int lr = lane & 31;
   const int lh = lane >> 5;
 
-  // A fragment of block i, k-slice ks: row wm0 + 32i + lr, logical chunk
-  // 2ks + lh.  a_swz depends on row bits 1..4 only, i.e. on lr: block i adds
-  // 32 rows.
+  // 16-bit operands.  A fragment of block i, k-slice ks: row wm0 + 32i + lr,
+  // logical chunk 2ks + lh.  a_swz depends on row bits 1..4 only, i.e. on lr:
+  // block i adds 32 rows.
   uint32_t a_frag_off[C::NS];
 #pragma unroll
   for (int ks = 0; ks < C::NS; ++ks)
@@ -604,9 +642,30 @@ __global__ void __launch_bounds__(C::NT, 1) gemm_epilogue_kernel(GemmArgs p) {
     for (int j = 0; j < C::FN; ++j) {
       const uint32_t krow = 8 * (g16 >> 1) + 4 * t + (r16 >> 2);
       const uint32_t col = wn0 + 32 * j + 16 * (g16 & 1) + 4 * (r16 & 3);
-      b_frag_off[t][j] = C::A_BYTES + krow * C::B_ROW + (((col >> 3) ^ b_swz<C::B_CHUNKS>(krow)) << 4) +
+      b_frag_off[t][j] = C::A_BYTES + krow * C::B_ROW + (((col >> 3) ^ b_swz<C::B_CHUNKS, C::ES>(krow)) << 4) +
                          (col & 4) * 2;
     }
+  // fp8 operands.  A fragment of block i, k-slice ks (64 k-values): row
+  // wm0 + 32i + lr, bytes 32 lh .. +31 of the slice, i.e. logical chunks
+  // 4ks + 2lh and 4ks + 2lh + 1 (two 16-byte reads).
+  uint32_t a8_off[C::NS][2];
+#pragma unroll
+  for (int ks = 0; ks < C::NS; ++ks)
+#pragma unroll
+    for (int h = 0; h < 2; ++h)
+      a8_off[ks][h] = (uint32_t)(wm0 + lr) * C::A_ROW + (((4u * ks + 2u * lh + h) ^ a_swz<C::A_CHUNKS>(lr)) << 4);
+  // B fragment of block j, k-slice 0, read q (0..3): within 16-lane group g
+  // lane r addresses k-row 32(g/2) + 8q + r/2 and the 8 columns wn0 + 32j +
+  // 16(g%2) + 8(r%2) .. +7; the 8-bit transposing read then gives lane l the
+  // k-values 32(l/32) + 8q .. +7 of column wn0 + 32j + l%32.  The swizzle
+  // depends on r/2 only, so read q adds 8q k-rows and slice ks 64ks.
+  uint32_t b8_off[C::FN];
+#pragma unroll
+  for (int j = 0; j < C::FN; ++j) {
+    const uint32_t krow = 32 * (g16 >> 1) + (r16 >> 1);
+    const uint32_t col = wn0 + 32 * j + 16 * (g16 & 1) + 8 * (r16 & 1);
+    b8_off[j] = C::A_BYTES + krow * C::B_ROW + (((col >> 4) ^ b_swz<C::B_CHUNKS, C::ES>(krow)) << 4) + (col & 8);
+  }
 
   f32x16 acc[C::FM][C::FN];
 #pragma unroll
@@ -616,24 +675,33 @@ __global__ void __launch_bounds__(C::NT, 1) gemm_epilogue_kernel(GemmArgs p) {
 #pragma unroll
       for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.0f;
 
-  // Two fragment sets (k-slice being computed / k-slice being read).  A
-  // fragment i is one 16-byte read; B fragment j is two transposing 8-byte
-  // reads (lo: k 0..3, hi: k 4..7 of the lane's 8).  A k-slice is read as NRD
-  // "pieces".
-  constexpr int NMF = C::FM * C::FN;      // MFMAs per k-slice
-  constexpr int NRD = C::FM + 2 * C::FN;  // LDS read instructions per k-slice
-  u32x4 fa[2][C::FM];
-  u32x2 fb[2][C::FN][2];
+  // Two fragment sets (k-slice being computed / k-slice being read).
+  // 16-bit: A fragment i is one 16-byte read; B fragment j is two transposing
+  // reads (lo: k 0..3, hi: k 4..7 of the lane's 8).  fp8: A fragment i is two
+  // 16-byte reads, B fragment j four 8-bit transposing reads (k 8q .. 8q+7 of
+  // the lane's 32).  A k-slice is read as NRD "pieces", in the order of first
+  // use by the MFMAs (i outer, j inner): A0, then B0 .. B(FN-1), then A1 ..
+  // A(FM-1).
+  constexpr int NMF = C::FM * C::FN;  // MFMAs per k-slice
+  constexpr int RA = C::ES == 2 ? 1 : 2, RB = C::ES == 2 ? 2 : 4;  // reads per A / B fragment
+  constexpr int NRD = RA * C::FM + RB * C::FN;                       // LDS read instructions per k-slice
+  u32x4 fa[2][C::FM][RA];
+  u32x2 fb[2][C::FN][RB];
   auto read_piece = [&](int set, int stage, int ks, int piece) {
     const uint8_t* const st = smem + stage * C::STAGE_BYTES;
-    // order of first use by the MFMAs (i outer, j inner): A0, then the B
-    // halves j = 0..FN-1, then A1 .. A(FM-1)
-    if (piece == 0 || piece > 2 * C::FN) {
-      const int i = piece == 0 ? 0 : piece - 2 * C::FN;
-      fa[set][i] = *(const u32x4*)(st + a_frag_off[ks] + i * 32 * C::A_ROW);
+    if (piece < RA || piece >= RA + RB * C::FN) {
+      const int t = piece < RA ? piece : piece - RB * C::FN;
+      const int i = t / RA, h = t % RA;
+      if constexpr (C::ES == 2)
+        fa[set][i][0] = *(const u32x4*)(st + a_frag_off[ks] + i * 32 * C::A_ROW);
+      else
+        fa[set][i][h] = *(const u32x4*)(st + a8_off[ks][h] + i * 32 * C::A_ROW);
     } else {
-      const int j = (piece - 1) >> 1, t = (piece - 1) & 1;
-      fb[set][j][t] = lds_read_tr<DT>(st + b_frag_off[t][j] + ks * 16 * C::B_ROW);
+      const int j = (piece - RA) / RB, t = (piece - RA) % RB;
+      if constexpr (C::ES == 2)
+        fb[set][j][t] = lds_read_tr<DT>(st + b_frag_off[t][j] + ks * 16 * C::B_ROW);
+      else
+        fb[set][j][t] = lds_read_tr8(st + b8_off[j] + (ks * 64 + 8 * t) * C::B_ROW);
     }
   };
   auto read_slice = [&](int set, int stage, int ks) {
@@ -644,9 +712,20 @@ __global__ void __launch_bounds__(C::NT, 1) gemm_epilogue_kernel(GemmArgs p) {
 #pragma unroll
     for (int i = 0; i < C::FM; ++i)
 #pragma unroll
-      for (int j = 0; j < C::FN; ++j)
-        acc[i][j] = mfma32<DT>(u32x4{fb[set][j][0][0], fb[set][j][0][1], fb[set][j][1][0], fb[set][j][1][1]},
-                               fa[set][i], acc[i][j]);
+      for (int j = 0; j < C::FN; ++j) {
+        if constexpr (C::ES == 2) {
+          acc[i][j] = mfma32<DT>(u32x4{fb[set][j][0][0], fb[set][j][0][1], fb[set][j][1][0], fb[set][j][1][1]},
+                                 fa[set][i][0], acc[i][j]);
+        } else {
+          // B is the first operand (format FB), A the second (format FA)
+          constexpr int FA = (F8 - 1) & 1, FB = (F8 - 1) >> 1;
+          const u32x8 b8{fb[set][j][0][0], fb[set][j][0][1], fb[set][j][1][0], fb[set][j][1][1],
+                         fb[set][j][2][0], fb[set][j][2][1], fb[set][j][3][0], fb[set][j][3][1]};
+          const u32x8 a8{fa[set][i][0][0], fa[set][i][0][1], fa[set][i][0][2], fa[set][i][0][3],
+                         fa[set][i][RA - 1][0], fa[set][i][RA - 1][1], fa[set][i][RA - 1][2], fa[set][i][RA - 1][3]};
+          acc[i][j] = mfma32_f8<FB, FA>(b8, a8, acc[i][j]);
+        }
+      }
   };
   // Scheduling hint for one k-slice: alternate the MFMAs with the LDS reads
   // of the next k-slice, reads first, so neither the MFMA pipe nor the LDS
@@ -732,8 +811,8 @@ __global__ void __launch_bounds__(C::NT, 1) gemm_epilogue_kernel(GemmArgs p) {
   wait_vmcnt<0>();
   // the ring is free once every wave is past its last fragment read
   __syncthreads();
-  epilogue_store<DT, EPI, C::WM, C::WN>(p, acc, m0, n0, wm0, wn0, lane, smem + wave * C::EPI_STAGE, bias_lds,
-                                        (float*)(smem + C::RED_OFF));
+  epilogue_store<DT, EPI, C::WM, C::WN, F8 != 0>(p, acc, m0, n0, wm0, wn0, lane, smem + wave * C::EPI_STAGE,
+                                                 bias_lds, (float*)(smem + C::RED_OFF), scale);
 }
 
 }  // namespace egm

@@ -1,6 +1,9 @@
 // egm_kernels.hip - instantiates the fused GEMM + epilogue kernel for every
-// (epilogue, tile config) and the stand-alone epilogue kernel for one dtype.
-// Built twice: -DEGM_DTYPE=0 (fp16) and -DEGM_DTYPE=1 (bf16).
+// (epilogue, tile config) and the stand-alone epilogue kernels for one dtype.
+// Built once per 16-bit dtype (-DEGM_DTYPE=0 fp16, 1 bf16) and, with
+// -DEGM_F8=1..4, once per (fp8 format pair, 16-bit output dtype): the forward
+// epilogues only, on one-byte tiles with 128-deep k-slabs (the same bytes per
+// slab row as the 64-deep 16-bit slabs).
 #include "egm_epilogue.hpp"
 #include "egm_gemm.hpp"
 #include "egm_launch.hpp"
@@ -8,19 +11,25 @@
 #ifndef EGM_DTYPE
 #error "EGM_DTYPE must be 0 (fp16) or 1 (bf16)"
 #endif
+#ifndef EGM_F8
+#define EGM_F8 0
+#endif
 
 namespace egm {
 namespace {
 
 constexpr int DT = EGM_DTYPE;
+constexpr int F8 = EGM_F8;
+constexpr int ES = F8 == 0 ? 2 : 1;
 
 template <int EPI, int CFG>
 void launch_gemm(dim3 grid, hipStream_t s, const GemmArgs& a) {
   constexpr ConfigInfo ci = kConfigs[CFG];
-  using C = TileCfg<ci.bm, ci.bn, ci.stages, ci.wm, ci.wn, ci.bk>;
-  hipLaunchKernelGGL((gemm_epilogue_kernel<DT, EPI, C>), grid, dim3(C::NT), 0, s, a);
+  using C = TileCfg<ci.bm, ci.bn, ci.stages, ci.wm, ci.wn, ci.bk * (2 / ES), ES>;
+  hipLaunchKernelGGL((gemm_epilogue_kernel<DT, EPI, C, F8>), grid, dim3(C::NT), 0, s, a);
 }
 
+#if EGM_F8 == 0
 template <int EPI>
 void launch_epi(dim3 grid, hipStream_t s, const EpiArgs& a) {
   hipLaunchKernelGGL((epilogue_kernel<DT, EPI>), grid, dim3(256), 0, s, a);
@@ -29,6 +38,7 @@ void launch_epi(dim3 grid, hipStream_t s, const EpiArgs& a) {
 void launch_partials(dim3 grid, hipStream_t s, const void* D, int64_t M, int32_t N, int32_t layout, float* partial) {
   hipLaunchKernelGGL((axis_partials_kernel<DT>), grid, dim3(256), 0, s, D, M, N, layout, partial);
 }
+#endif
 
 template <int EPI>
 GemmLaunch gemm_row(int cfg) {
@@ -51,12 +61,15 @@ GemmLaunch gemm_table(int epi, int cfg) {
     case EPI_GELU: return gemm_row<EPI_GELU>(cfg);
     case EPI_RELU_AUX: return gemm_row<EPI_RELU_AUX>(cfg);
     case EPI_RESID: return gemm_row<EPI_RESID>(cfg);
+#if EGM_F8 == 0
     case EPI_DRELU: return gemm_row<EPI_DRELU>(cfg);
     case EPI_DRELU_BGRAD: return gemm_row<EPI_DRELU_BGRAD>(cfg);
+#endif
     default: return nullptr;
   }
 }
 
+#if EGM_F8 == 0
 EpiLaunch epi_table(int epi) {
   switch (epi) {
     case EPI_BIAS: return &launch_epi<EPI_BIAS>;
@@ -68,10 +81,15 @@ EpiLaunch epi_table(int epi) {
     default: return nullptr;
   }
 }
+#endif
 
 }  // namespace
 
-#if EGM_DTYPE == 0
+#if EGM_F8 != 0
+#define EGM_CAT3(a, b, c) a##b##_##c
+#define EGM_FP8_LAUNCHER(dt, f8) EGM_CAT3(gemm_launcher_fp8_, dt, f8)
+GemmLaunch EGM_FP8_LAUNCHER(EGM_DTYPE, EGM_F8)(int epi, int cfg) { return gemm_table(epi, cfg); }
+#elif EGM_DTYPE == 0
 GemmLaunch gemm_launcher_f16(int epi, int cfg) { return gemm_table(epi, cfg); }
 EpiLaunch epi_launcher_f16(int epi) { return epi_table(epi); }
 PartialsLaunch partials_launcher_f16() { return &launch_partials; }

@@ -51,6 +51,27 @@ PartialsLaunch partials_launcher_bf16();
 void launch_bias_grad_finish(dim3 grid, hipStream_t stream, const float* partial, int64_t chunks, int64_t len,
                              float* out);
 
+// fp8 operands (defined in egm_kernels.hip built with -DEGM_F8): one table per
+// (output dtype 0 fp16 / 1 bf16, format pair f8 = 1 + fa + 2 fb); forward
+// epilogues only (nullptr otherwise)
+GemmLaunch gemm_launcher_fp8_0_1(int epi, int cfg);
+GemmLaunch gemm_launcher_fp8_0_2(int epi, int cfg);
+GemmLaunch gemm_launcher_fp8_0_3(int epi, int cfg);
+GemmLaunch gemm_launcher_fp8_0_4(int epi, int cfg);
+GemmLaunch gemm_launcher_fp8_1_1(int epi, int cfg);
+GemmLaunch gemm_launcher_fp8_1_2(int epi, int cfg);
+GemmLaunch gemm_launcher_fp8_1_3(int epi, int cfg);
+GemmLaunch gemm_launcher_fp8_1_4(int epi, int cfg);
+
+inline GemmLaunch gemm_launcher_fp8(int dt, int f8, int epi, int cfg) {
+  using Table = GemmLaunch (*)(int, int);
+  static constexpr Table tables[2][4] = {
+      {&gemm_launcher_fp8_0_1, &gemm_launcher_fp8_0_2, &gemm_launcher_fp8_0_3, &gemm_launcher_fp8_0_4},
+      {&gemm_launcher_fp8_1_1, &gemm_launcher_fp8_1_2, &gemm_launcher_fp8_1_3, &gemm_launcher_fp8_1_4}};
+  if ((dt != DT_F16 && dt != DT_BF16) || f8 < 1 || f8 > 4) return nullptr;
+  return tables[dt == DT_F16 ? 0 : 1][f8 - 1](epi, cfg);
+}
+
 inline GemmLaunch gemm_launcher(int dt, int epi, int cfg) {
   return dt == DT_F16 ? gemm_launcher_f16(epi, cfg) : gemm_launcher_bf16(epi, cfg);
 }

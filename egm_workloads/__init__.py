@@ -324,8 +324,9 @@ BACKWARD_WORKLOADS = {
 }
 
 
-#: fp8 operands on the square workload: A ~ N(0,1), B ~ N(0,1/K), both
-#: quantised per tensor to E4M3, bias (1,n) ~ N(0,1) and output in bf16
+#: fp8 operands on the square workload, with its draws: A, B ~ N(0,1)/sqrt(K),
+#: each quantised per tensor to E4M3 (the scale absorbs the 1/sqrt(K)), bias
+#: (1,n) ~ N(0,1) and output in bf16
 FP8_WORKLOADS = {
     "gemm_relu_aux_bias_fp8e4m3_8192x8192x8192": Workload(
         "gemm_relu_aux_bias_fp8e4m3_8192x8192x8192", 8192, 8192, 8192, BF16, ("RELU_AUX_BIAS",), "col",
@@ -335,7 +336,8 @@ FP8_WORKLOADS = {
 
 def fp8_workload_operands(name: str, seed: int = 0) -> Fp8Operands:
     w = FP8_WORKLOADS[name]
-    return fp8_operands(w.m, w.n, w.k, E4M3, E4M3, w.dtype, seed, bias_layout=w.bias_layout)
+    return fp8_operands(w.m, w.n, w.k, E4M3, E4M3, w.dtype, seed, a_std=1.0 / math.sqrt(w.k),
+                        b_std=1.0 / math.sqrt(w.k), bias_layout=w.bias_layout)
 
 
 def mask_bits(m: int, n: int, seed: int, tensor_index: int) -> np.ndarray:

@@ -2,9 +2,10 @@
  * egm.h - fused dense GEMM + epilogue for AMD Instinct MI355X (gfx950).
  *
  *   D = epilogue(A . B),  A [m,k], B [k,n], D [m,n], all row-major, one 16-bit
- *   dtype (fp16 or bf16) for A, B, bias, residual and D; products accumulate in
- *   fp32 and the epilogue runs on the fp32 accumulators before the single
- *   round-to-nearest-even conversion to the output dtype.
+ *   dtype (fp16 or bf16) for A, B, bias, residual and D (egm_plan_fp8: fp8
+ *   A and B with per-tensor scales, 16-bit bias, residual and D); products
+ *   accumulate in fp32 and the epilogue runs on the fp32 accumulators before
+ *   the single round-to-nearest-even conversion to the output dtype.
  *
  * Pages this interface follows (cited by title):
  *   [bias-fusion] "通过 nvmath-python 的 cuBLASLt 绑定，在 PyTorch 中实现偏差融合以提升推理性能"
@@ -49,15 +50,15 @@
 extern "C" {
 #endif
 
-#define EGM_ABI_VERSION 2
+#define EGM_ABI_VERSION 3
 
 typedef enum egm_status_t {
   EGM_OK = 0,
   EGM_ERR_INVALID_VALUE = 1, /* NULL pointer, unknown enum, bad option */
   EGM_ERR_NOT_SUPPORTED = 2, /* valid request outside what v1 implements */
-  EGM_ERR_SHAPE = 3,         /* negative dims, n or k not a multiple of 8, too large */
-  EGM_ERR_DTYPE = 4,         /* dtype other than fp16 / bf16 */
-  EGM_ERR_ALIGNMENT = 5,     /* device pointer not 16-byte aligned */
+  EGM_ERR_SHAPE = 3,         /* negative dims, n or k not a multiple of 8 (16 for fp8), too large */
+  EGM_ERR_DTYPE = 4,         /* dtype other than fp16 / bf16, or an unknown fp8 format */
+  EGM_ERR_ALIGNMENT = 5,     /* device pointer not 16-byte aligned (fp8 scales: 4-byte) */
   EGM_ERR_INVALID_PLAN = 6,  /* NULL, freed or foreign plan handle */
   EGM_ERR_HIP = 7,           /* the HIP runtime reported an error at launch */
   EGM_ERR_NO_MEMORY = 8,     /* host allocation of the plan failed */
@@ -68,6 +69,12 @@ typedef enum egm_dtype_t {
   EGM_F16 = 0,  /* IEEE binary16 */
   EGM_BF16 = 1  /* bfloat16 (upper half of binary32) */
 } egm_dtype_t;
+
+/* fp8 operand formats of egm_plan_fp8 (the OCP 8-bit floats gfx950 implements). */
+typedef enum egm_fp8_format_t {
+  EGM_E4M3 = 0, /* 4 exponent bits (bias 7), 3 mantissa bits; no infinities; largest 448 */
+  EGM_E5M2 = 1  /* 5 exponent bits (bias 15), 2 mantissa bits; IEEE inf / NaN; largest 57344 */
+} egm_fp8_format_t;
 
 /*
  * Epilogues.  Z = A.B + bias (fp32, bias broadcast per egm_bias_layout_t).
@@ -159,6 +166,32 @@ typedef struct egm_plan_s* egm_plan_t;
 egm_status_t egm_plan(egm_plan_t* out, int64_t m, int64_t n, int64_t k, egm_dtype_t dtype,
                       egm_epilog_t epilog, const egm_epilog_inputs_t* in,
                       const egm_plan_options_t* opt);
+
+/*
+ * egm_plan_fp8 - as egm_plan, with fp8 operands and per-tensor scales
+ * ([bias-fusion] body: the data-type item of the checklist lists FP8 among the
+ * supported types; the closing paragraph names FP8 among the features to come).
+ *   D = epilogue(scale_a * scale_b * (A8 . B8) + bias)
+ *   a_format, b_format  egm_fp8_format_t of A [m,k] and B [k,n] (one byte per
+ *           element, row-major); any pairing.
+ *   out_dtype  EGM_F16 or EGM_BF16: the type of the bias, the residual and D
+ *           (the page's same-type rule is read as covering the two operands).
+ *   scale_a, scale_b  device pointers to one fp32 each (4-byte aligned), the
+ *           dequantisation scales (A = scale_a * A8); read by every execute at
+ *           its start, in stream order, so a kernel earlier on the stream may
+ *           write them; NULL means 1.  They must stay valid for every execute.
+ *   m, n, k as egm_plan, but n and k multiples of 16 (16-byte operand rows).
+ *   epilog  DEFAULT .. BIAS_RESIDUAL; the backward epilogues return
+ *           EGM_ERR_NOT_SUPPORTED.
+ * Products of two fp8 values are exact in fp32 and accumulate in fp32; the
+ * scale is one fp32 multiply of the accumulator before the bias.  execute,
+ * free, describe and the workspace query work as for egm_plan's plans.
+ * No device work and no HIP call.
+ */
+egm_status_t egm_plan_fp8(egm_plan_t* out, int64_t m, int64_t n, int64_t k, egm_fp8_format_t a_format,
+                          egm_fp8_format_t b_format, egm_dtype_t out_dtype, const float* scale_a,
+                          const float* scale_b, egm_epilog_t epilog, const egm_epilog_inputs_t* in,
+                          const egm_plan_options_t* opt);
 
 /*
  * egm_execute - enqueue the plan on a HIP stream (asynchronous).

@@ -126,3 +126,35 @@ def compare_bias_grad(got, want, bound, *, d_ref=None, dtype=None, layout=None):
         raise AssertionError(f"{int(bad.sum())} of {err.size} bias-gradient values exceed the bound; first at {i}: "
                              f"got={got[i]!r} want={want[i]!r} bound={b[i]:.3g}")
     return {"max_abs_err": float(err.max()) if err.size else 0.0}
+
+
+def fp8_to_device(bits, fmt):
+    import torch
+    t = torch.from_numpy(np.ascontiguousarray(bits, dtype=np.uint8)).cuda()
+    return t.view(torch.float8_e4m3fn if fmt == "e4m3" else torch.float8_e5m2)
+
+
+def scale_tensor(value):
+    import torch
+    return torch.tensor([float(np.float32(value))], dtype=torch.float32, device="cuda")
+
+
+def run_fp8(ops, epilog, *, fused=True, force_config=-1, null_scales=False):
+    """Run one epilog on Fp8Operands through the binding; returns (D bits, mask or None)."""
+    import torch
+    import dense_gemm_epilogue_fp16_amd as egm
+    a, b = fp8_to_device(ops.a, ops.a_fmt), fp8_to_device(ops.b, ops.b_fmt)
+    sa = None if null_scales else scale_tensor(ops.scale_a)
+    sb = None if null_scales else scale_tensor(ops.scale_b)
+    ins = {}
+    if epilog != "DEFAULT":
+        ins["bias"] = bias_tensor(ops.bias, ops.bias_layout, ops.out_dtype)
+    if epilog == "BIAS_RESIDUAL":
+        ins["residual"] = to_device(ops.residual, ops.out_dtype)
+    with egm.Matmul(a, b, scale_a=sa, scale_b=sb, out_dtype=torch_dtype(ops.out_dtype)) as mm:
+        mm.plan(epilog=epilog, epilog_inputs=ins, fused=fused, force_config=force_config)
+        out = mm.execute()
+        torch.cuda.synchronize()
+    if isinstance(out, tuple):
+        return to_host_bits(out[0]), out[1].cpu().numpy()
+    return to_host_bits(out), None

@@ -24,7 +24,7 @@ def declared_functions():
 
 def test_every_declared_symbol_is_exported():
     names = declared_functions()
-    assert len(names) == 10
+    assert len(names) == 11
     assert sorted(egm.EXPORTS) == names
     lib = ctypes.CDLL(egm.LIB_PATH)
     for name in names:
@@ -32,7 +32,7 @@ def test_every_declared_symbol_is_exported():
 
 
 def test_abi_version_and_status_strings():
-    assert egm.egm_abi_version() == 2
+    assert egm.egm_abi_version() == 3
     for s in range(10):
         assert egm.status_string(s).startswith("EGM_")
     assert "unknown" in egm.status_string(12345)
@@ -240,3 +240,45 @@ def test_backward_workspace_and_execute_validation():
         assert egm.egm_execute(h, FAKE, FAKE, FAKE, 0, raw_status=True) == egm.EGM_ERR_INVALID_VALUE
     finally:
         egm.egm_free(h)
+
+
+def test_fp8_plan_validation_and_describe():
+    F8 = egm.EGM_E4M3, egm.EGM_E5M2
+    E4, E5 = F8
+    h = egm.egm_plan_fp8(256, 512, 1024, E4, E5, BF16, FAKE, FAKE + 4, E["RELU_AUX_BIAS"], FAKE, COL)
+    try:
+        d = egm.egm_plan_describe(h)
+        assert "operands=e4m3xe5m2" in d and "dtype=bf16" in d and "mfma=32x32x64" in d and "kslab=128" in d
+        assert egm.egm_plan_workspace_bytes(h) == 0
+    finally:
+        egm.egm_free(h)
+    # NULL scales mean 1; every format pairing plans
+    for fa in F8:
+        for fb in F8:
+            st, h = egm.egm_plan_fp8(64, 64, 64, fa, fb, F16, 0, 0, E["DEFAULT"], raw_status=True)
+            assert st == egm.EGM_OK
+            egm.egm_free(h)
+    bad = [
+        (dict(a_format=7), egm.EGM_ERR_DTYPE),
+        (dict(b_format=-1), egm.EGM_ERR_DTYPE),
+        (dict(out_dtype=5), egm.EGM_ERR_DTYPE),
+        (dict(n=72), egm.EGM_ERR_SHAPE),   # a multiple of 8 but not of 16: half a 16-byte fp8 row
+        (dict(k=24), egm.EGM_ERR_SHAPE),
+        (dict(epilog=E["DRELU"]), egm.EGM_ERR_NOT_SUPPORTED),
+        (dict(epilog=E["DRELU_BGRAD"]), egm.EGM_ERR_NOT_SUPPORTED),
+        (dict(scale_a=FAKE + 2), egm.EGM_ERR_ALIGNMENT),
+        (dict(scale_b=FAKE + 1), egm.EGM_ERR_ALIGNMENT),
+        (dict(bias=FAKE + 8), egm.EGM_ERR_ALIGNMENT),
+        (dict(bias=0), egm.EGM_ERR_INVALID_VALUE),
+    ]
+    for kw, want in bad:
+        args = dict(m=64, n=64, k=64, a_format=E4, b_format=E4, out_dtype=BF16, scale_a=FAKE, scale_b=FAKE,
+                    epilog=E["BIAS"], bias=FAKE, bias_layout=COL)
+        args.update(kw)
+        if args["epilog"] in (E["DRELU"], E["DRELU_BGRAD"]):
+            args.update(bias=0, bias_layout=0)
+        st, h = egm.egm_plan_fp8(args.pop("m"), args.pop("n"), args.pop("k"), args.pop("a_format"),
+                                 args.pop("b_format"), args.pop("out_dtype"), args.pop("scale_a"),
+                                 args.pop("scale_b"), args.pop("epilog"), args.pop("bias"),
+                                 args.pop("bias_layout"), raw_status=True)
+        assert st == want and h is None, (kw, st)
