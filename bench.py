@@ -33,6 +33,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 PEAK_TFLOPS = 2500.0      # MI355X dense fp16 / bf16 MFMA (published)
+PEAK_TFLOPS_FP8 = 5000.0  # MI355X dense fp8 MFMA (published)
 PEAK_HBM_GBS = 8000.0     # MI355X HBM3E (published)
 DEFAULT_WORKLOAD = "gemm_relu_bias_fp16_65536x16384x16384"
 # device code of the fused kernel and the config table that picks its instance
@@ -60,11 +61,12 @@ def traffic_from_profile(workload: str):
     return t.get("bytes_per_launch")
 
 
-def algorithmic_bytes(m, n, k, epilog, bias_layout):
+def algorithmic_bytes(m, n, k, epilog, bias_layout, operand_bytes=2):
     """Fused path: read A, B, bias (+R) once, write D (+mask) once; the
     backward epilogues read the mask instead of a bias and (BGRAD) write the
-    fp32 bias gradient."""
-    b = 2 * (m * k + k * n + m * n)
+    fp32 bias gradient.  operand_bytes: 2 (fp16/bf16) or 1 (fp8 A and B; the
+    bias, residual and D stay 16-bit)."""
+    b = operand_bytes * (m * k + k * n) + 2 * m * n
     if epilog in ("DRELU", "DRELU_BGRAD"):
         b += m * n // 8
         if epilog == "DRELU_BGRAD":
@@ -130,9 +132,28 @@ def main():
 
     t_setup = time.time()
     name = args.workload
-    wl = W.WORKLOADS[name] if name in W.WORKLOADS else W.BACKWARD_WORKLOADS[name]
+    wl = {**W.WORKLOADS, **W.BACKWARD_WORKLOADS, **W.FP8_WORKLOADS}[name]
+    fp8 = name in W.FP8_WORKLOADS
     keep = []
-    if name in W.BACKWARD_WORKLOADS:
+    mm_kw = {}  # Matmul constructor arguments (fp8: scales and output dtype)
+    if fp8:
+        ops = W.fp8_workload_operands(name)
+        f8t = torch.float8_e4m3fn if ops.a_fmt == "e4m3" else torch.float8_e5m2
+        a = torch.from_numpy(ops.a).to(dev).view(f8t)
+        b = torch.from_numpy(ops.b).to(dev).view(f8t)
+        sa = torch.tensor([float(ops.scale_a)], dtype=torch.float32, device=dev)
+        sb = torch.tensor([float(ops.scale_b)], dtype=torch.float32, device=dev)
+        bias = to_dev(ops.bias, ops.out_dtype, (ops.m, 1) if ops.bias_layout == "row" else (1, ops.n))
+        d = torch.empty((ops.m, ops.n), dtype=bias.dtype, device=dev)
+        epilog = wl.epilogs[-1]
+        out = dict(out=d)
+        if epilog == "RELU_AUX_BIAS":
+            out["aux"] = torch.empty((ops.m, ops.n // 8), dtype=torch.uint8, device=dev)
+        specs = [((a, b), epilog, {"bias": bias}, out, (ops.m, ops.n, ops.k), ops.bias_layout)]
+        mm_kw = dict(scale_a=sa, scale_b=sb, out_dtype=bias.dtype)
+        keep += [a, b, bias, d, sa, sb]
+        host_ops = ops
+    elif name in W.BACKWARD_WORKLOADS:
         ops, mask = W.backward_operands(name)
         a = to_dev(ops.a, ops.dtype, (ops.m, ops.k))
         b = to_dev(ops.b, ops.dtype, (ops.k, ops.n))
@@ -184,7 +205,7 @@ def main():
     def make(fused):
         res = []
         for (aa, bb), ep, ins, out, (m, n, k), layout in specs:
-            mm = egm.Matmul(aa, bb)
+            mm = egm.Matmul(aa, bb, **mm_kw)
             mm.plan(ep, ins, fused=fused)
             res.append((mm, out, (m, n, k), ep, layout))
         return res
@@ -248,11 +269,14 @@ def main():
     tb = traffic_from_profile(name)
 
     value = flops / (fused_ms * 1e-3) / 1e12
-    alg = sum(algorithmic_bytes(m, n, k, ep, lay) for _, _, (m, n, k), ep, lay in fused_plans)
+    peak = PEAK_TFLOPS_FP8 if fp8 else PEAK_TFLOPS
+    ob = 1 if fp8 else 2
+    alg = sum(algorithmic_bytes(m, n, k, ep, lay, ob) for _, _, (m, n, k), ep, lay in fused_plans)
     # P written and read back (+ D read again for the two-kernel bias gradient)
     extra = sum((6 if ep == "DRELU_BGRAD" else 4) * m * n for _, _, (m, n, k), ep, _ in fused_plans)
     result = {
-        "metric": "fused GEMM+epilogue TFLOP/s (fp16/bf16 MFMA, fp32 accumulate)",
+        "metric": ("fused GEMM+epilogue TFLOP/s (fp8 MFMA, fp32 accumulate)" if fp8 else
+                   "fused GEMM+epilogue TFLOP/s (fp16/bf16 MFMA, fp32 accumulate)"),
         "value": round(value, 2),
         "unit": "TFLOP/s",
         "n_gpus": 1,
@@ -262,27 +286,29 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": wl.dtype,
+        "dtype": f"fp8_{ops.a_fmt}" if fp8 else wl.dtype,
         "data": "synthetic (seeded normal operands, resident in HBM)",
         "config": {"workload": name, "m": wl.m, "n": wl.n, "k": wl.k, "epilog": "+".join(wl.epilogs),
                    "bias": "(m,1)" if wl.bias_layout == "row" else "(1,n)", "accumulate": "fp32",
+                   **({"operands": f"{ops.a_fmt} x {ops.b_fmt}, per-tensor scales", "out": wl.dtype} if fp8 else {}),
                    "plan": fused_plans[0][0].describe()},
-        "pct_of_mfma_peak": round(100.0 * value / PEAK_TFLOPS, 2),
+        "pct_of_mfma_peak": round(100.0 * value / peak, 2),
         "unfused_ms_per_step": round(unfused_ms, 4),
         "speedup_vs_unfused": round(unfused_ms / fused_cmp_ms, 4),
         "bytes_fused_algorithmic": alg,
         "bytes_saved_by_fusion": extra,
-        "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_TFLOPS, "unit": "TFLOP/s",
-                     "frac": round(achieved / PEAK_TFLOPS, 4), "traffic": tb,
+        "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": peak, "unit": "TFLOP/s",
+                     "frac": round(achieved / peak, 4), "traffic": tb,
                      "kernel": f"gemm_epilogue_kernel {dm}x{dn}x{dk} {dom[3]}",
                      "avg_launch_ms": round(dom_ms, 4), "flops_per_launch": dom_flops,
-                     "algorithmic_bytes_per_launch": algorithmic_bytes(dm, dn, dk, dom[3], dom[4])},
+                     "algorithmic_bytes_per_launch": algorithmic_bytes(dm, dn, dk, dom[3], dom[4], ob)},
         "setup_s": round(setup_s, 1),
         "timed_wall_s": round(fused_wall, 3),
     }
 
     if args.torch_context:
-        result["torch_context"] = torch_context(specs, timed, steps, warmup, flops)
+        result["torch_context"] = (torch_context_fp8(specs, mm_kw, timed, steps, warmup, flops) if fp8 else
+                                   torch_context(specs, timed, steps, warmup, flops))
 
     if args.cold:
         result["cold_cache"] = cold_and_latency(lambda: step(fused_plans), lambda: step(unfused_plans),
@@ -337,6 +363,38 @@ def torch_context(specs, timed, steps, warmup, flops):
         res[label] = round(ms, 5)
     res["matmul_tflops"] = round(flops / (res["matmul_ms"] * 1e-3) / 1e12, 2)
     res["note"] = "torch.matmul is the vendor GEMM (hipBLASLt); the second figure is the eager op sequence"
+    return res
+
+
+def torch_context_fp8(specs, mm_kw, timed, steps, warmup, flops):
+    """torch._scaled_mm (the vendor fp8 GEMM, per-tensor scales, bf16 out) on
+    the same operands, alone and with torch's eager bias + activation: context,
+    not a code path of the library."""
+    import torch
+    (aa, bb), ep, ins, out, _, _ = specs[0]
+    bt = bb.t().contiguous().t()  # the vendor call wants B column-major
+    sa, sb = mm_kw["scale_a"], mm_kw["scale_b"]
+
+    def run(with_epilogue):
+        y = torch._scaled_mm(aa, bt, scale_a=sa, scale_b=sb, out_dtype=mm_kw["out_dtype"])
+        if with_epilogue:
+            y = y + ins["bias"]
+            if ep in ("RELU_BIAS", "RELU_AUX_BIAS"):
+                y = torch.relu(y)
+                if ep == "RELU_AUX_BIAS":
+                    (y > 0)
+        return y
+
+    res = {}
+    try:
+        for label, w in (("matmul_ms", False), ("matmul_bias_act_ms", True)):
+            ms, _ = _timed_callables([lambda w=w: run(w)], timed, steps, warmup)
+            res[label] = round(ms, 5)
+        res["matmul_tflops"] = round(flops / (res["matmul_ms"] * 1e-3) / 1e12, 2)
+        res["note"] = ("torch._scaled_mm is the vendor fp8 GEMM (hipBLASLt); the second figure adds torch's eager "
+                       "bias and activation")
+    except Exception as exc:  # the vendor call may be missing for this type on this build
+        res = {"error": f"{type(exc).__name__}: {exc}"[:300]}
     return res
 
 
@@ -535,6 +593,43 @@ def _cpu_baseline_backward(name, ops, keep, target_s, cores):
             "parity_tol": eo.TOLERANCE[ops.dtype]}
 
 
+def _cpu_baseline_fp8(name, ops, keep, target_s, cores):
+    """The fp8 oracle on a row sample; checks the GPU's D on those rows."""
+    import numpy as np
+    import torch
+
+    import egm_workloads as W
+    from oracle import egm_oracle as eo
+    epilog = W.FP8_WORKLOADS[name].epilogs[-1]
+
+    def ref(rows):
+        return eo.reference_fp8(ops.a, ops.b, ops.a_fmt, ops.b_fmt, ops.scale_a, ops.scale_b, ops.out_dtype, epilog,
+                                ops.bias, ops.bias_layout, rows=rows)
+
+    times = {}
+    for cnt in (64, 192):
+        rows = W.sample_rows(ops.m, min(ops.m, cnt), seed=2)
+        t0 = time.perf_counter()
+        ref(rows)
+        times[cnt] = time.perf_counter() - t0
+    per_row = max((times[192] - times[64]) / 128.0, 1e-6)
+    fixed = max(times[64] - 64 * per_row, 0.0)
+    count = int(min(ops.m, 32768, max(64, (target_s - fixed) / per_row)))
+    rows = W.sample_rows(ops.m, count, seed=2)
+    t0 = time.perf_counter()
+    y, _, _ = ref(rows)
+    secs = time.perf_counter() - t0
+    gpu_d = keep[3]
+    sel = gpu_d.index_select(0, torch.from_numpy(rows).to(gpu_d.device)).cpu()
+    d = eo.widen(sel.view(torch.int16).numpy().view(np.uint16), ops.out_dtype)
+    flops = 2.0 * len(rows) * ops.n * ops.k
+    return {"value": round(flops / secs / 1e12, 4), "unit": "TFLOP/s", "cores": int(cores), "kind": "oracle",
+            "sample": f"{len(rows)} of {ops.m} output rows x all {ops.n} columns (k={ops.k}), {epilog} on "
+                      f"{ops.a_fmt} x {ops.b_fmt} operands, fp64 numpy oracle; {secs:.1f} s",
+            "seconds": round(secs, 2), "parity_max_abs_err": float(np.abs(d - y).max()),
+            "parity_tol": eo.TOLERANCE[ops.out_dtype]}
+
+
 def cpu_baseline(name, ops, keep, target_s):
     """The CPU fp64 oracle on a row sample of the same workload; also checks
     the GPU's D on those rows (a bench-time parity spot check)."""
@@ -551,6 +646,8 @@ def cpu_baseline(name, ops, keep, target_s):
         cores = len(os.sched_getaffinity(0))
     if ops is not None and "mask" in ops.meta:  # backward: the DRELU part on a row sample
         return _cpu_baseline_backward(name, ops, keep, target_s, cores)
+    if name in W.FP8_WORKLOADS:
+        return _cpu_baseline_fp8(name, ops, keep, target_s, cores)
     if ops is None:  # FFN chain: time the up-projection oracle on a row sample
         f = W.ffn_operands()
         a, b, bias, layout, epilog, dtype = f.x, f.w1, f.b1, "col", "GELU_BIAS", "bf16"

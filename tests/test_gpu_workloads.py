@@ -94,6 +94,21 @@ def test_backward_workload(fused):
 
 @pytest.mark.slow
 @pytest.mark.parametrize("fused", [True, False])
+def test_fp8_workload(fused):
+    """The E4M3 8192^3 RELU_AUX_BIAS workload at full size, in the launch
+    configuration bench.py times: every output and every mask bit."""
+    from parity import run_fp8
+    name = "gemm_relu_aux_bias_fp8e4m3_8192x8192x8192"
+    ops = W.fp8_workload_operands(name)
+    d, mask = run_fp8(ops, "RELU_AUX_BIAS", fused=fused)
+    y, z, mref = eo.reference_fp8(ops.a, ops.b, ops.a_fmt, ops.b_fmt, ops.scale_a, ops.scale_b, ops.out_dtype,
+                                  "RELU_AUX_BIAS", ops.bias, ops.bias_layout)
+    st = compare(d, y, ops.out_dtype, z=z, mask=mask, mask_ref=mref, unfused=not fused)
+    print(f"[{name} fused={fused}] {st}", flush=True)
+
+
+@pytest.mark.slow
+@pytest.mark.parametrize("fused", [True, False])
 def test_largest_sampled_rows(fused):
     import torch
     import dense_gemm_epilogue_fp16_amd as egm
