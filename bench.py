@@ -99,6 +99,9 @@ def main():
     ap.add_argument("--torch-context", action="store_true",
                     help="also time torch.matmul (the vendor GEMM, no epilogue) and torch's eager "
                          "matmul + bias + activation on the same operands, with the same warm-up and step counts")
+    ap.add_argument("--launch-amortisation", type=int, default=0, metavar="N",
+                    help="also time N problems of the workload's shape (own A and D, shared B) as N separate "
+                         "executes, as one replayed HIP graph of those executes, and as one strided-batch launch")
     ap.add_argument("--sustain", type=float, default=0.0,
                     help="instead of the bench line: run the fused step back to back for this many seconds and "
                          "print one JSON line per second with its throughput and the board power and clocks "
@@ -310,6 +313,9 @@ def main():
         result["torch_context"] = (torch_context_fp8(specs, mm_kw, timed, steps, warmup, flops) if fp8 else
                                    torch_context(specs, timed, steps, warmup, flops))
 
+    if args.launch_amortisation:
+        result["launch_amortisation"] = launch_amortisation(specs, mm_kw, args.launch_amortisation, dev)
+
     if args.cold:
         result["cold_cache"] = cold_and_latency(lambda: step(fused_plans), lambda: step(unfused_plans),
                                                 flops, alg, dev, stream)
@@ -395,6 +401,74 @@ def torch_context_fp8(specs, mm_kw, timed, steps, warmup, flops):
                        "bias and activation")
     except Exception as exc:  # the vendor call may be missing for this type on this build
         res = {"error": f"{type(exc).__name__}: {exc}"[:300]}
+    return res
+
+
+def launch_amortisation(specs, mm_kw, nprob, dev, target_ms=400.0):
+    """Per-GEMM time of nprob problems of the workload's shape (own A and D,
+    shared B and bias): nprob executes launched one by one, the same executes
+    captured once in a HIP graph and replayed, and one strided-batch execute;
+    plus the host time of one execute call."""
+    import torch
+
+    import dense_gemm_epilogue_fp16_amd as egm
+    if len(specs) != 1 or specs[0][1] == "DRELU_BGRAD":
+        return {"error": "one forward GEMM per step only"}
+    (aa, bb), ep, ins, out, (m, n, k), _ = specs[0]
+    mm = egm.Matmul(aa, bb, **mm_kw)
+    mm.plan(ep, ins)
+    a_b = aa.unsqueeze(0).expand(nprob, m, k).contiguous()
+    d_b = torch.empty((nprob, m, n), dtype=mm.dtype, device=dev)
+    aux_b = torch.empty((nprob, m, n // 8), dtype=torch.uint8, device=dev) if ep == "RELU_AUX_BIAS" else None
+
+    def eager():
+        for i in range(nprob):
+            mm.execute(a=a_b[i], out=d_b[i], aux=aux_b[i] if aux_b is not None else None)
+
+    def batched():
+        mm.execute_batched(a_b, bb, out=d_b, aux=aux_b)
+
+    side = torch.cuda.Stream(dev)
+    side.wait_stream(torch.cuda.current_stream(dev))
+    with torch.cuda.stream(side):
+        eager()
+    torch.cuda.current_stream(dev).wait_stream(side)
+    torch.cuda.synchronize(dev)
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        eager()
+
+    def time_it(fn):
+        fn()
+        torch.cuda.synchronize(dev)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        fn()
+        e1.record()
+        torch.cuda.synchronize(dev)
+        once = max(e0.elapsed_time(e1), 1e-3)
+        reps = max(3, int(target_ms / once))
+        e0.record()
+        for _ in range(reps):
+            fn()
+        e1.record()
+        torch.cuda.synchronize(dev)
+        return e0.elapsed_time(e1) / reps * 1000.0 / nprob  # us per GEMM
+
+    res = {"problems": nprob, "shape": [m, n, k], "epilog": ep,
+           "eager_us_per_gemm": round(time_it(eager), 3),
+           "graph_us_per_gemm": round(time_it(g.replay), 3),
+           "strided_us_per_gemm": round(time_it(batched), 3)}
+    torch.cuda.synchronize(dev)
+    t0 = time.perf_counter()
+    eager()
+    res["host_us_per_execute_call"] = round((time.perf_counter() - t0) * 1e6 / nprob, 2)
+    torch.cuda.synchronize(dev)
+    res["flops_per_gemm"] = 2 * m * n * k
+    res["note"] = ("eager = one launch per execute; graph = the same executes captured in one HIP graph; strided = "
+                   "egm_execute_strided, one launch for all problems")
+    mm.free()
+    del g
     return res
 
 

@@ -63,7 +63,8 @@ EGM_BIAS_COL = 2  # shape (1, n)
 
 #: every symbol include/egm.h declares
 EXPORTS = (
-    "egm_plan", "egm_plan_fp8", "egm_execute", "egm_free", "egm_plan_workspace_bytes", "egm_plan_describe",
+    "egm_plan", "egm_plan_fp8", "egm_execute", "egm_execute_strided", "egm_free", "egm_plan_workspace_bytes",
+    "egm_plan_describe",
     "egm_plan_config", "egm_num_configs", "egm_config_describe", "egm_status_string", "egm_abi_version",
 )
 
@@ -89,7 +90,7 @@ class PlanOptions(ctypes.Structure):
 def _load() -> ctypes.CDLL:
     if not os.path.exists(LIB_PATH):
         raise ImportError(
-            f"{LIB_PATH} is not built: run `python -m dense_gemm_epilogue_fp16_amd.build` "
+            f"{LIB_PATH} is not built: run `python dense_gemm_epilogue_fp16_amd/build.py` "
             "(or __graft_entry__.build()); there is no fallback path")
     # torch first, so the library binds to the HIP runtime torch already loaded
     try:
@@ -106,6 +107,8 @@ def _load() -> ctypes.CDLL:
     lib.egm_plan_fp8.restype = i32
     lib.egm_execute.argtypes = [vp, vp, vp, vp, vp, vp, sz, vp]
     lib.egm_execute.restype = i32
+    lib.egm_execute_strided.argtypes = [vp, i64, vp, i64, vp, i64, vp, i64, vp, i64, vp]
+    lib.egm_execute_strided.restype = i32
     lib.egm_free.argtypes = [vp]
     lib.egm_free.restype = i32
     lib.egm_plan_workspace_bytes.argtypes = [vp]
@@ -178,6 +181,16 @@ def egm_execute(plan: int, A: int, B: int, D: int, aux: int = 0, workspace: int 
     if raw_status:
         return st
     _check(st, "egm_execute")
+    return None
+
+
+def egm_execute_strided(plan: int, batch: int, A: int, stride_a: int, B: int, stride_b: int, D: int, stride_d: int,
+                        aux: int = 0, stride_aux: int = 0, stream: int = 0, raw_status: bool = False):
+    st = LIB.egm_execute_strided(plan, int(batch), A or None, int(stride_a), B or None, int(stride_b), D or None,
+                                 int(stride_d), aux or None, int(stride_aux), stream or None)
+    if raw_status:
+        return st
+    _check(st, "egm_execute_strided")
     return None
 
 
@@ -291,6 +304,7 @@ class Matmul:
         self.dtype = out_dtype
         self._plan = None
         self._keep = ()
+        self._res_batch = 0
         self.epilog = None
 
     @staticmethod
@@ -343,11 +357,13 @@ class Matmul:
                 raise ValueError(f"bias shape {tuple(bias.shape)} must be (m,1)=({self.m},1) or (1,n)=(1,{self.n})")
             bias_ptr = bias.data_ptr()
             keep.append(bias)
+        self._res_batch = 0
         if "residual" in ins:
             r = ins["residual"]
             self._check_operand(r, "residual")
-            if r.dtype != self.dtype or tuple(r.shape) != (self.m, self.n):
-                raise ValueError("residual must be [m,n] in the operand dtype")
+            if r.dtype != self.dtype or tuple(r.shape[-2:]) != (self.m, self.n) or r.dim() not in (2, 3):
+                raise ValueError("residual must be [m,n] (or [batch,m,n] for execute_batched) in the output dtype")
+            self._res_batch = r.shape[0] if r.dim() == 3 else 1
             res_ptr = r.data_ptr()
             keep.append(r)
         self.free()
@@ -408,6 +424,51 @@ class Matmul:
         if self.epilog == "DRELU":
             return d
         return (d, mask) if mask is not None else d
+
+    def execute_batched(self, a, b, out=None, aux=None, stream=None):
+        """One launch over a batch of problems of the planned shape: ``a`` is
+        [batch, m, k] or the planned [m, k] shared by every problem, ``b`` is
+        [batch, k, n] or [k, n] shared; returns D [batch, m, n] (and the
+        [batch, m, n/8] mask for RELU_AUX_BIAS).  DRELU takes ``aux`` as the
+        [batch, m, n/8] input mask.  A BIAS_RESIDUAL residual bound at plan
+        must then be [batch, m, n].  Every problem's buffers must start
+        16-byte aligned: with masks, m*n/8 must be a multiple of 16."""
+        import torch
+        plan = self._require()
+        batch = None
+        strides = []
+        for t, shape, dt in ((a, (self.m, self.k), self.a.dtype), (b, (self.k, self.n), self.b.dtype)):
+            self._check_operand(t, "operand", fp8=self.fp8 is not None)
+            if t.dtype != dt:
+                raise ValueError("batched operands keep the planned dtype")
+            if tuple(t.shape) == shape:
+                strides.append(0)
+            elif t.dim() == 3 and tuple(t.shape[1:]) == shape:
+                if batch is not None and t.shape[0] != batch:
+                    raise ValueError("batch sizes differ")
+                batch = t.shape[0]
+                strides.append(shape[0] * shape[1])
+            else:
+                raise ValueError(f"operand shape {tuple(t.shape)} is neither {shape} nor [batch, *{shape}]")
+        if batch is None:
+            raise ValueError("at least one operand must carry the batch dimension")
+        if self.epilog == "BIAS_RESIDUAL" and self._res_batch < batch:
+            raise ValueError(f"the residual bound at plan holds {self._res_batch} problems, the batch {batch}: it "
+                             "advances with D and must be [batch, m, n]")
+        d = out if out is not None else torch.empty((batch, self.m, self.n), dtype=self.dtype, device=a.device)
+        mask = None
+        if self.epilog == "RELU_AUX_BIAS":
+            mask = aux if aux is not None else torch.empty((batch, self.m, self.n // 8), dtype=torch.uint8,
+                                                           device=a.device)
+        elif self.epilog == "DRELU":
+            if aux is None or aux.dtype != torch.uint8 or tuple(aux.shape) != (batch, self.m, self.n // 8):
+                raise ValueError("DRELU takes the forward masks: aux = uint8 [batch, m, n/8] on the GPU")
+            mask = aux
+        s = stream if stream is not None else torch.cuda.current_stream(a.device)
+        egm_execute_strided(plan, batch, a.data_ptr(), strides[0], b.data_ptr(), strides[1], d.data_ptr(),
+                            self.m * self.n, mask.data_ptr() if mask is not None else 0,
+                            self.m * (self.n // 8) if mask is not None else 0, s.cuda_stream)
+        return (d, mask) if self.epilog == "RELU_AUX_BIAS" else d
 
     def free(self):
         if self._plan is not None:

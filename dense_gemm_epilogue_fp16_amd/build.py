@@ -1,6 +1,6 @@
 """Build libegm.so (the C-ABI library) in-tree with hipcc for gfx950.
 
-    python -m dense_gemm_epilogue_fp16_amd.build      # or build() from Python
+    python dense_gemm_epilogue_fp16_amd/build.py      # or build() from Python (loads this file by path)
 
 Translation units: egm_kernels.hip once per 16-bit dtype (fp16, bf16) and
 once per (fp8 format pair, output dtype), and the host API egm_api.hip,

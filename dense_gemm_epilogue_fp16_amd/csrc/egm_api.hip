@@ -134,8 +134,15 @@ void describe(const egm_plan_s* p, char* buf, size_t len) {
            p->autotune_pending ? " autotune=pending" : "");
 }
 
+// a strided batch of problems in one launch (grid.y); {1, 0, ...} for one problem
+struct Batch {
+  int64_t count;
+  int64_t stride_a, stride_b, stride_d, stride_aux;
+};
+constexpr Batch kOne{1, 0, 0, 0, 0};
+
 hipError_t launch_plan(const egm_plan_s* p, int cfg, const void* A, const void* B, void* D, void* aux,
-                       void* ws, hipStream_t s) {
+                       void* ws, hipStream_t s, const Batch& bt = kOne) {
   const ConfigInfo& c = kConfigs[cfg];
   const int dt = p->dtype == EGM_F16 ? egm::DT_F16 : egm::DT_BF16;
   const int64_t chunks = grad_chunks(p, cfg);
@@ -149,6 +156,10 @@ hipError_t launch_plan(const egm_plan_s* p, int cfg, const void* A, const void* 
   g.partial = partial;
   g.scale_a = p->scale_a;
   g.scale_b = p->scale_b;
+  g.stride_a = bt.stride_a;
+  g.stride_b = bt.stride_b;
+  g.stride_d = bt.stride_d;
+  g.stride_aux = bt.stride_aux;
   g.M = int32_t(p->m);
   g.N = int32_t(p->n);
   g.K = int32_t(p->k);
@@ -156,7 +167,7 @@ hipError_t launch_plan(const egm_plan_s* p, int cfg, const void* A, const void* 
   g.tiles_m = int32_t(cdiv(p->m, c.bm));
   g.tiles_n = int32_t(cdiv(p->n, c.bn));
   g.group_m = effective_group_m(p, cfg);
-  const dim3 grid(uint32_t(int64_t(g.tiles_m) * g.tiles_n));
+  const dim3 grid(uint32_t(int64_t(g.tiles_m) * g.tiles_n), uint32_t(bt.count));
   const int epi = epi_of(p->epilog);
   const bool two_kernels = !p->fused && epi != egm::EPI_NONE;
   g.D = two_kernels ? ws : D;
@@ -411,6 +422,38 @@ egm_status_t egm_execute(egm_plan_t plan, const void* A, const void* B, void* D,
   return err == hipSuccess ? EGM_OK : EGM_ERR_HIP;
 }
 
+egm_status_t egm_execute_strided(egm_plan_t plan, int64_t batch, const void* A, int64_t stride_a, const void* B,
+                                 int64_t stride_b, void* D, int64_t stride_d, void* aux, int64_t stride_aux,
+                                 void* stream) {
+  if (!valid_plan(plan)) return EGM_ERR_INVALID_PLAN;
+  egm_plan_s* p = plan;
+  if (batch < 0 || batch > 65535) return EGM_ERR_INVALID_VALUE;
+  if (!p->fused || p->epilog == EGM_EPILOG_DRELU_BGRAD) return EGM_ERR_NOT_SUPPORTED;
+  const bool need_aux = p->epilog == EGM_EPILOG_RELU_AUX_BIAS || p->epilog == EGM_EPILOG_DRELU;
+  const bool empty = batch == 0 || p->m == 0 || p->n == 0;
+  if (need_aux ? (aux == nullptr && !empty) : aux != nullptr) return EGM_ERR_INVALID_VALUE;
+  if (stride_a < 0 || stride_b < 0 || stride_d < 0 || stride_aux < 0) return EGM_ERR_INVALID_VALUE;
+  // the outputs of different problems must not overlap
+  if (batch > 1 && (stride_d < p->m * p->n || (need_aux && stride_aux < p->m * (p->n / 8))))
+    return EGM_ERR_INVALID_VALUE;
+  if (empty) return EGM_OK;
+  if (D == nullptr) return EGM_ERR_INVALID_VALUE;
+  if (p->k > 0 && (A == nullptr || B == nullptr)) return EGM_ERR_INVALID_VALUE;
+  // every problem's operands keep the 16-byte alignment of the first
+  const int64_t es = p->f8 != 0 ? 1 : 2;
+  if ((A && !aligned16(A)) || (B && !aligned16(B)) || !aligned16(D) || (aux && !aligned16(aux)) ||
+      (stride_a * es) % 16 != 0 || (stride_b * es) % 16 != 0 || (stride_d * 2) % 16 != 0 || stride_aux % 16 != 0)
+    return EGM_ERR_ALIGNMENT;
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  hipError_t err;
+  if (p->autotune_pending) {  // tuned on the first problem
+    err = autotune(p, A, B, D, aux, nullptr, s);
+    if (err != hipSuccess) return EGM_ERR_HIP;
+  }
+  err = launch_plan(p, p->config, A, B, D, aux, nullptr, s, Batch{batch, stride_a, stride_b, stride_d, stride_aux});
+  return err == hipSuccess ? EGM_OK : EGM_ERR_HIP;
+}
+
 egm_status_t egm_free(egm_plan_t plan) {
   if (plan == nullptr) return EGM_OK;
   if (plan->magic != kPlanMagic) return EGM_ERR_INVALID_PLAN;
@@ -446,7 +489,7 @@ const char* egm_status_string(egm_status_t s) {
     case EGM_OK: return "EGM_OK";
     case EGM_ERR_INVALID_VALUE: return "EGM_ERR_INVALID_VALUE: invalid argument";
     case EGM_ERR_NOT_SUPPORTED: return "EGM_ERR_NOT_SUPPORTED: not supported";
-    case EGM_ERR_SHAPE: return "EGM_ERR_SHAPE: invalid shape (dims >= 0, n and k multiples of 8, n,k <= 2^21)";
+    case EGM_ERR_SHAPE: return "EGM_ERR_SHAPE: invalid shape (dims >= 0, n and k multiples of 8 (16 for fp8), n,k <= 2^21)";
     case EGM_ERR_DTYPE: return "EGM_ERR_DTYPE: dtype must be fp16 or bf16";
     case EGM_ERR_ALIGNMENT: return "EGM_ERR_ALIGNMENT: device pointers must be 16-byte aligned";
     case EGM_ERR_INVALID_PLAN: return "EGM_ERR_INVALID_PLAN: invalid or freed plan";

@@ -54,6 +54,9 @@ struct GemmArgs {
                      // [ceil(N/BN), M])
   const float* scale_a;  // fp8 operands: per-tensor dequantisation scales (one fp32 each;
   const float* scale_b;  // NULL = 1), read once per workgroup
+  // strided batches (grid.y problems in one launch): problem z reads A, B, R
+  // and writes D, aux at these element (aux: byte) offsets times z
+  int64_t stride_a, stride_b, stride_d, stride_aux;
   int32_t M, N, K;
   int32_t bias_layout;
   int32_t tiles_m, tiles_n;
@@ -534,6 +537,14 @@ __global__ void __launch_bounds__(C::NT, 1) gemm_epilogue_kernel(GemmArgs p) {
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform per wave
   const int M = p.M, N = p.N, K = p.K;
 
+  if (gridDim.y > 1) {  // problem blockIdx.y of a strided batch
+    const int64_t z = blockIdx.y;
+    p.A = (const uint8_t*)p.A + z * p.stride_a * C::ES;
+    p.B = (const uint8_t*)p.B + z * p.stride_b * C::ES;
+    p.D = (uint8_t*)p.D + z * p.stride_d * 2;
+    if (p.R != nullptr) p.R = (const uint8_t*)p.R + z * p.stride_d * 2;
+    if (p.aux != nullptr) p.aux = (uint8_t*)p.aux + z * p.stride_aux;
+  }
   int tm, tn;
   tile_coords(blockIdx.x, p.tiles_m, p.tiles_n, p.group_m, tm, tn);
   const int m0 = tm * C::BM;

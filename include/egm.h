@@ -50,7 +50,7 @@
 extern "C" {
 #endif
 
-#define EGM_ABI_VERSION 3
+#define EGM_ABI_VERSION 4
 
 typedef enum egm_status_t {
   EGM_OK = 0,
@@ -214,6 +214,24 @@ egm_status_t egm_plan_fp8(egm_plan_t* out, int64_t m, int64_t n, int64_t k, egm_
  */
 egm_status_t egm_execute(egm_plan_t plan, const void* A, const void* B, void* D, void* aux,
                          void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * egm_execute_strided - launch amortisation: the plan on `batch` independent
+ * problems of its shape in ONE launch ([op-fusion] §一: each extra kernel
+ * launch costs fixed overhead that small operators cannot hide).  Problem z
+ * (0 <= z < batch) reads A + z*stride_a and B + z*stride_b (strides in
+ * operand elements; 0 shares one operand, e.g. a weight), and writes
+ * D + z*stride_d (output elements) and aux + z*stride_aux (bytes); a
+ * BIAS_RESIDUAL residual advances with stride_d; the bias (bound at plan) is
+ * shared.  The plan must be fused; DRELU_BGRAD is not supported (its partial
+ * sums are per launch).  batch <= 65535; 0 does nothing.  Every problem's
+ * pointers must keep 16-byte alignment, and outputs must not overlap
+ * (stride_d >= m*n, stride_aux >= m*n/8 for batch > 1).  No workspace is
+ * needed.  Asynchronous and stream-ordered like egm_execute.
+ */
+egm_status_t egm_execute_strided(egm_plan_t plan, int64_t batch, const void* A, int64_t stride_a, const void* B,
+                                 int64_t stride_b, void* D, int64_t stride_d, void* aux, int64_t stride_aux,
+                                 void* stream);
 
 /* egm_free - release a plan.  NULL is accepted (EGM_OK).  A plan must not be
  * used after it is freed; work already enqueued is unaffected. */

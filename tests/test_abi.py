@@ -24,7 +24,7 @@ def declared_functions():
 
 def test_every_declared_symbol_is_exported():
     names = declared_functions()
-    assert len(names) == 11
+    assert len(names) == 12
     assert sorted(egm.EXPORTS) == names
     lib = ctypes.CDLL(egm.LIB_PATH)
     for name in names:
@@ -32,7 +32,7 @@ def test_every_declared_symbol_is_exported():
 
 
 def test_abi_version_and_status_strings():
-    assert egm.egm_abi_version() == 3
+    assert egm.egm_abi_version() == 4
     for s in range(10):
         assert egm.status_string(s).startswith("EGM_")
     assert "unknown" in egm.status_string(12345)
@@ -282,3 +282,41 @@ def test_fp8_plan_validation_and_describe():
                                  args.pop("scale_b"), args.pop("epilog"), args.pop("bias"),
                                  args.pop("bias_layout"), raw_status=True)
         assert st == want and h is None, (kw, st)
+
+
+def test_execute_strided_validation_before_any_hip_call():
+    h = egm.egm_plan(64, 64, 64, F16, E["RELU_AUX_BIAS"], FAKE, COL)
+    try:
+        def st(**kw):
+            args = dict(batch=4, A=FAKE, stride_a=64 * 64, B=FAKE, stride_b=0, D=FAKE, stride_d=64 * 64, aux=FAKE,
+                        stride_aux=64 * 8)
+            args.update(kw)
+            return egm.egm_execute_strided(h, args["batch"], args["A"], args["stride_a"], args["B"], args["stride_b"],
+                                           args["D"], args["stride_d"], args["aux"], args["stride_aux"],
+                                           raw_status=True)
+        assert st(batch=-1) == egm.EGM_ERR_INVALID_VALUE
+        assert st(batch=65536) == egm.EGM_ERR_INVALID_VALUE
+        assert st(aux=0) == egm.EGM_ERR_INVALID_VALUE                # RELU_AUX_BIAS writes masks
+        assert st(stride_d=64 * 64 - 8) == egm.EGM_ERR_INVALID_VALUE  # outputs would overlap
+        assert st(stride_aux=64 * 8 - 16) == egm.EGM_ERR_INVALID_VALUE
+        assert st(stride_a=-8) == egm.EGM_ERR_INVALID_VALUE
+        assert st(stride_a=64 * 64 + 4) == egm.EGM_ERR_ALIGNMENT       # problem 1's A off 16 bytes
+        assert st(stride_aux=64 * 8 + 8) == egm.EGM_ERR_ALIGNMENT
+        assert st(D=0) == egm.EGM_ERR_INVALID_VALUE
+        assert st(batch=0) == egm.EGM_OK                              # nothing to do, no HIP call
+        assert egm.egm_execute_strided(0, 1, FAKE, 0, FAKE, 0, FAKE, 0, raw_status=True) == egm.EGM_ERR_INVALID_PLAN
+    finally:
+        egm.egm_free(h)
+    # the two-kernel path and the bias gradient's per-launch partials do not batch
+    h = egm.egm_plan(64, 64, 64, F16, E["BIAS"], FAKE, COL, fused=0)
+    try:
+        assert egm.egm_execute_strided(h, 2, FAKE, 4096, FAKE, 0, FAKE, 4096, raw_status=True) == \
+            egm.EGM_ERR_NOT_SUPPORTED
+    finally:
+        egm.egm_free(h)
+    h = egm.egm_plan(64, 64, 64, F16, E["DRELU_BGRAD"], 0, COL, bias_grad=FAKE)
+    try:
+        assert egm.egm_execute_strided(h, 2, FAKE, 4096, FAKE, 0, FAKE, 4096, FAKE, 512, raw_status=True) == \
+            egm.EGM_ERR_NOT_SUPPORTED
+    finally:
+        egm.egm_free(h)
