@@ -340,6 +340,40 @@ def fp8_workload_operands(name: str, seed: int = 0) -> Fp8Operands:
                         b_std=1.0 / math.sqrt(w.k), bias_layout=w.bias_layout)
 
 
+@dataclass
+class LayerNormOperands:
+    """Bit patterns of one LayerNorm problem over rows of length n."""
+
+    m: int
+    n: int
+    dtype: str
+    x: np.ndarray                    # [m, n] uint16
+    gamma: np.ndarray                # [n] uint16
+    beta: np.ndarray                 # [n] uint16
+    residual: np.ndarray | None = None  # [m, n] uint16
+
+
+def layernorm_operands(m, n, dtype, seed=0, *, x_std=1.0, x_mean=0.5, gamma_std=0.05, beta_std=0.1,
+                       residual_std=None) -> LayerNormOperands:
+    """x ~ N(x_mean, x_std^2) (tensor 0), gamma ~ 1 + N(0, gamma_std^2) (1),
+    beta ~ N(0, beta_std^2) (2), optional residual (3); each rounded once."""
+    x = normal_f32((m, n), x_std, seed, 0) + np.float32(x_mean)
+    g = normal_f32((n,), gamma_std, seed, 1) + np.float32(1.0)
+    return LayerNormOperands(m, n, dtype, f32_to_bits(x, dtype), f32_to_bits(g, dtype),
+                             normal_bits((n,), beta_std, dtype, seed, 2),
+                             normal_bits((m, n), residual_std, dtype, seed, 3) if residual_std is not None else None)
+
+
+#: LayerNorm after the FFN down-projection (its 4096 x 1024 hidden state), and
+#: a large problem of the same row kernel for the HBM roofline
+LAYERNORM_WORKLOADS = {
+    "layernorm_bf16_4096x1024": Workload("layernorm_bf16_4096x1024", 4096, 1024, 0, BF16, ("LAYERNORM",), "col",
+                                         "the FFN block's normalisation of its 4096 x 1024 output"),
+    "layernorm_bf16_65536x16384": Workload("layernorm_bf16_65536x16384", 65536, 16384, 0, BF16, ("LAYERNORM",),
+                                           "col", "2 GiB in, 2 GiB out: the row kernel at HBM scale"),
+}
+
+
 def mask_bits(m: int, n: int, seed: int, tensor_index: int) -> np.ndarray:
     """A packed [m, n/8] uint8 mask of independent fair bits."""
     if n % 8:

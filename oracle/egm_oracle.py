@@ -55,6 +55,14 @@ output would lose the precision the epilogue exists to keep.  Then
   Z = scale_a * scale_b * (A8 . B8) + bias,  Y = epilogue(Z)
 with the same epilogues as above.
 
+LayerNorm after the down-projection ([op-fusion] §二: the formula
+y = (x - mu) / sqrt(sigma^2 + eps) * gamma + beta over the last axis, eps 1e-5
+by default, and the variant that adds a residual to the normalised output;
+the page computes mean and variance in one pass with Welford's method, which
+reaches the same statistics up to rounding): mu is the row mean, sigma^2 the
+row's biased variance (divided by the row length), gamma and beta per column.
+The oracle is that definition in fp64.
+
 Every function here is pinned by ``tests/test_oracle_pins.py`` against brute
 force, closed forms, invariants and library routines.
 """
@@ -349,3 +357,38 @@ def backward_reference(a_bits, b_bits, dtype, epilog, mask, bias_layout=None):
     if bias_layout is None:
         raise ValueError("DRELU_BGRAD needs the bias layout")
     return dz, bias_grad(dz, bias_layout), bias_grad_error_bound(a64, b64, mask, bias_layout)
+
+
+# ---------------------------------------------------------------------------
+# LayerNorm over the last axis ([op-fusion] §二)
+# ---------------------------------------------------------------------------
+LN_EPS = 1e-5
+
+
+def layer_norm(x64: np.ndarray, gamma64=None, beta64=None, eps: float = LN_EPS, r64=None):
+    """y = (x - mean) / sqrt(var + eps) * gamma + beta (+ r), per row, in fp64,
+    with the biased variance; returns (y, mean, rstd).  gamma = None means 1,
+    beta = None means 0; r (optional) is added to the normalised output."""
+    x = np.asarray(x64, dtype=np.float64)
+    n = x.shape[-1]
+    if n == 0:
+        raise ValueError("LayerNorm needs a non-empty row")
+    mean = x.sum(axis=-1) / n
+    centred = x - mean[..., None]
+    var = (centred * centred).sum(axis=-1) / n
+    rstd = 1.0 / np.sqrt(var + float(eps))
+    y = centred * rstd[..., None]
+    if gamma64 is not None:
+        y = y * np.asarray(gamma64, dtype=np.float64).reshape(-1)[None, :]
+    if beta64 is not None:
+        y = y + np.asarray(beta64, dtype=np.float64).reshape(-1)[None, :]
+    if r64 is not None:
+        y = y + np.asarray(r64, dtype=np.float64)
+    return y, mean, rstd
+
+
+def layer_norm_reference(x_bits, dtype, gamma_bits=None, beta_bits=None, eps: float = LN_EPS, residual_bits=None):
+    """LayerNorm of 16-bit inputs (bit patterns), every parameter widened exactly."""
+    return layer_norm(widen(x_bits, dtype), None if gamma_bits is None else widen(gamma_bits, dtype),
+                      None if beta_bits is None else widen(beta_bits, dtype), eps,
+                      None if residual_bits is None else widen(residual_bits, dtype))

@@ -558,4 +558,85 @@ def pin_fp8_scales(o):
     assert np.array_equal(y5, np.repeat(o.widen(ops.bias, BF16)[:, None], 32, axis=1))
 
 
+# ---------------------------------------------------------------------------
+# LayerNorm
+# ---------------------------------------------------------------------------
+def _golden_layernorm():
+    cases, cur = [], None
+    with open(os.path.join(GOLDEN, "layernorm_small.txt")) as f:
+        for line in f:
+            if not line.strip() or line.startswith("#"):
+                continue
+            key, *vals = line.split()
+            if key == "CASE":
+                cur = {"name": vals[0], "eps": float(vals[1])}
+                cases.append(cur)
+            else:
+                cur[key] = np.array([float(v) for v in vals])
+    return cases
+
+
+def pin_layernorm_golden(o):
+    cases = _golden_layernorm()
+    assert len(cases) >= 6
+    for c in cases:
+        y, _, _ = o.layer_norm(c["X"][None, :], c["GAMMA"], c["BETA"], c["eps"],
+                               c["R"][None, :] if "R" in c else None)
+        assert np.array_equal(y[0], c["Y"]), (c["name"], y[0], c["Y"])
+
+
+def pin_layernorm_library(o):
+    """torch.nn.functional.layer_norm in fp64 (an independent implementation)."""
+    import torch
+    rng = np.random.default_rng(12)
+    for n in (8, 100, 1024):
+        x = rng.standard_normal((7, n)) * 3 + 1
+        g, b = rng.standard_normal(n), rng.standard_normal(n)
+        for eps in (1e-5, 0.5):
+            y, mean, rstd = o.layer_norm(x, g, b, eps)
+            ref = torch.nn.functional.layer_norm(torch.from_numpy(x), (n,), torch.from_numpy(g), torch.from_numpy(b),
+                                                 eps).numpy()
+            assert np.allclose(y, ref, rtol=0, atol=1e-12)
+            assert np.allclose(mean, x.mean(axis=1), rtol=0, atol=1e-13)
+            assert np.allclose(rstd, 1 / np.sqrt(x.var(axis=1) + eps), rtol=1e-13, atol=0)
+
+
+def pin_layernorm_brute_force(o):
+    """Exact rational mean and variance by loops; one final square root."""
+    rng = np.random.default_rng(13)
+    for n in (3, 8, 17):
+        x = rng.integers(-20, 21, size=(4, n)) / 8.0
+        g, b = rng.integers(-8, 9, size=n) / 4.0, rng.integers(-8, 9, size=n) / 4.0
+        y, mean, rstd = o.layer_norm(x, g, b, 0.0625)
+        for i in range(4):
+            xs = [Fraction(*float(v).as_integer_ratio()) for v in x[i]]
+            mu = sum(xs, Fraction(0)) / n
+            var = sum(((v - mu) ** 2 for v in xs), Fraction(0)) / n
+            rs = 1.0 / math.sqrt(float(var + Fraction(1, 16)))
+            assert float(mu) == mean[i] and abs(rstd[i] - rs) <= 1e-15 * rs
+            for j in range(n):
+                want = float(xs[j] - mu) * rs * float(g[j]) + float(b[j])
+                assert abs(y[i, j] - want) <= 1e-13 * (1 + abs(want))
+
+
+def pin_layernorm_invariants(o):
+    """Shift invariance; scale invariance at eps = 0; the normalised row has
+    mean 0 and variance var / (var + eps); gamma, beta and the residual act
+    affinely."""
+    rng = np.random.default_rng(14)
+    x = rng.standard_normal((5, 64))
+    y0, _, _ = o.layer_norm(x, None, None, 1e-5)
+    y1, _, _ = o.layer_norm(x + 7.0, None, None, 1e-5)
+    assert np.allclose(y0, y1, rtol=0, atol=1e-12)
+    ya, _, _ = o.layer_norm(x, None, None, 0.0)
+    yb, _, _ = o.layer_norm(x * 3.5, None, None, 0.0)
+    assert np.allclose(ya, yb, rtol=0, atol=1e-12)
+    var = x.var(axis=1)
+    assert np.allclose(y0.mean(axis=1), 0.0, atol=1e-14)
+    assert np.allclose(y0.var(axis=1), var / (var + 1e-5), rtol=1e-12)
+    g, b, r = rng.standard_normal(64), rng.standard_normal(64), rng.standard_normal((5, 64))
+    yg, _, _ = o.layer_norm(x, g, b, 1e-5, r)
+    assert np.allclose(yg, y0 * g[None, :] + b[None, :] + r, rtol=0, atol=1e-12)
+
+
 PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_")]

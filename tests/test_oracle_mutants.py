@@ -150,7 +150,47 @@ def _fp8_scale_on_bias(a, b, fa, fb, sa, sb, out, epilog, bias_bits=None, bias_l
     return y, z, (eo.relu_mask(z) if epilog == "RELU_AUX_BIAS" else None)
 
 
+def _ln_unbiased(x64, gamma64=None, beta64=None, eps=1e-5, r64=None):
+    x = np.asarray(x64, dtype=np.float64)
+    n = x.shape[-1]
+    y, mean, _ = _orig["layer_norm"](x, None, None, 0.0)
+    var = ((x - mean[..., None]) ** 2).sum(axis=-1) / max(n - 1, 1)
+    rstd = 1 / np.sqrt(var + eps)
+    y = (x - mean[..., None]) * rstd[..., None]
+    y = y * (1 if gamma64 is None else np.asarray(gamma64)[None, :]) + (0 if beta64 is None else np.asarray(beta64)[None, :])
+    return (y if r64 is None else y + r64), mean, rstd
+
+
+def _ln_eps_outside(x64, gamma64=None, beta64=None, eps=1e-5, r64=None):
+    x = np.asarray(x64, dtype=np.float64)
+    mean = x.mean(axis=-1)
+    rstd = 1 / (np.sqrt(((x - mean[..., None]) ** 2).mean(axis=-1)) + eps)
+    y = (x - mean[..., None]) * rstd[..., None]
+    y = y * (1 if gamma64 is None else np.asarray(gamma64)[None, :]) + (0 if beta64 is None else np.asarray(beta64)[None, :])
+    return (y if r64 is None else y + r64), mean, rstd
+
+
+def _ln_residual_before(x64, gamma64=None, beta64=None, eps=1e-5, r64=None):
+    x = np.asarray(x64, dtype=np.float64) + (0 if r64 is None else np.asarray(r64))
+    return _orig["layer_norm"](x, gamma64, beta64, eps, None)
+
+
+def _ln_gamma_beta_swapped(x64, gamma64=None, beta64=None, eps=1e-5, r64=None):
+    return _orig["layer_norm"](x64, beta64, gamma64, eps, r64)
+
+
+def _ln_column_stats(x64, gamma64=None, beta64=None, eps=1e-5, r64=None):
+    y, mean, rstd = _orig["layer_norm"](np.asarray(x64, dtype=np.float64).T, None, None, eps, None)
+    y = y.T * (1 if gamma64 is None else np.asarray(gamma64)[None, :]) + (0 if beta64 is None else np.asarray(beta64)[None, :])
+    return (y if r64 is None else y + r64), mean, rstd
+
+
 MUTANTS = {
+    "ln_unbiased_variance": ("layer_norm", _ln_unbiased),
+    "ln_eps_outside_sqrt": ("layer_norm", _ln_eps_outside),
+    "ln_residual_before_norm": ("layer_norm", _ln_residual_before),
+    "ln_gamma_beta_swapped": ("layer_norm", _ln_gamma_beta_swapped),
+    "ln_column_statistics": ("layer_norm", _ln_column_stats),
     "fp8_e4m3_bias_8": ("FP8_FORMATS", {"e4m3": (4, 3, 8), "e5m2": (5, 2, 15)}),
     "fp8_subnormal_as_normal": ("decode_fp8", _fp8_subnormal_as_normal),
     "fp8_e5m2_no_infinity": ("decode_fp8", _fp8_e5m2_no_infinity),

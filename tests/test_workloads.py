@@ -100,3 +100,13 @@ def test_fp8_quantize_recipe():
     assert list(big) == [0x7E, 0xFE]
     w = W.FP8_WORKLOADS["gemm_relu_aux_bias_fp8e4m3_8192x8192x8192"]
     assert (w.m, w.n, w.k, w.dtype, w.bias_layout) == (8192, 8192, 8192, W.BF16, "col")
+
+
+def test_layernorm_operands():
+    o = W.layernorm_operands(40, 96, W.BF16, seed=2, residual_std=0.5)
+    x = W.bits_to_f32(o.x, W.BF16)
+    assert o.x.shape == (40, 96) and o.gamma.shape == (96,) and o.beta.shape == (96,) and o.residual.shape == (40, 96)
+    assert abs(float(x.mean()) - 0.5) < 0.1 and 0.8 < float(x.std()) < 1.2
+    g = W.bits_to_f32(o.gamma, W.BF16)
+    assert abs(float(g.mean()) - 1.0) < 0.05
+    assert set(W.LAYERNORM_WORKLOADS) == {"layernorm_bf16_4096x1024", "layernorm_bf16_65536x16384"}
