@@ -63,7 +63,8 @@ EGM_BIAS_COL = 2  # shape (1, n)
 
 #: every symbol include/egm.h declares
 EXPORTS = (
-    "egm_plan", "egm_plan_fp8", "egm_execute", "egm_execute_strided", "egm_free", "egm_plan_workspace_bytes",
+    "egm_plan", "egm_plan_fp8", "egm_execute", "egm_execute_strided", "egm_layernorm", "egm_free",
+    "egm_plan_workspace_bytes",
     "egm_plan_describe",
     "egm_plan_config", "egm_num_configs", "egm_config_describe", "egm_status_string", "egm_abi_version",
 )
@@ -109,6 +110,8 @@ def _load() -> ctypes.CDLL:
     lib.egm_execute.restype = i32
     lib.egm_execute_strided.argtypes = [vp, i64, vp, i64, vp, i64, vp, i64, vp, i64, vp]
     lib.egm_execute_strided.restype = i32
+    lib.egm_layernorm.argtypes = [i64, i64, i32, vp, vp, vp, vp, ctypes.c_float, vp, vp, vp, vp]
+    lib.egm_layernorm.restype = i32
     lib.egm_free.argtypes = [vp]
     lib.egm_free.restype = i32
     lib.egm_plan_workspace_bytes.argtypes = [vp]
@@ -192,6 +195,44 @@ def egm_execute_strided(plan: int, batch: int, A: int, stride_a: int, B: int, st
         return st
     _check(st, "egm_execute_strided")
     return None
+
+
+def egm_layernorm(rows: int, cols: int, dtype: int, x: int, residual: int, gamma: int, beta: int, eps: float,
+                  y: int, mean: int = 0, rstd: int = 0, stream: int = 0, raw_status: bool = False):
+    st = LIB.egm_layernorm(int(rows), int(cols), int(dtype), x or None, residual or None, gamma or None,
+                           beta or None, float(eps), y or None, mean or None, rstd or None, stream or None)
+    if raw_status:
+        return st
+    _check(st, "egm_layernorm")
+    return None
+
+
+def layer_norm(x, gamma=None, beta=None, eps: float = 1e-5, residual=None, out=None, return_stats: bool = False,
+               stream=None):
+    """LayerNorm over the last axis of a 2-D fp16/bf16 GPU tensor x [rows, cols]:
+    (x - mean) / sqrt(var + eps) * gamma + beta (+ residual), one launch of the
+    library's row kernel.  ``out`` may be x (in place).  With ``return_stats``
+    also returns the fp32 mean and rstd per row."""
+    import torch
+    for t, name in ((x, "x"), (residual, "residual"), (out, "out")):
+        if t is not None and (not t.is_cuda or not t.is_contiguous() or t.dtype != x.dtype or tuple(t.shape) !=
+                              tuple(x.shape) or t.dim() != 2):
+            raise ValueError(f"{name} must be a contiguous [rows, cols] GPU tensor in x's dtype")
+    for t, name in ((gamma, "gamma"), (beta, "beta")):
+        if t is not None and (not t.is_cuda or not t.is_contiguous() or t.dtype != x.dtype or t.numel() != x.shape[1]):
+            raise ValueError(f"{name} must be a contiguous [cols] GPU tensor in x's dtype")
+    rows, cols = x.shape
+    y = out if out is not None else torch.empty_like(x)
+    mean = rstd = None
+    if return_stats:
+        mean = torch.empty(rows, dtype=torch.float32, device=x.device)
+        rstd = torch.empty(rows, dtype=torch.float32, device=x.device)
+    s = stream if stream is not None else torch.cuda.current_stream(x.device)
+    egm_layernorm(rows, cols, _dtype_code(x), x.data_ptr(), residual.data_ptr() if residual is not None else 0,
+                  gamma.data_ptr() if gamma is not None else 0, beta.data_ptr() if beta is not None else 0, eps,
+                  y.data_ptr(), mean.data_ptr() if mean is not None else 0,
+                  rstd.data_ptr() if rstd is not None else 0, s.cuda_stream)
+    return (y, mean, rstd) if return_stats else y
 
 
 def egm_free(plan: int, raw_status: bool = False):

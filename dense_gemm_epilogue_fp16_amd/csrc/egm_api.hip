@@ -22,6 +22,7 @@
 #include "egm_epilogue.hpp"
 #include "egm_gemm.hpp"
 #include "egm_launch.hpp"
+#include "egm_layernorm.hpp"
 
 namespace {
 
@@ -498,6 +499,44 @@ const char* egm_status_string(egm_status_t s) {
     case EGM_ERR_WORKSPACE: return "EGM_ERR_WORKSPACE: workspace missing or too small";
   }
   return "EGM: unknown status";
+}
+
+egm_status_t egm_layernorm(int64_t rows, int64_t cols, egm_dtype_t dtype, const void* x, const void* residual,
+                           const void* gamma, const void* beta, float eps, void* y, float* mean, float* rstd,
+                           void* stream) {
+  if (rows < 0 || cols <= 0 || cols % 8 != 0) return EGM_ERR_SHAPE;
+  constexpr int64_t kMaxCols = int64_t(egm::kLnConfigs[egm::kNumLnConfigs - 1].tpr) *
+                               egm::kLnConfigs[egm::kNumLnConfigs - 1].cpt * 8;
+  if (cols > kMaxCols) return EGM_ERR_SHAPE;
+  if (dtype != EGM_F16 && dtype != EGM_BF16) return EGM_ERR_DTYPE;
+  if (!(eps >= 0.0f) || eps > 3.0e38f) return EGM_ERR_INVALID_VALUE;  // also rejects NaN
+  if (rows == 0) return EGM_OK;
+  if (x == nullptr || y == nullptr) return EGM_ERR_INVALID_VALUE;
+  if (!aligned16(x) || !aligned16(y) || (residual && !aligned16(residual)) || (gamma && !aligned16(gamma)) ||
+      (beta && !aligned16(beta)) || (reinterpret_cast<uintptr_t>(mean) & 3u) != 0 ||
+      (reinterpret_cast<uintptr_t>(rstd) & 3u) != 0)
+    return EGM_ERR_ALIGNMENT;
+  int cfg = 0;
+  while (int64_t(egm::kLnConfigs[cfg].tpr) * egm::kLnConfigs[cfg].cpt * 8 < cols) ++cfg;
+  const egm::LnLaunch launch = dtype == EGM_F16 ? egm::layernorm_launcher_f16(cfg, residual != nullptr)
+                                                : egm::layernorm_launcher_bf16(cfg, residual != nullptr);
+  if (launch == nullptr) return EGM_ERR_NOT_SUPPORTED;
+  egm::LnArgs a{};
+  a.x = x;
+  a.r = residual;
+  a.gamma = gamma;
+  a.beta = beta;
+  a.y = y;
+  a.mean = mean;
+  a.rstd = rstd;
+  a.M = rows;
+  a.N = int32_t(cols);
+  a.eps = eps;
+  const int64_t rows_per_wg = 256 / egm::kLnConfigs[cfg].tpr;
+  const int64_t wgs = cdiv(rows, rows_per_wg);
+  if (wgs > int64_t(0x7fffffff)) return EGM_ERR_SHAPE;
+  launch(dim3(uint32_t(wgs)), reinterpret_cast<hipStream_t>(stream), a);
+  return hipGetLastError() == hipSuccess ? EGM_OK : EGM_ERR_HIP;
 }
 
 int32_t egm_abi_version(void) { return EGM_ABI_VERSION; }

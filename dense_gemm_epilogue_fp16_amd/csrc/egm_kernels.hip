@@ -7,6 +7,7 @@
 #include "egm_epilogue.hpp"
 #include "egm_gemm.hpp"
 #include "egm_launch.hpp"
+#include "egm_layernorm.hpp"
 
 #ifndef EGM_DTYPE
 #error "EGM_DTYPE must be 0 (fp16) or 1 (bf16)"
@@ -37,6 +38,27 @@ void launch_epi(dim3 grid, hipStream_t s, const EpiArgs& a) {
 
 void launch_partials(dim3 grid, hipStream_t s, const void* D, int64_t M, int32_t N, int32_t layout, float* partial) {
   hipLaunchKernelGGL((axis_partials_kernel<DT>), grid, dim3(256), 0, s, D, M, N, layout, partial);
+}
+
+template <int CFG, bool RES>
+void launch_ln(dim3 grid, hipStream_t s, const LnArgs& a) {
+  constexpr LnConfig c = kLnConfigs[CFG];
+  hipLaunchKernelGGL((layernorm_kernel<DT, c.tpr, c.cpt, RES>), grid, dim3(256), 0, s, a);
+}
+
+template <bool RES>
+LnLaunch ln_row(int cfg) {
+  static_assert(kNumLnConfigs == 7, "update the LayerNorm launch table with its config table");
+  switch (cfg) {
+    case 0: return &launch_ln<0, RES>;
+    case 1: return &launch_ln<1, RES>;
+    case 2: return &launch_ln<2, RES>;
+    case 3: return &launch_ln<3, RES>;
+    case 4: return &launch_ln<4, RES>;
+    case 5: return &launch_ln<5, RES>;
+    case 6: return &launch_ln<6, RES>;
+    default: return nullptr;
+  }
 }
 #endif
 
@@ -90,6 +112,7 @@ EpiLaunch epi_table(int epi) {
 #define EGM_FP8_LAUNCHER(dt, f8) EGM_CAT3(gemm_launcher_fp8_, dt, f8)
 GemmLaunch EGM_FP8_LAUNCHER(EGM_DTYPE, EGM_F8)(int epi, int cfg) { return gemm_table(epi, cfg); }
 #elif EGM_DTYPE == 0
+LnLaunch layernorm_launcher_f16(int cfg, bool residual) { return residual ? ln_row<true>(cfg) : ln_row<false>(cfg); }
 GemmLaunch gemm_launcher_f16(int epi, int cfg) { return gemm_table(epi, cfg); }
 EpiLaunch epi_launcher_f16(int epi) { return epi_table(epi); }
 PartialsLaunch partials_launcher_f16() { return &launch_partials; }
@@ -98,6 +121,7 @@ void launch_bias_grad_finish(dim3 grid, hipStream_t s, const float* partial, int
   hipLaunchKernelGGL(bias_grad_finish_kernel<float>, grid, dim3(256), 0, s, partial, chunks, len, out);
 }
 #else
+LnLaunch layernorm_launcher_bf16(int cfg, bool residual) { return residual ? ln_row<true>(cfg) : ln_row<false>(cfg); }
 GemmLaunch gemm_launcher_bf16(int epi, int cfg) { return gemm_table(epi, cfg); }
 EpiLaunch epi_launcher_bf16(int epi) { return epi_table(epi); }
 PartialsLaunch partials_launcher_bf16() { return &launch_partials; }

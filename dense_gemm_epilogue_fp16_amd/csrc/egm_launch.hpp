@@ -10,6 +10,19 @@ namespace egm {
 
 struct GemmArgs;
 struct EpiArgs;
+struct LnArgs;
+
+// LayerNorm row kernel shapes: tpr threads per row (64: one wave; 256: a
+// workgroup), each holding cpt 16-byte chunks; rows up to tpr * cpt * 8
+// elements.  The host picks the first config whose capacity covers the row.
+struct LnConfig {
+  int tpr, cpt;
+};
+inline constexpr LnConfig kLnConfigs[] = {{64, 1}, {64, 2}, {64, 4}, {64, 8}, {256, 4}, {256, 8}, {256, 16}};
+inline constexpr int kNumLnConfigs = int(sizeof(kLnConfigs) / sizeof(kLnConfigs[0]));
+using LnLaunch = void (*)(dim3 grid, hipStream_t stream, const LnArgs& args);
+LnLaunch layernorm_launcher_f16(int cfg, bool residual);
+LnLaunch layernorm_launcher_bf16(int cfg, bool residual);
 
 struct ConfigInfo {
   int bm, bn;      // output tile

@@ -50,7 +50,7 @@
 extern "C" {
 #endif
 
-#define EGM_ABI_VERSION 4
+#define EGM_ABI_VERSION 5
 
 typedef enum egm_status_t {
   EGM_OK = 0,
@@ -232,6 +232,28 @@ egm_status_t egm_execute(egm_plan_t plan, const void* A, const void* B, void* D,
 egm_status_t egm_execute_strided(egm_plan_t plan, int64_t batch, const void* A, int64_t stride_a, const void* B,
                                  int64_t stride_b, void* D, int64_t stride_d, void* aux, int64_t stride_aux,
                                  void* stream);
+
+/*
+ * egm_layernorm - LayerNorm over the rows of x [rows, cols] (row-major, fp16
+ * or bf16), the normalisation that follows the FFN down-projection
+ * ([op-fusion] §二, formula and the LayerNorm + residual variant):
+ *   y[i,j] = (x[i,j] - mean_i) / sqrt(var_i + eps) * gamma[j] + beta[j] (+ residual[i,j])
+ * mean_i and var_i (biased: divided by cols) over row i, from one pass over
+ * the row with Welford-style merging of partial statistics in fp32; the
+ * result is rounded once to dtype.  The residual is added after the affine
+ * step; the post-norm form LN(x + r) is the BIAS_RESIDUAL GEMM epilogue
+ * followed by this call without a residual.
+ *   gamma, beta  [cols] in dtype, or NULL (1 and 0).   residual  [rows, cols] or NULL.
+ *   eps          >= 0 (1e-5 is the usual value).
+ *   y            [rows, cols] output; may be x itself (in place).
+ *   mean, rstd   [rows] fp32 outputs (1 / sqrt(var + eps)), or NULL.
+ *   cols a multiple of 8, 8 <= cols <= 32768; rows >= 0 (0 does nothing).
+ * Device pointers 16-byte aligned (mean, rstd 4-byte).  One launch on the
+ * stream, asynchronous; no workspace.  Does not need a plan.
+ */
+egm_status_t egm_layernorm(int64_t rows, int64_t cols, egm_dtype_t dtype, const void* x, const void* residual,
+                           const void* gamma, const void* beta, float eps, void* y, float* mean, float* rstd,
+                           void* stream);
 
 /* egm_free - release a plan.  NULL is accepted (EGM_OK).  A plan must not be
  * used after it is freed; work already enqueued is unaffected. */

@@ -24,7 +24,7 @@ def declared_functions():
 
 def test_every_declared_symbol_is_exported():
     names = declared_functions()
-    assert len(names) == 12
+    assert len(names) == 13
     assert sorted(egm.EXPORTS) == names
     lib = ctypes.CDLL(egm.LIB_PATH)
     for name in names:
@@ -32,7 +32,7 @@ def test_every_declared_symbol_is_exported():
 
 
 def test_abi_version_and_status_strings():
-    assert egm.egm_abi_version() == 4
+    assert egm.egm_abi_version() == 5
     for s in range(10):
         assert egm.status_string(s).startswith("EGM_")
     assert "unknown" in egm.status_string(12345)
@@ -320,3 +320,25 @@ def test_execute_strided_validation_before_any_hip_call():
             egm.EGM_ERR_NOT_SUPPORTED
     finally:
         egm.egm_free(h)
+
+
+def test_layernorm_validation_before_any_hip_call():
+    def st(**kw):
+        a = dict(rows=16, cols=1024, dtype=BF16, x=FAKE, residual=0, gamma=FAKE, beta=FAKE, eps=1e-5, y=FAKE, mean=0,
+                 rstd=0)
+        a.update(kw)
+        return egm.egm_layernorm(a["rows"], a["cols"], a["dtype"], a["x"], a["residual"], a["gamma"], a["beta"],
+                                 a["eps"], a["y"], a["mean"], a["rstd"], raw_status=True)
+    assert st(cols=0) == egm.EGM_ERR_SHAPE
+    assert st(cols=12) == egm.EGM_ERR_SHAPE          # not a multiple of 8
+    assert st(cols=32768 + 8) == egm.EGM_ERR_SHAPE   # longer than one row kernel holds
+    assert st(rows=-1) == egm.EGM_ERR_SHAPE
+    assert st(dtype=9) == egm.EGM_ERR_DTYPE
+    assert st(eps=-1.0) == egm.EGM_ERR_INVALID_VALUE
+    assert st(eps=float("nan")) == egm.EGM_ERR_INVALID_VALUE
+    assert st(x=0) == egm.EGM_ERR_INVALID_VALUE
+    assert st(y=0) == egm.EGM_ERR_INVALID_VALUE
+    assert st(gamma=FAKE + 2) == egm.EGM_ERR_ALIGNMENT
+    assert st(residual=FAKE + 8) == egm.EGM_ERR_ALIGNMENT
+    assert st(mean=FAKE + 2) == egm.EGM_ERR_ALIGNMENT
+    assert st(rows=0) == egm.EGM_OK                  # nothing to do, no HIP call

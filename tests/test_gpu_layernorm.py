@@ -1,0 +1,105 @@
+"""LayerNorm row kernel on the GPU against the CPU oracle, through the C ABI,
+and the whole FFN block (up GELU_BIAS, down BIAS_RESIDUAL, LayerNorm)."""
+import numpy as np
+import pytest
+
+import egm_workloads as W
+from oracle import egm_oracle as eo
+from parity import compare, to_device, to_host_bits
+
+pytestmark = pytest.mark.gpu
+
+# one row length per row-kernel config (64 x 1 .. 256 x 16 chunks), plus
+# lengths that leave some threads a chunk short
+COLS = [8, 200, 520, 1024, 2048, 4096, 4104, 8192, 16384, 32768]
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    import torch
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import dense_gemm_epilogue_fp16_amd  # noqa: F401  (fails loudly without libegm.so)
+
+
+def _check_stats(mean, rstd, mref, rref):
+    mean, rstd = mean.cpu().numpy().astype(np.float64), rstd.cpu().numpy().astype(np.float64)
+    assert np.all(np.abs(mean - mref) <= 1e-4 * (1 + np.abs(mref))), float(np.abs(mean - mref).max())
+    assert np.all(np.abs(rstd - rref) <= 1e-4 * rref), float((np.abs(rstd - rref) / rref).max())
+
+
+@pytest.mark.parametrize("dtype", ["fp16", "bf16"])
+@pytest.mark.parametrize("cols", COLS)
+def test_layernorm_vs_oracle(cols, dtype):
+    import dense_gemm_epilogue_fp16_amd as egm
+    rows = 37  # not a multiple of the 4 rows a 64-thread workgroup takes
+    o = W.layernorm_operands(rows, cols, dtype, seed=cols, residual_std=0.3)
+    x, g, b, r = (to_device(o.x, dtype), to_device(o.gamma, dtype), to_device(o.beta, dtype),
+                  to_device(o.residual, dtype))
+    for res in (None, r):
+        y, mean, rstd = egm.layer_norm(x, g, b, 1e-5, residual=res, return_stats=True)
+        yr, mr, rr = eo.layer_norm_reference(o.x, dtype, o.gamma, o.beta, 1e-5, o.residual if res is not None else None)
+        compare(to_host_bits(y), yr, dtype)
+        _check_stats(mean, rstd, mr, rr)
+
+
+def test_layernorm_options_and_edges():
+    import torch
+    import dense_gemm_epilogue_fp16_amd as egm
+    o = W.layernorm_operands(64, 768, "bf16", seed=5)
+    x = to_device(o.x, "bf16")
+    # no gamma / beta
+    y = egm.layer_norm(x, eps=0.5)
+    yr, _, _ = eo.layer_norm_reference(o.x, "bf16", None, None, 0.5)
+    compare(to_host_bits(y), yr, "bf16")
+    # in place
+    x2 = x.clone()
+    g, b = to_device(o.gamma, "bf16"), to_device(o.beta, "bf16")
+    egm.layer_norm(x2, g, b, out=x2)
+    yr, _, _ = eo.layer_norm_reference(o.x, "bf16", o.gamma, o.beta)
+    compare(to_host_bits(x2), yr, "bf16")
+    # constant rows: the centred row is 0, so y is beta exactly
+    c = torch.full((5, 768), 3.25, dtype=torch.bfloat16, device="cuda")
+    y = egm.layer_norm(c, g, b)
+    torch.cuda.synchronize()
+    assert torch.equal(y.view(torch.int16), b.expand(5, -1).contiguous().view(torch.int16))
+    # no rows
+    e = torch.empty((0, 64), dtype=torch.float16, device="cuda")
+    assert egm.layer_norm(e).shape == (0, 64)
+
+
+def test_ffn_block_with_layernorm():
+    """X -> GELU(X W1 + b1) -> (. W2 + b2 + X) -> LayerNorm on the GPU.
+    (i) The LayerNorm step on the oracle's own rounded D (uploaded) against the
+    oracle, to the bf16 tolerance.  (ii) The whole GPU chain against the
+    oracle's chain: the GPU's D may differ from the oracle's by the down
+    projection's tolerance t = 2e-2, which the normalisation carries over
+    scaled by |gamma| rstd (a shift of one value moves the mean and variance
+    only by 1/N of it), so the bound is 2e-2 + 2 t max|gamma| max(rstd).  No GPU
+    output is an oracle input."""
+    import torch
+    import dense_gemm_epilogue_fp16_amd as egm
+    f = W.ffn_operands()
+    ln = W.layernorm_operands(f.tokens, f.hidden, "bf16", seed=11)
+    x, w1, w2 = to_device(f.x, "bf16"), to_device(f.w1, "bf16"), to_device(f.w2, "bf16")
+    b1, b2 = to_device(f.b1, "bf16").reshape(1, -1), to_device(f.b2, "bf16").reshape(1, -1)
+    g, b = to_device(ln.gamma, "bf16"), to_device(ln.beta, "bf16")
+    y_up, _, _ = eo.reference(f.x, f.w1, "bf16", "GELU_BIAS", f.b1, "col")
+    h_ref = eo.round_to_bits(y_up, "bf16")
+    y_dn, _, _ = eo.reference(h_ref, f.w2, "bf16", "BIAS_RESIDUAL", f.b2, "col", f.x)
+    d_ref = eo.round_to_bits(y_dn, "bf16")
+    y_ln, _, rstd = eo.layer_norm_reference(d_ref, "bf16", ln.gamma, ln.beta)
+    with egm.Matmul(x, w1) as up, egm.Matmul(torch.empty((f.tokens, f.ffn), dtype=torch.bfloat16, device="cuda"),
+                                             w2) as down:
+        up.plan("GELU_BIAS", {"bias": b1})
+        down.plan("BIAS_RESIDUAL", {"bias": b2, "residual": x})
+        h = up.execute()
+        d = down.execute(a=h)
+        y = egm.layer_norm(d, g, b)
+        y_on_ref = egm.layer_norm(to_device(d_ref, "bf16"), g, b)
+        torch.cuda.synchronize()
+    print("[layernorm on the oracle's D]", compare(to_host_bits(y_on_ref), y_ln, "bf16"), flush=True)
+    t = eo.TOLERANCE["bf16"]
+    bound = t + 2 * t * float(np.abs(eo.widen(ln.gamma, "bf16")).max()) * float(rstd.max())
+    print("[ffn block + layernorm, GPU chain]", compare(to_host_bits(y), y_ln, "bf16", tol=bound),
+          f"bound {bound:.3g}", flush=True)
