@@ -37,7 +37,8 @@ PEAK_TFLOPS_FP8 = 5000.0  # MI355X dense fp8 MFMA (published)
 PEAK_HBM_GBS = 8000.0     # MI355X HBM3E (published)
 DEFAULT_WORKLOAD = "gemm_relu_bias_fp16_65536x16384x16384"
 # device code of the fused kernel and the config table that picks its instance
-KERNEL_SOURCES = ("egm_gemm.hpp", "egm_device.hpp", "egm_kernels.hip", "egm_launch.hpp")
+KERNEL_SOURCES = ("egm_gemm.hpp", "egm_device.hpp", "egm_kernels.hip", "egm_launch.hpp", "egm_epilogue.hpp",
+                  "egm_layernorm.hpp")
 
 
 def kernel_source_hash() -> str:
@@ -135,6 +136,9 @@ def main():
 
     t_setup = time.time()
     name = args.workload
+    if name in W.LAYERNORM_WORKLOADS:
+        bench_layernorm(args, name, dev)
+        return
     wl = {**W.WORKLOADS, **W.BACKWARD_WORKLOADS, **W.FP8_WORKLOADS}[name]
     fp8 = name in W.FP8_WORKLOADS
     keep = []
@@ -404,6 +408,116 @@ def torch_context_fp8(specs, mm_kw, timed, steps, warmup, flops):
     return res
 
 
+def bench_layernorm(args, name, dev):
+    """The LayerNorm row kernel: one step = one launch over the whole
+    [rows, cols] input, inputs resident in HBM.  Memory-bound: value and
+    roofline in GB/s of algorithmic bytes (x read, y written, gamma and beta
+    read once).  The comparison path is the page's own multi-kernel form
+    (mean, centre, variance, rsqrt, scale and shift as separate torch ops)."""
+    import numpy as np
+    import torch
+
+    import dense_gemm_epilogue_fp16_amd as egm
+    import egm_workloads as W
+    wl = W.LAYERNORM_WORKLOADS[name]
+    t0 = time.time()
+    o = W.layernorm_operands(wl.m, wl.n, wl.dtype, seed=0)
+
+    def to_dev(bits, shape):
+        return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).reshape(shape).to(dev)
+
+    x, g, b = to_dev(o.x, (wl.m, wl.n)), to_dev(o.gamma, (wl.n,)), to_dev(o.beta, (wl.n,))
+    y = torch.empty_like(x)
+    if args.copy_mib:  # counter calibration, as for the GEMM workloads
+        src = torch.zeros(args.copy_mib << 20, dtype=torch.uint8, device=dev)
+        torch.bitwise_not(src, out=torch.empty_like(src))
+        del src
+    torch.cuda.synchronize(dev)
+    setup_s = time.time() - t0
+    stream = torch.cuda.current_stream(dev)
+
+    def fused():
+        egm.layer_norm(x, g, b, 1e-5, out=y)
+
+    def multi_kernel():  # the eager op sequence: each line its own kernel(s) and HBM round trip
+        mean = x.mean(dim=-1, keepdim=True)
+        xc = x - mean
+        var = (xc * xc).mean(dim=-1, keepdim=True)
+        return xc * torch.rsqrt(var + 1e-5) * g + b
+
+    def timed(fn, steps, warmup):
+        for _ in range(warmup):
+            fn()
+        torch.cuda.synchronize(dev)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        t = time.perf_counter()
+        e0.record(stream)
+        for _ in range(steps):
+            fn()
+        e1.record(stream)
+        torch.cuda.synchronize(dev)
+        return e0.elapsed_time(e1) / steps, time.perf_counter() - t
+
+    probe, _ = timed(fused, 1, 1)
+    warmup = args.warmup if args.warmup is not None else max(3, int(500.0 / max(probe, 1e-3)))
+    steps = args.steps if args.steps is not None else max(10, int(1000.0 / max(probe, 1e-3)))
+    for _ in range(warmup):
+        fused()
+    ms, wall = timed(fused, steps, 0)
+    unf = [timed(multi_kernel, steps, 1)[0], timed(multi_kernel, steps, 1)[0]]
+    fus = [ms, timed(fused, steps, 1)[0]]
+    alg = 2 * 2 * wl.m * wl.n + 2 * 2 * wl.n
+    gbs = alg / (ms * 1e-3) / 1e9
+    tb = traffic_from_profile(name)
+    result = {
+        "metric": "LayerNorm row kernel GB/s (algorithmic bytes: x read, y written once)",
+        "value": round(gbs, 1), "unit": "GB/s", "n_gpus": 1, "steps": steps, "warmup": warmup,
+        "ms_per_step": round(ms, 5), "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": wl.dtype, "data": "synthetic (seeded normal rows, resident in HBM)",
+        "config": {"workload": name, "rows": wl.m, "cols": wl.n, "eps": 1e-5, "affine": True,
+                   "statistics": "fp32, one pass (Welford merge)"},
+        "unfused_ms_per_step": round(sum(unf) / 2, 5),
+        "speedup_vs_unfused": round((sum(unf) / 2) / (sum(fus) / 2), 4),
+        "unfused_note": "torch eager: mean, centre, variance, rsqrt, scale, shift as separate kernels",
+        "bytes_fused_algorithmic": alg,
+        "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                     "frac": round(gbs / PEAK_HBM_GBS, 4), "traffic": tb,
+                     "kernel": f"layernorm_kernel {wl.m}x{wl.n}", "avg_launch_ms": round(ms, 5),
+                     "algorithmic_bytes_per_launch": alg},
+        "setup_s": round(setup_s, 1), "timed_wall_s": round(wall, 3),
+    }
+    if args.torch_context:
+        tl, _ = timed(lambda: torch.nn.functional.layer_norm(x, (wl.n,), g, b, 1e-5), steps, warmup)
+        result["torch_context"] = {"layer_norm_ms": round(tl, 5), "layer_norm_gbs": round(alg / (tl * 1e-3) / 1e9, 1),
+                                   "note": "torch.nn.functional.layer_norm (torch's own fused kernel)"}
+    if not args.no_cpu_baseline:
+        from oracle import egm_oracle as eo
+        try:
+            from threadpoolctl import threadpool_info
+            cores = max([i.get("num_threads", 1) for i in threadpool_info() if i.get("user_api") == "blas"] or [1])
+        except Exception:  # pragma: no cover
+            cores = len(os.sched_getaffinity(0))
+        count = min(wl.m, 2048)
+        secs = 0.0
+        while True:
+            rows = W.sample_rows(wl.m, count, seed=2)
+            t = time.perf_counter()
+            yr, _, _ = eo.layer_norm_reference(o.x[rows], wl.dtype, o.gamma, o.beta, 1e-5)
+            secs = time.perf_counter() - t
+            if secs > 0.5 * args.cpu_seconds or count >= wl.m:
+                break
+            count = min(wl.m, int(count * max(2.0, 0.6 * args.cpu_seconds / max(secs, 1e-3))))
+        sel = y.index_select(0, torch.from_numpy(rows).to(dev)).cpu()
+        d = eo.widen(sel.view(torch.int16).numpy().view(np.uint16), wl.dtype)
+        byts = 4.0 * len(rows) * wl.n
+        result["cpu_baseline"] = {"value": round(byts / secs / 1e9, 3), "unit": "GB/s", "cores": int(cores),
+                                  "kind": "oracle", "sample": f"{len(rows)} of {wl.m} rows x {wl.n}, fp64 numpy "
+                                  f"oracle; {secs:.1f} s", "seconds": round(secs, 2),
+                                  "parity_max_abs_err": float(np.abs(d - yr).max()),
+                                  "parity_tol": eo.TOLERANCE[wl.dtype]}
+    print(json.dumps(result), flush=True)
+
+
 def launch_amortisation(specs, mm_kw, nprob, dev, target_ms=400.0):
     """Per-GEMM time of nprob problems of the workload's shape (own A and D,
     shared B and bias): nprob executes launched one by one, the same executes
@@ -615,7 +729,7 @@ def ingest_pmc(workload, fetch_dir, write_dir, copy_mib):
     fetch = _pmc_per_kernel(fetch_dir, "FETCH_SIZE")
     write = _pmc_per_kernel(write_dir, "WRITE_SIZE")
     copy_k = [k for k in fetch if "bitwise_not" in k]
-    gemm_k = [k for k in fetch if "gemm_epilogue_kernel" in k]
+    gemm_k = [k for k in fetch if "gemm_epilogue_kernel" in k or "layernorm_kernel" in k]
     if not copy_k or not gemm_k:
         raise SystemExit(f"kernels not found: {sorted(fetch)}")
     copy_bytes = float(copy_mib << 20)
