@@ -132,6 +132,7 @@ def _load() -> ctypes.CDLL:
 
 
 LIB = _load()
+_EXECUTE = LIB.egm_execute
 
 
 # ---------------------------------------------------------------------------
@@ -339,6 +340,7 @@ class Matmul:
         if self.fp8 is None and a.dtype != b.dtype:
             raise TypeError("a and b must share one dtype (no implicit conversion)")
         self.a, self.b = a, b
+        self._dev = a.device.index if a.device.index is not None else torch.cuda.current_device()
         self.scale_a, self.scale_b = scale_a, scale_b
         self.m, self.k = a.shape
         self.n = b.shape[1]
@@ -441,30 +443,55 @@ class Matmul:
     def execute(self, a=None, b=None, out=None, aux=None, stream=None):
         import torch
         plan = self._require()
-        a = self.a if a is None else a
-        b = self.b if b is None else b
-        for t, shape, dt in ((a, (self.m, self.k), self.a.dtype), (b, (self.k, self.n), self.b.dtype)):
-            self._check_operand(t, "operand", fp8=self.fp8 is not None)
-            if tuple(t.shape) != shape or t.dtype != dt:
-                raise ValueError("rebound operand must keep the planned shape and dtype")
-        d = out if out is not None else torch.empty((self.m, self.n), dtype=self.dtype, device=a.device)
+        # the planned operands need no re-check; rebound ones keep shape and dtype
+        if a is None:
+            a = self.a
+        elif a is not self.a:
+            self._check_rebound(a, (self.m, self.k), self.a.dtype)
+        if b is None:
+            b = self.b
+        elif b is not self.b:
+            self._check_rebound(b, (self.k, self.n), self.b.dtype)
+        if out is None:
+            d = torch.empty((self.m, self.n), dtype=self.dtype, device=a.device)
+        else:
+            self._check_output(out, (self.m, self.n), self.dtype, "out")
+            d = out
         mask = None
         if self.epilog == "RELU_AUX_BIAS":
-            mask = aux if aux is not None else torch.empty((self.m, self.n // 8), dtype=torch.uint8, device=a.device)
+            if aux is None:
+                mask = torch.empty((self.m, self.n // 8), dtype=torch.uint8, device=a.device)
+            else:
+                self._check_output(aux, (self.m, self.n // 8), torch.uint8, "aux")
+                mask = aux
         elif self.epilog in BACKWARD_EPILOGS:
-            if aux is None or aux.dtype != torch.uint8 or tuple(aux.shape) != (self.m, self.n // 8) \
-                    or not aux.is_cuda or not aux.is_contiguous():
+            if aux is None:
                 raise ValueError("the backward epilogues take the forward mask: aux = uint8 [m, n/8] on the GPU")
+            self._check_output(aux, (self.m, self.n // 8), torch.uint8, "aux")
             mask = aux
-        s = stream if stream is not None else torch.cuda.current_stream(a.device)
+        elif aux is not None:
+            raise ValueError(f"{self.epilog} takes no mask")
+        raw = stream.cuda_stream if stream is not None else torch._C._cuda_getCurrentRawStream(self._dev)
         ws = self._ws
-        egm_execute(plan, a.data_ptr(), b.data_ptr(), d.data_ptr(), mask.data_ptr() if mask is not None else 0,
-                    ws.data_ptr() if ws is not None else 0, ws.numel() if ws is not None else 0, s.cuda_stream)
+        st = _EXECUTE(plan, a.data_ptr(), b.data_ptr(), d.data_ptr(), mask.data_ptr() if mask is not None else None,
+                      ws.data_ptr() if ws is not None else None, ws.numel() if ws is not None else 0, raw)
+        if st != EGM_OK:
+            raise EgmError(st, "egm_execute")
         if self.epilog == "DRELU_BGRAD":
             return d, self.bias_grad
         if self.epilog == "DRELU":
             return d
         return (d, mask) if mask is not None else d
+
+    def _check_rebound(self, t, shape, dtype):
+        self._check_operand(t, "operand", fp8=self.fp8 is not None)
+        if tuple(t.shape) != shape or t.dtype != dtype:
+            raise ValueError("rebound operand must keep the planned shape and dtype")
+
+    @staticmethod
+    def _check_output(t, shape, dtype, name):
+        if not t.is_cuda or t.dtype != dtype or tuple(t.shape) != shape or not t.is_contiguous():
+            raise ValueError(f"{name} must be a contiguous {dtype} GPU tensor of shape {shape}")
 
     def execute_batched(self, a, b, out=None, aux=None, stream=None):
         """One launch over a batch of problems of the planned shape: ``a`` is
@@ -496,15 +523,22 @@ class Matmul:
         if self.epilog == "BIAS_RESIDUAL" and self._res_batch < batch:
             raise ValueError(f"the residual bound at plan holds {self._res_batch} problems, the batch {batch}: it "
                              "advances with D and must be [batch, m, n]")
+        if out is not None:
+            self._check_output(out, (batch, self.m, self.n), self.dtype, "out")
         d = out if out is not None else torch.empty((batch, self.m, self.n), dtype=self.dtype, device=a.device)
         mask = None
         if self.epilog == "RELU_AUX_BIAS":
+            if aux is not None:
+                self._check_output(aux, (batch, self.m, self.n // 8), torch.uint8, "aux")
             mask = aux if aux is not None else torch.empty((batch, self.m, self.n // 8), dtype=torch.uint8,
                                                            device=a.device)
         elif self.epilog == "DRELU":
-            if aux is None or aux.dtype != torch.uint8 or tuple(aux.shape) != (batch, self.m, self.n // 8):
+            if aux is None:
                 raise ValueError("DRELU takes the forward masks: aux = uint8 [batch, m, n/8] on the GPU")
+            self._check_output(aux, (batch, self.m, self.n // 8), torch.uint8, "aux")
             mask = aux
+        elif aux is not None:
+            raise ValueError(f"{self.epilog} takes no mask")
         s = stream if stream is not None else torch.cuda.current_stream(a.device)
         egm_execute_strided(plan, batch, a.data_ptr(), strides[0], b.data_ptr(), strides[1], d.data_ptr(),
                             self.m * self.n, mask.data_ptr() if mask is not None else 0,

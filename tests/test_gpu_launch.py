@@ -165,3 +165,33 @@ def test_graph_capture_replays_match_eager():
         assert torch.equal(d_batch.view(torch.int16), want_batch.view(torch.int16)), rep
     for mm in (mm_aux, mm_unf, mm_bg, mm_f8, mm_b):
         mm.free()
+
+
+def test_binding_rejects_bad_output_buffers():
+    """Wrong-sized, wrong-typed or strided outputs are refused on the host:
+    the library cannot see buffer sizes, so a short buffer would be written
+    past its end."""
+    import torch
+    import dense_gemm_epilogue_fp16_amd as egm
+    a = torch.zeros((64, 32), dtype=torch.float16, device="cuda")
+    b = torch.zeros((32, 48), dtype=torch.float16, device="cuda")
+    bias = torch.zeros((1, 48), dtype=torch.float16, device="cuda")
+    with egm.Matmul(a, b) as mm:
+        mm.plan("RELU_AUX_BIAS", {"bias": bias})
+        for bad in (torch.empty((64, 40), dtype=torch.float16, device="cuda"),
+                    torch.empty((64, 48), dtype=torch.bfloat16, device="cuda"),
+                    torch.empty((48, 64), dtype=torch.float16, device="cuda").t()):
+            with pytest.raises(ValueError):
+                mm.execute(out=bad)
+        with pytest.raises(ValueError):
+            mm.execute(aux=torch.empty((64, 5), dtype=torch.uint8, device="cuda"))
+        with pytest.raises(ValueError):
+            mm.execute_batched(torch.zeros((2, 64, 32), dtype=torch.float16, device="cuda"), b,
+                               out=torch.empty((1, 64, 48), dtype=torch.float16, device="cuda"))
+        d, m = mm.execute()
+        torch.cuda.synchronize()
+        assert d.shape == (64, 48) and m.shape == (64, 6)
+    with egm.Matmul(a, b) as mm:
+        mm.plan("BIAS", {"bias": bias})
+        with pytest.raises(ValueError):
+            mm.execute(aux=torch.empty((64, 6), dtype=torch.uint8, device="cuda"))
