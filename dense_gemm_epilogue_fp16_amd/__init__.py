@@ -85,7 +85,7 @@ class EpilogInputs(ctypes.Structure):
 
 class PlanOptions(ctypes.Structure):
     _fields_ = [("fused", ctypes.c_int32), ("force_config", ctypes.c_int32),
-                ("autotune", ctypes.c_int32), ("group_m", ctypes.c_int32)]
+                ("autotune", ctypes.c_int32), ("group_m", ctypes.c_int32), ("b_transposed", ctypes.c_int32)]
 
 
 def _load() -> ctypes.CDLL:
@@ -149,11 +149,11 @@ def _check(status: int, where: str) -> None:
 
 def egm_plan(m: int, n: int, k: int, dtype: int, epilog: int, bias: int = 0, bias_layout: int = EGM_BIAS_NONE,
              residual: int = 0, *, bias_grad: int = 0, fused: int = 1, force_config: int = -1, autotune: int = 0,
-             group_m: int = 0, raw_status: bool = False):
+             group_m: int = 0, b_transposed: int = 0, raw_status: bool = False):
     """Returns the plan handle (int), or (status, handle) with ``raw_status``."""
     h = ctypes.c_void_p()
     ins = EpilogInputs(bias or None, bias_layout, residual or None, bias_grad or None)
-    opt = PlanOptions(fused, force_config, autotune, group_m)
+    opt = PlanOptions(fused, force_config, autotune, group_m, b_transposed)
     st = LIB.egm_plan(ctypes.byref(h), int(m), int(n), int(k), int(dtype), int(epilog), ctypes.byref(ins),
                       ctypes.byref(opt))
     if raw_status:
@@ -164,12 +164,13 @@ def egm_plan(m: int, n: int, k: int, dtype: int, epilog: int, bias: int = 0, bia
 
 def egm_plan_fp8(m: int, n: int, k: int, a_format: int, b_format: int, out_dtype: int, scale_a: int, scale_b: int,
                  epilog: int, bias: int = 0, bias_layout: int = EGM_BIAS_NONE, residual: int = 0, *, fused: int = 1,
-                 force_config: int = -1, autotune: int = 0, group_m: int = 0, raw_status: bool = False):
+                 force_config: int = -1, autotune: int = 0, group_m: int = 0, b_transposed: int = 0,
+                 raw_status: bool = False):
     """fp8 operands with per-tensor scales (device pointers to one fp32 each,
     0 = NULL = 1); returns the plan handle, or (status, handle) with ``raw_status``."""
     h = ctypes.c_void_p()
     ins = EpilogInputs(bias or None, bias_layout, residual or None, None)
-    opt = PlanOptions(fused, force_config, autotune, group_m)
+    opt = PlanOptions(fused, force_config, autotune, group_m, b_transposed)
     st = LIB.egm_plan_fp8(ctypes.byref(h), int(m), int(n), int(k), int(a_format), int(b_format), int(out_dtype),
                           scale_a or None, scale_b or None, int(epilog), ctypes.byref(ins), ctypes.byref(opt))
     if raw_status:
@@ -285,6 +286,13 @@ def _dtype_code(t) -> int:
     raise TypeError(f"dtype {dt} not supported: fp16 or bf16 only")
 
 
+def _is_transposed_view(t) -> bool:
+    """True for a 2-D tensor that is the transpose of a contiguous one
+    (strides (1, rows)), e.g. w.t() for a contiguous w; not for a tensor that
+    is also contiguous (a single row or column)."""
+    return t.dim() == 2 and not t.is_contiguous() and t.stride() == (1, t.shape[0])
+
+
 def _fp8_code(t):
     """egm_fp8_format_t of an fp8 tensor (OCP float8_e4m3fn / float8_e5m2), else None."""
     import torch
@@ -312,6 +320,10 @@ class Matmul:
     fp8: ``a`` and ``b`` of dtype float8_e4m3fn / float8_e5m2 (any pairing),
     ``scale_a`` / ``scale_b`` one-element float32 GPU tensors (None = 1),
     ``out_dtype`` fp16 or bf16 (default bf16) for D, the bias and the residual.
+
+    ``b`` may be a transposed view of a contiguous [n, k] tensor (``w.t()``,
+    a linear layer's weight): the plan then reads it in that layout, with no
+    copy (the ``b_transposed`` plan option).
     """
 
     def __init__(self, a, b, *, scale_a=None, scale_b=None, out_dtype=None):
@@ -333,8 +345,9 @@ class Matmul:
             if out_dtype is not None and out_dtype != a.dtype:
                 raise TypeError("16-bit operands produce their own dtype (no implicit conversion)")
             out_dtype = a.dtype
+        self.bt = _is_transposed_view(b)
         self._check_operand(a, "a", fp8=self.fp8 is not None)
-        self._check_operand(b, "b", fp8=self.fp8 is not None)
+        self._check_operand(b, "b", fp8=self.fp8 is not None, transposed=self.bt)
         if a.dim() != 2 or b.dim() != 2 or a.shape[1] != b.shape[0]:
             raise ValueError(f"shapes {tuple(a.shape)} and {tuple(b.shape)} do not multiply")
         if self.fp8 is None and a.dtype != b.dtype:
@@ -351,11 +364,14 @@ class Matmul:
         self.epilog = None
 
     @staticmethod
-    def _check_operand(t, name, fp8=False):
+    def _check_operand(t, name, fp8=False, transposed=False):
         if not t.is_cuda:
             raise ValueError(f"{name} must be a GPU tensor")
-        if not t.is_contiguous():
-            raise ValueError(f"{name} must be contiguous row-major")
+        if transposed:
+            if not _is_transposed_view(t):
+                raise ValueError(f"{name} must be a transposed view of a contiguous tensor, as planned")
+        elif not t.is_contiguous():
+            raise ValueError(f"{name} must be contiguous row-major (or, for b, a transposed contiguous tensor)")
         if fp8:
             if _fp8_code(t) is None:
                 raise TypeError(f"{name}: dtype {t.dtype} is not an fp8 operand type")
@@ -418,11 +434,12 @@ class Matmul:
             keep += [t for t in (self.scale_a, self.scale_b) if t is not None]
             self._plan = egm_plan_fp8(self.m, self.n, self.k, self.fp8[0], self.fp8[1], _dtype_code(self.dtype), sa,
                                       sb, EPILOGS[epilog], bias_ptr, layout, res_ptr, fused=int(fused),
-                                      force_config=force_config, autotune=int(autotune), group_m=group_m)
+                                      force_config=force_config, autotune=int(autotune), group_m=group_m,
+                                      b_transposed=int(self.bt))
         else:
             self._plan = egm_plan(self.m, self.n, self.k, _dtype_code(self.a), EPILOGS[epilog], bias_ptr, layout,
                                   res_ptr, bias_grad=grad_ptr, fused=int(fused), force_config=force_config,
-                                  autotune=int(autotune), group_m=group_m)
+                                  autotune=int(autotune), group_m=group_m, b_transposed=int(self.bt))
         self._keep = tuple(keep)
         self.epilog = epilog
         self._ws = None
@@ -451,7 +468,7 @@ class Matmul:
         if b is None:
             b = self.b
         elif b is not self.b:
-            self._check_rebound(b, (self.k, self.n), self.b.dtype)
+            self._check_rebound(b, (self.k, self.n), self.b.dtype, transposed=self.bt)
         if out is None:
             d = torch.empty((self.m, self.n), dtype=self.dtype, device=a.device)
         else:
@@ -483,8 +500,8 @@ class Matmul:
             return d
         return (d, mask) if mask is not None else d
 
-    def _check_rebound(self, t, shape, dtype):
-        self._check_operand(t, "operand", fp8=self.fp8 is not None)
+    def _check_rebound(self, t, shape, dtype, transposed=False):
+        self._check_operand(t, "operand", fp8=self.fp8 is not None, transposed=transposed)
         if tuple(t.shape) != shape or t.dtype != dtype:
             raise ValueError("rebound operand must keep the planned shape and dtype")
 
@@ -505,13 +522,18 @@ class Matmul:
         plan = self._require()
         batch = None
         strides = []
-        for t, shape, dt in ((a, (self.m, self.k), self.a.dtype), (b, (self.k, self.n), self.b.dtype)):
-            self._check_operand(t, "operand", fp8=self.fp8 is not None)
-            if t.dtype != dt:
-                raise ValueError("batched operands keep the planned dtype")
+        for t, shape, dt, tr in ((a, (self.m, self.k), self.a.dtype, False),
+                                 (b, (self.k, self.n), self.b.dtype, self.bt)):
+            if not t.is_cuda or t.dtype != dt:
+                raise ValueError("batched operands are GPU tensors of the planned dtype")
             if tuple(t.shape) == shape:
+                self._check_operand(t, "operand", fp8=self.fp8 is not None, transposed=tr)
                 strides.append(0)
             elif t.dim() == 3 and tuple(t.shape[1:]) == shape:
+                # each problem's matrix in the planned layout, problems back to back
+                want = (shape[0] * shape[1], 1, shape[0]) if tr else (shape[0] * shape[1], shape[1], 1)
+                if t.stride() != want:
+                    raise ValueError(f"batched operand strides {t.stride()} must be {want}")
                 if batch is not None and t.shape[0] != batch:
                     raise ValueError("batch sizes differ")
                 batch = t.shape[0]

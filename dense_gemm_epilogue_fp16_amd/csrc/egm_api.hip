@@ -94,6 +94,7 @@ struct egm_plan_s {
   int32_t f8;                // 0: 16-bit operands; 1 + fa + 2 fb: fp8 operands (formats of A, B)
   const float* scale_a;      // fp8: per-tensor scales (device, may be NULL)
   const float* scale_b;
+  int32_t b_transposed;      // B given as [N, K] row-major
 };
 
 namespace {
@@ -125,9 +126,10 @@ void describe(const egm_plan_s* p, char* buf, size_t len) {
   else
     snprintf(operands, sizeof(operands), "%s", p->dtype == EGM_F16 ? "fp16" : "bf16");
   snprintf(buf, len,
-           "egm m=%lld n=%lld k=%lld operands=%s dtype=%s epilog=%s bias=%s path=%s tile=%dx%d kslab=%d waves=%dx%d "
+           "egm m=%lld n=%lld k=%lld operands=%s%s dtype=%s epilog=%s bias=%s path=%s tile=%dx%d kslab=%d waves=%dx%d "
            "mfma=%s lds_ring=%d group_m=%d tiles=%lld workspace=%zu%s",
-           (long long)p->m, (long long)p->n, (long long)p->k, operands, p->dtype == EGM_F16 ? "fp16" : "bf16",
+           (long long)p->m, (long long)p->n, (long long)p->k, operands, p->b_transposed ? " b=[n,k]" : "",
+           p->dtype == EGM_F16 ? "fp16" : "bf16",
            epilog_name(p->epilog), p->bias_layout == EGM_BIAS_ROW ? "row(m,1)" : p->bias_layout == EGM_BIAS_COL ? "col(1,n)" : "none",
            p->fused ? "fused" : "unfused(gemm+epilogue)", c.bm, c.bn, p->f8 != 0 ? 2 * c.bk : c.bk, c.wm, c.wn,
            p->f8 != 0 ? "32x32x64" : "32x32x16", c.stages, effective_group_m(p, p->config),
@@ -173,7 +175,9 @@ hipError_t launch_plan(const egm_plan_s* p, int cfg, const void* A, const void* 
   const bool two_kernels = !p->fused && epi != egm::EPI_NONE;
   g.D = two_kernels ? ws : D;
   const int gemm_epi = two_kernels ? egm::EPI_NONE : epi;
-  GemmLaunch gl = p->f8 != 0 ? egm::gemm_launcher_fp8(dt, p->f8, gemm_epi, cfg) : egm::gemm_launcher(dt, gemm_epi, cfg);
+  const bool b_t = p->b_transposed != 0;
+  GemmLaunch gl = p->f8 != 0 ? egm::gemm_launcher_fp8(dt, p->f8, gemm_epi, cfg, b_t)
+                             : egm::gemm_launcher(dt, gemm_epi, cfg, b_t);
   if (gl == nullptr) return hipErrorInvalidValue;
   gl(grid, s, g);
   hipError_t err = hipGetLastError();
@@ -298,8 +302,10 @@ egm_status_t plan_impl(egm_plan_t* out, int64_t m, int64_t n, int64_t k, egm_dty
     }
   }
 
-  int32_t fused = 1, force = -1, tune = 0, group_m = 0;
+  int32_t fused = 1, force = -1, tune = 0, group_m = 0, b_transposed = 0;
   if (opt != nullptr) {
+    if (opt->b_transposed != 0 && opt->b_transposed != 1) return EGM_ERR_INVALID_VALUE;
+    b_transposed = opt->b_transposed;
     if (opt->fused != 0 && opt->fused != 1) return EGM_ERR_INVALID_VALUE;
     if (opt->force_config < -1 || opt->force_config >= kNumConfigs) return EGM_ERR_INVALID_VALUE;
     if (opt->autotune != 0 && opt->autotune != 1) return EGM_ERR_INVALID_VALUE;
@@ -326,6 +332,7 @@ egm_status_t plan_impl(egm_plan_t* out, int64_t m, int64_t n, int64_t k, egm_dty
   p->f8 = f8;
   p->scale_a = scale_a;
   p->scale_b = scale_b;
+  p->b_transposed = b_transposed;
   p->fused = fused;
   p->config = force >= 0 ? force : choose_config(m, n, k);
   // the grid is one workgroup per output tile and tile ids are 32-bit

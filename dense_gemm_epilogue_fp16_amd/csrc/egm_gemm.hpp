@@ -523,8 +523,11 @@ __device__ __forceinline__ void epilogue_store(const GemmArgs& p, f32x16 (&acc)[
 
 // DT: the output (and bias / residual) type, and the operand type when F8 is 0.
 // F8 = 1 + fa + 2 fb for fp8 operands (fa, fb: 0 E4M3, 1 E5M2 for A and B),
-// with C::ES == 1.
-template <int DT, int EPI, class C, int F8 = 0>
+// with C::ES == 1.  BT: B is given transposed, as [N, K] row-major (a linear
+// layer's weight); its tile then sits in LDS exactly like A's (K-contiguous
+// rows, the same swizzle, the same 16-byte fragment reads), so no
+// transposing read is needed.
+template <int DT, int EPI, class C, int F8 = 0, bool BT = false>
 __global__ void __launch_bounds__(C::NT, 1) gemm_epilogue_kernel(GemmArgs p) {
   static_assert((F8 == 0) == (C::ES == 2), "fp8 kernels use one-byte tiles");
   // the k-slab ring, then the tile's bias slice
@@ -550,13 +553,6 @@ __global__ void __launch_bounds__(C::NT, 1) gemm_epilogue_kernel(GemmArgs p) {
   const int m0 = tm * C::BM;
   const int n0 = tn * C::BN;
   const int KT = (K + C::BK - 1) / C::BK;
-  // fp8: the product of the two per-tensor scales (uniform; NULL reads as 1)
-  float scale = 1.0f;
-  if constexpr (F8 != 0) {
-    const float sa = p.scale_a != nullptr ? *p.scale_a : 1.0f;
-    const float sb = p.scale_b != nullptr ? *p.scale_b : 1.0f;
-    scale = sa * sb;
-  }
 
   // A (1,n) bias: wave 0 copies the tile's BN values straight into LDS ahead
   // of the operand loads (its completion is covered by the prologue's wait;
@@ -587,13 +583,23 @@ __global__ void __launch_bounds__(C::NT, 1) gemm_epilogue_kernel(GemmArgs p) {
   // q*R + L/B_CHUNKS, physical chunk L%B_CHUNKS holding logical chunk
   // (L%B_CHUNKS) ^ b_swz(k-row).  Columns past N read 0; k-rows past K fall
   // outside the slab's buffer range and read 0.
-  uint32_t b_off[C::B_PW];
+  // Transposed B: load q fills tile rows (n) R*q .. R*q+R-1 as A's loads do;
+  // rows past N fall outside the slab's buffer range, columns past K read 0.
+  uint32_t b_off[C::B_PW], b_k8[C::B_PW];
 #pragma unroll
   for (int u = 0; u < C::B_PW; ++u) {
     const uint32_t q = wave * C::B_PW + u;
-    const uint32_t krow = q * C::B_ROWS_PER_DMA + lane / C::B_CHUNKS;
-    const uint32_t lc = (lane % C::B_CHUNKS) ^ b_swz<C::B_CHUNKS, C::ES>(krow);
-    b_off[u] = (n0 + (int)lc * C::CE < N) ? (krow * (uint32_t)N + lc * C::CE) * C::ES : OOB_OFFSET;
+    if constexpr (BT) {
+      const uint32_t row = C::A_ROWS_PER_DMA * q + lane / C::A_CHUNKS;
+      const uint32_t lc = (lane % C::A_CHUNKS) ^ a_swz<C::A_CHUNKS>(row);
+      b_k8[u] = lc * C::CE;
+      b_off[u] = (row * (uint32_t)K + lc * C::CE) * C::ES;
+    } else {
+      const uint32_t krow = q * C::B_ROWS_PER_DMA + lane / C::B_CHUNKS;
+      const uint32_t lc = (lane % C::B_CHUNKS) ^ b_swz<C::B_CHUNKS, C::ES>(krow);
+      b_k8[u] = 0;
+      b_off[u] = (n0 + (int)lc * C::CE < N) ? (krow * (uint32_t)N + lc * C::CE) * C::ES : OOB_OFFSET;
+    }
   }
 
   // Buffer ranges of slab kt (uniform: computed once per slab): A from
@@ -610,9 +616,15 @@ __global__ void __launch_bounds__(C::NT, 1) gemm_epilogue_kernel(GemmArgs p) {
     const uint64_t a_start = (uint64_t)m0 * K + r.kbase, a_size = (uint64_t)M * K;
     r.a = make_srd((const uint8_t*)p.A + (a_start < a_size ? a_start : 0) * C::ES,
                    a_start < a_size && r.kbase < (uint32_t)K ? (a_size - a_start) * C::ES : 0);
-    const uint64_t b_start = (uint64_t)r.kbase * N + n0, b_size = (uint64_t)K * N;
-    r.b = make_srd((const uint8_t*)p.B + (b_start < b_size ? b_start : 0) * C::ES,
-                   b_start < b_size ? (b_size - b_start) * C::ES : 0);
+    if constexpr (BT) {
+      const uint64_t b_start = (uint64_t)n0 * K + r.kbase, b_size = (uint64_t)N * K;
+      r.b = make_srd((const uint8_t*)p.B + (b_start < b_size ? b_start : 0) * C::ES,
+                     b_start < b_size && r.kbase < (uint32_t)K ? (b_size - b_start) * C::ES : 0);
+    } else {
+      const uint64_t b_start = (uint64_t)r.kbase * N + n0, b_size = (uint64_t)K * N;
+      r.b = make_srd((const uint8_t*)p.B + (b_start < b_size ? b_start : 0) * C::ES,
+                     b_start < b_size ? (b_size - b_start) * C::ES : 0);
+    }
     return r;
   };
   // Load q (0 .. PW-1) of this wave for a slab into ring buffer `stage`: the
@@ -623,7 +635,8 @@ __global__ void __launch_bounds__(C::NT, 1) gemm_epilogue_kernel(GemmArgs p) {
       dma16(r.a, sa + (wave * C::A_PW + q) * 1024u, r.kbase + a_k8[q] < (uint32_t)K ? a_off[q] : OOB_OFFSET);
     } else {
       const int u = q - C::A_PW;
-      dma16(r.b, sa + C::A_BYTES + (wave * C::B_PW + u) * 1024u, b_off[u]);
+      dma16(r.b, sa + C::A_BYTES + (wave * C::B_PW + u) * 1024u,
+            !BT || r.kbase + b_k8[u] < (uint32_t)K ? b_off[u] : OOB_OFFSET);
     }
   };
 
@@ -677,6 +690,17 @@ __global__ void __launch_bounds__(C::NT, 1) gemm_epilogue_kernel(GemmArgs p) {
     const uint32_t col = wn0 + 32 * j + 16 * (g16 & 1) + 8 * (r16 & 1);
     b8_off[j] = C::A_BYTES + krow * C::B_ROW + (((col >> 4) ^ b_swz<C::B_CHUNKS, C::ES>(krow)) << 4) + (col & 8);
   }
+  // Transposed B: fragment j is tile row wn0 + 32j + lr of the B tile, read
+  // exactly like an A fragment (16-bit: logical chunk 2ks + lh; fp8: chunks
+  // 4ks + 2lh and 4ks + 2lh + 1).
+  uint32_t bt_off[C::NS][2];
+#pragma unroll
+  for (int ks = 0; ks < C::NS; ++ks)
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const uint32_t chunk = C::ES == 2 ? 2u * ks + lh : 4u * ks + 2u * lh + h;
+      bt_off[ks][h] = C::A_BYTES + (uint32_t)(wn0 + lr) * C::A_ROW + ((chunk ^ a_swz<C::A_CHUNKS>(lr)) << 4);
+    }
 
   f32x16 acc[C::FM][C::FN];
 #pragma unroll
@@ -694,10 +718,12 @@ __global__ void __launch_bounds__(C::NT, 1) gemm_epilogue_kernel(GemmArgs p) {
   // use by the MFMAs (i outer, j inner): A0, then B0 .. B(FN-1), then A1 ..
   // A(FM-1).
   constexpr int NMF = C::FM * C::FN;  // MFMAs per k-slice
-  constexpr int RA = C::ES == 2 ? 1 : 2, RB = C::ES == 2 ? 2 : 4;  // reads per A / B fragment
-  constexpr int NRD = RA * C::FM + RB * C::FN;                       // LDS read instructions per k-slice
+  constexpr int RA = C::ES == 2 ? 1 : 2;                   // reads per A fragment
+  constexpr int RB = BT ? RA : (C::ES == 2 ? 2 : 4);        // reads per B fragment
+  constexpr int NRD = RA * C::FM + RB * C::FN;              // LDS read instructions per k-slice
   u32x4 fa[2][C::FM][RA];
-  u32x2 fb[2][C::FN][RB];
+  u32x2 fb[2][C::FN][BT ? 1 : RB];
+  u32x4 fbt[2][C::FN][RA];  // transposed B: A-like 16-byte pieces
   auto read_piece = [&](int set, int stage, int ks, int piece) {
     const uint8_t* const st = smem + stage * C::STAGE_BYTES;
     if (piece < RA || piece >= RA + RB * C::FN) {
@@ -709,7 +735,9 @@ __global__ void __launch_bounds__(C::NT, 1) gemm_epilogue_kernel(GemmArgs p) {
         fa[set][i][h] = *(const u32x4*)(st + a8_off[ks][h] + i * 32 * C::A_ROW);
     } else {
       const int j = (piece - RA) / RB, t = (piece - RA) % RB;
-      if constexpr (C::ES == 2)
+      if constexpr (BT)
+        fbt[set][j][t] = *(const u32x4*)(st + bt_off[ks][t] + j * 32 * C::A_ROW);
+      else if constexpr (C::ES == 2)
         fb[set][j][t] = lds_read_tr<DT>(st + b_frag_off[t][j] + ks * 16 * C::B_ROW);
       else
         fb[set][j][t] = lds_read_tr8(st + b8_off[j] + (ks * 64 + 8 * t) * C::B_ROW);
@@ -724,7 +752,16 @@ __global__ void __launch_bounds__(C::NT, 1) gemm_epilogue_kernel(GemmArgs p) {
     for (int i = 0; i < C::FM; ++i)
 #pragma unroll
       for (int j = 0; j < C::FN; ++j) {
-        if constexpr (C::ES == 2) {
+        if constexpr (BT && C::ES == 2) {
+          acc[i][j] = mfma32<DT>(fbt[set][j][0], fa[set][i][0], acc[i][j]);
+        } else if constexpr (BT) {
+          constexpr int FA = (F8 - 1) & 1, FB = (F8 - 1) >> 1;
+          const u32x8 b8{fbt[set][j][0][0], fbt[set][j][0][1], fbt[set][j][0][2], fbt[set][j][0][3],
+                         fbt[set][j][1][0], fbt[set][j][1][1], fbt[set][j][1][2], fbt[set][j][1][3]};
+          const u32x8 a8{fa[set][i][0][0], fa[set][i][0][1], fa[set][i][0][2], fa[set][i][0][3],
+                         fa[set][i][1][0], fa[set][i][1][1], fa[set][i][1][2], fa[set][i][1][3]};
+          acc[i][j] = mfma32_f8<FB, FA>(b8, a8, acc[i][j]);
+        } else if constexpr (C::ES == 2) {
           acc[i][j] = mfma32<DT>(u32x4{fb[set][j][0][0], fb[set][j][0][1], fb[set][j][1][0], fb[set][j][1][1]},
                                  fa[set][i][0], acc[i][j]);
         } else {
@@ -818,6 +855,14 @@ __global__ void __launch_bounds__(C::NT, 1) gemm_epilogue_kernel(GemmArgs p) {
     }
   }
 
+  // fp8: the product of the two per-tensor scales (uniform; NULL reads as 1),
+  // loaded only now so that no register holds it through the main loop
+  float scale = 1.0f;
+  if constexpr (F8 != 0) {
+    const float sa = p.scale_a != nullptr ? *p.scale_a : 1.0f;
+    const float sb = p.scale_b != nullptr ? *p.scale_b : 1.0f;
+    scale = sa * sb;
+  }
   // drain: no load may still be writing LDS when the workgroup retires
   wait_vmcnt<0>();
   // the ring is free once every wave is past its last fragment read

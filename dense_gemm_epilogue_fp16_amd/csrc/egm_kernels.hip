@@ -23,11 +23,11 @@ constexpr int DT = EGM_DTYPE;
 constexpr int F8 = EGM_F8;
 constexpr int ES = F8 == 0 ? 2 : 1;
 
-template <int EPI, int CFG>
+template <int EPI, int CFG, bool BT>
 void launch_gemm(dim3 grid, hipStream_t s, const GemmArgs& a) {
   constexpr ConfigInfo ci = kConfigs[CFG];
   using C = TileCfg<ci.bm, ci.bn, ci.stages, ci.wm, ci.wn, ci.bk * (2 / ES), ES>;
-  hipLaunchKernelGGL((gemm_epilogue_kernel<DT, EPI, C, F8>), grid, dim3(C::NT), 0, s, a);
+  hipLaunchKernelGGL((gemm_epilogue_kernel<DT, EPI, C, F8, BT>), grid, dim3(C::NT), 0, s, a);
 }
 
 #if EGM_F8 == 0
@@ -62,34 +62,37 @@ LnLaunch ln_row(int cfg) {
 }
 #endif
 
-template <int EPI>
+template <int EPI, bool BT>
 GemmLaunch gemm_row(int cfg) {
   static_assert(kNumConfigs == 5, "update the launch table with the config table");
   switch (cfg) {
-    case 0: return &launch_gemm<EPI, 0>;
-    case 1: return &launch_gemm<EPI, 1>;
-    case 2: return &launch_gemm<EPI, 2>;
-    case 3: return &launch_gemm<EPI, 3>;
-    case 4: return &launch_gemm<EPI, 4>;
+    case 0: return &launch_gemm<EPI, 0, BT>;
+    case 1: return &launch_gemm<EPI, 1, BT>;
+    case 2: return &launch_gemm<EPI, 2, BT>;
+    case 3: return &launch_gemm<EPI, 3, BT>;
+    case 4: return &launch_gemm<EPI, 4, BT>;
     default: return nullptr;
   }
 }
 
-GemmLaunch gemm_table(int epi, int cfg) {
+template <bool BT>
+GemmLaunch gemm_table_bt(int epi, int cfg) {
   switch (epi) {
-    case EPI_NONE: return gemm_row<EPI_NONE>(cfg);
-    case EPI_BIAS: return gemm_row<EPI_BIAS>(cfg);
-    case EPI_RELU: return gemm_row<EPI_RELU>(cfg);
-    case EPI_GELU: return gemm_row<EPI_GELU>(cfg);
-    case EPI_RELU_AUX: return gemm_row<EPI_RELU_AUX>(cfg);
-    case EPI_RESID: return gemm_row<EPI_RESID>(cfg);
+    case EPI_NONE: return gemm_row<EPI_NONE, BT>(cfg);
+    case EPI_BIAS: return gemm_row<EPI_BIAS, BT>(cfg);
+    case EPI_RELU: return gemm_row<EPI_RELU, BT>(cfg);
+    case EPI_GELU: return gemm_row<EPI_GELU, BT>(cfg);
+    case EPI_RELU_AUX: return gemm_row<EPI_RELU_AUX, BT>(cfg);
+    case EPI_RESID: return gemm_row<EPI_RESID, BT>(cfg);
 #if EGM_F8 == 0
-    case EPI_DRELU: return gemm_row<EPI_DRELU>(cfg);
-    case EPI_DRELU_BGRAD: return gemm_row<EPI_DRELU_BGRAD>(cfg);
+    case EPI_DRELU: return gemm_row<EPI_DRELU, BT>(cfg);
+    case EPI_DRELU_BGRAD: return gemm_row<EPI_DRELU_BGRAD, BT>(cfg);
 #endif
     default: return nullptr;
   }
 }
+
+GemmLaunch gemm_table(int epi, int cfg, bool bt) { return bt ? gemm_table_bt<true>(epi, cfg) : gemm_table_bt<false>(epi, cfg); }
 
 #if EGM_F8 == 0
 EpiLaunch epi_table(int epi) {
@@ -110,10 +113,10 @@ EpiLaunch epi_table(int epi) {
 #if EGM_F8 != 0
 #define EGM_CAT3(a, b, c) a##b##_##c
 #define EGM_FP8_LAUNCHER(dt, f8) EGM_CAT3(gemm_launcher_fp8_, dt, f8)
-GemmLaunch EGM_FP8_LAUNCHER(EGM_DTYPE, EGM_F8)(int epi, int cfg) { return gemm_table(epi, cfg); }
+GemmLaunch EGM_FP8_LAUNCHER(EGM_DTYPE, EGM_F8)(int epi, int cfg, bool bt) { return gemm_table(epi, cfg, bt); }
 #elif EGM_DTYPE == 0
 LnLaunch layernorm_launcher_f16(int cfg, bool residual) { return residual ? ln_row<true>(cfg) : ln_row<false>(cfg); }
-GemmLaunch gemm_launcher_f16(int epi, int cfg) { return gemm_table(epi, cfg); }
+GemmLaunch gemm_launcher_f16(int epi, int cfg, bool bt) { return gemm_table(epi, cfg, bt); }
 EpiLaunch epi_launcher_f16(int epi) { return epi_table(epi); }
 PartialsLaunch partials_launcher_f16() { return &launch_partials; }
 void launch_bias_grad_finish(dim3 grid, hipStream_t s, const float* partial, int64_t chunks, int64_t len,
@@ -122,7 +125,7 @@ void launch_bias_grad_finish(dim3 grid, hipStream_t s, const float* partial, int
 }
 #else
 LnLaunch layernorm_launcher_bf16(int cfg, bool residual) { return residual ? ln_row<true>(cfg) : ln_row<false>(cfg); }
-GemmLaunch gemm_launcher_bf16(int epi, int cfg) { return gemm_table(epi, cfg); }
+GemmLaunch gemm_launcher_bf16(int epi, int cfg, bool bt) { return gemm_table(epi, cfg, bt); }
 EpiLaunch epi_launcher_bf16(int epi) { return epi_table(epi); }
 PartialsLaunch partials_launcher_bf16() { return &launch_partials; }
 #endif

@@ -54,8 +54,9 @@ using PartialsLaunch = void (*)(dim3 grid, hipStream_t stream, const void* D, in
                                 int32_t layout, float* partial);
 
 // Defined in egm_kernels.hip (compiled once per dtype).
-GemmLaunch gemm_launcher_f16(int epi, int cfg);
-GemmLaunch gemm_launcher_bf16(int epi, int cfg);
+// bt: B given transposed ([N, K] row-major)
+GemmLaunch gemm_launcher_f16(int epi, int cfg, bool bt);
+GemmLaunch gemm_launcher_bf16(int epi, int cfg, bool bt);
 EpiLaunch epi_launcher_f16(int epi);
 EpiLaunch epi_launcher_bf16(int epi);
 PartialsLaunch partials_launcher_f16();
@@ -67,26 +68,26 @@ void launch_bias_grad_finish(dim3 grid, hipStream_t stream, const float* partial
 // fp8 operands (defined in egm_kernels.hip built with -DEGM_F8): one table per
 // (output dtype 0 fp16 / 1 bf16, format pair f8 = 1 + fa + 2 fb); forward
 // epilogues only (nullptr otherwise)
-GemmLaunch gemm_launcher_fp8_0_1(int epi, int cfg);
-GemmLaunch gemm_launcher_fp8_0_2(int epi, int cfg);
-GemmLaunch gemm_launcher_fp8_0_3(int epi, int cfg);
-GemmLaunch gemm_launcher_fp8_0_4(int epi, int cfg);
-GemmLaunch gemm_launcher_fp8_1_1(int epi, int cfg);
-GemmLaunch gemm_launcher_fp8_1_2(int epi, int cfg);
-GemmLaunch gemm_launcher_fp8_1_3(int epi, int cfg);
-GemmLaunch gemm_launcher_fp8_1_4(int epi, int cfg);
+GemmLaunch gemm_launcher_fp8_0_1(int epi, int cfg, bool bt);
+GemmLaunch gemm_launcher_fp8_0_2(int epi, int cfg, bool bt);
+GemmLaunch gemm_launcher_fp8_0_3(int epi, int cfg, bool bt);
+GemmLaunch gemm_launcher_fp8_0_4(int epi, int cfg, bool bt);
+GemmLaunch gemm_launcher_fp8_1_1(int epi, int cfg, bool bt);
+GemmLaunch gemm_launcher_fp8_1_2(int epi, int cfg, bool bt);
+GemmLaunch gemm_launcher_fp8_1_3(int epi, int cfg, bool bt);
+GemmLaunch gemm_launcher_fp8_1_4(int epi, int cfg, bool bt);
 
-inline GemmLaunch gemm_launcher_fp8(int dt, int f8, int epi, int cfg) {
-  using Table = GemmLaunch (*)(int, int);
+inline GemmLaunch gemm_launcher_fp8(int dt, int f8, int epi, int cfg, bool bt) {
+  using Table = GemmLaunch (*)(int, int, bool);
   static constexpr Table tables[2][4] = {
       {&gemm_launcher_fp8_0_1, &gemm_launcher_fp8_0_2, &gemm_launcher_fp8_0_3, &gemm_launcher_fp8_0_4},
       {&gemm_launcher_fp8_1_1, &gemm_launcher_fp8_1_2, &gemm_launcher_fp8_1_3, &gemm_launcher_fp8_1_4}};
   if ((dt != DT_F16 && dt != DT_BF16) || f8 < 1 || f8 > 4) return nullptr;
-  return tables[dt == DT_F16 ? 0 : 1][f8 - 1](epi, cfg);
+  return tables[dt == DT_F16 ? 0 : 1][f8 - 1](epi, cfg, bt);
 }
 
-inline GemmLaunch gemm_launcher(int dt, int epi, int cfg) {
-  return dt == DT_F16 ? gemm_launcher_f16(epi, cfg) : gemm_launcher_bf16(epi, cfg);
+inline GemmLaunch gemm_launcher(int dt, int epi, int cfg, bool bt) {
+  return dt == DT_F16 ? gemm_launcher_f16(epi, cfg, bt) : gemm_launcher_bf16(epi, cfg, bt);
 }
 inline EpiLaunch epi_launcher(int dt, int epi) { return dt == DT_F16 ? epi_launcher_f16(epi) : epi_launcher_bf16(epi); }
 inline PartialsLaunch partials_launcher(int dt) { return dt == DT_F16 ? partials_launcher_f16() : partials_launcher_bf16(); }

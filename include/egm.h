@@ -50,7 +50,7 @@
 extern "C" {
 #endif
 
-#define EGM_ABI_VERSION 5
+#define EGM_ABI_VERSION 6
 
 typedef enum egm_status_t {
   EGM_OK = 0,
@@ -145,6 +145,11 @@ typedef struct egm_plan_options_t {
                             thread-safe) */
   int32_t group_m;       /* 0 (default): per-shape choice; else tile rows per
                             L2-sharing group in the workgroup order */
+  int32_t b_transposed;  /* 0 (default): B is [k,n] row-major.  1: B is given
+                            transposed, as [n,k] row-major (B^T; the layout of
+                            a linear layer's [out, in] weight), which the
+                            kernel streams like A.  Strided batches advance B
+                            by stride_b elements either way. */
 } egm_plan_options_t;
 
 typedef struct egm_plan_s* egm_plan_t;
@@ -195,7 +200,8 @@ egm_status_t egm_plan_fp8(egm_plan_t* out, int64_t m, int64_t n, int64_t k, egm_
 
 /*
  * egm_execute - enqueue the plan on a HIP stream (asynchronous).
- *   A     [m,k] device, row-major.          B [k,n] device, row-major.
+ *   A     [m,k] device, row-major.          B [k,n] device, row-major ([n,k] row-major
+ *         with the b_transposed option).
  *   D     [m,n] device, row-major output.
  *   aux   [m, n/8] uint8 device mask: the OUTPUT of RELU_AUX_BIAS and the INPUT
  *         of DRELU / DRELU_BGRAD; required for those three, else NULL.

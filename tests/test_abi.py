@@ -32,7 +32,7 @@ def test_every_declared_symbol_is_exported():
 
 
 def test_abi_version_and_status_strings():
-    assert egm.egm_abi_version() == 5
+    assert egm.egm_abi_version() == 6
     for s in range(10):
         assert egm.status_string(s).startswith("EGM_")
     assert "unknown" in egm.status_string(12345)
@@ -342,3 +342,17 @@ def test_layernorm_validation_before_any_hip_call():
     assert st(residual=FAKE + 8) == egm.EGM_ERR_ALIGNMENT
     assert st(mean=FAKE + 2) == egm.EGM_ERR_ALIGNMENT
     assert st(rows=0) == egm.EGM_OK                  # nothing to do, no HIP call
+
+
+def test_b_transposed_option():
+    h = egm.egm_plan(256, 512, 1024, BF16, E["BIAS"], FAKE, COL, b_transposed=1)
+    try:
+        assert " b=[n,k]" in egm.egm_plan_describe(h)
+    finally:
+        egm.egm_free(h)
+    st, h = egm.egm_plan(256, 512, 1024, BF16, E["BIAS"], FAKE, COL, b_transposed=2, raw_status=True)
+    assert st == egm.EGM_ERR_INVALID_VALUE and h is None
+    st, h = egm.egm_plan_fp8(64, 64, 64, egm.EGM_E4M3, egm.EGM_E5M2, BF16, 0, 0, E["DEFAULT"], b_transposed=1,
+                             raw_status=True)
+    assert st == egm.EGM_OK
+    egm.egm_free(h)
