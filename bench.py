@@ -726,17 +726,30 @@ def ingest_pmc(workload, fetch_dir, write_dir, copy_mib):
     calibration pass over copy_mib MiB (an elementwise bitwise-not, which
     reads and writes exactly that many bytes; host-to-device copies of the
     inputs use other kernels)."""
+    import re
+
+    import egm_workloads as W
     fetch = _pmc_per_kernel(fetch_dir, "FETCH_SIZE")
     write = _pmc_per_kernel(write_dir, "WRITE_SIZE")
     copy_k = [k for k in fetch if "bitwise_not" in k]
-    gemm_k = [k for k in fetch if "gemm_epilogue_kernel" in k or "layernorm_kernel" in k]
+    if workload in W.LAYERNORM_WORKLOADS:
+        gemm_k = [k for k in fetch if "layernorm_kernel" in k]
+    else:
+        # the dominant fused kernel bench.py reports: the workload's first GEMM
+        # (the FFN's up-projection) with its last epilog, never the first
+        # kernel of the two-kernel path (epilog id 0)
+        wl = {**W.WORKLOADS, **W.BACKWARD_WORKLOADS, **W.FP8_WORKLOADS}[workload]
+        ids = {"BIAS": 1, "RELU_BIAS": 2, "GELU_BIAS": 3, "RELU_AUX_BIAS": 4, "BIAS_RESIDUAL": 5, "DRELU": 6,
+               "DRELU_BGRAD": 7}
+        epi = ids[wl.epilogs[0] if workload.startswith("ffn_") else wl.epilogs[-1]]
+        gemm_k = [k for k in fetch if re.search(rf"gemm_epilogue_kernel<\d+, {epi},", k)]
     if not copy_k or not gemm_k:
         raise SystemExit(f"kernels not found: {sorted(fetch)}")
     copy_bytes = float(copy_mib << 20)
     ck = max(copy_k, key=lambda k: fetch[k])
     f_scale = copy_bytes / (fetch[ck] * 1024.0)
     w_scale = copy_bytes / (write[ck] * 1024.0)
-    gk = max(gemm_k, key=lambda k: fetch[k])
+    gk = max(gemm_k, key=lambda k: fetch[k])  # one kernel name per workload in practice
     out = {"workload": workload, "kernel": gk, "kernel_source_hash": kernel_source_hash(),
            "fetch_kib_per_launch": fetch[gk], "write_kib_per_launch": write.get(gk),
            "copy_kernel": ck, "copy_bytes": copy_bytes, "copy_fetch_kib": fetch[ck], "copy_write_kib": write[ck],
