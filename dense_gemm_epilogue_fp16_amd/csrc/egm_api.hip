@@ -53,17 +53,26 @@ const char* epilog_name(int e) {
 
 int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
-// Per-shape choice: the config with the smallest estimated time, counting
-// whole waves of tiles over the 256 CUs, scaled by the config's relative
-// efficiency.  Ties go to the larger tile (lower id).
+// A launch of config c is one workgroup per output tile along grid.x, and a
+// grid dimension holds at most 2^32 - 1 work-items (workgroups x threads).
+bool grid_fits(int64_t m, int64_t n, int c) {
+  const int64_t tiles = cdiv(m, kConfigs[c].bm) * cdiv(n, kConfigs[c].bn);
+  return tiles * 64 * kConfigs[c].wm * kConfigs[c].wn <= int64_t(0xffffffff);
+}
+
+// Per-shape choice: among the configs whose grid fits, the one with the
+// smallest estimated time, counting whole waves of tiles over the 256 CUs,
+// scaled by the config's relative efficiency.  Ties go to the larger tile
+// (lower id).  -1 when no config fits.
 int choose_config(int64_t m, int64_t n, int64_t k) {
-  int best = 0;
+  int best = -1;
   double best_t = 0;
   for (int c = 0; c < kNumConfigs; ++c) {
+    if (!grid_fits(m, n, c)) continue;
     const int64_t tiles = cdiv(m, kConfigs[c].bm) * cdiv(n, kConfigs[c].bn);
     const int64_t waves = cdiv(tiles, kNumCUs);
     const double t = double(waves) * kConfigs[c].bm * kConfigs[c].bn * double(k > 0 ? k : 1) / kConfigs[c].rel_eff;
-    if (c == 0 || t < best_t * 0.999) {
+    if (best < 0 || t < best_t * 0.999) {
       best = c;
       best_t = t;
     }
@@ -233,6 +242,7 @@ hipError_t autotune(egm_plan_s* p, const void* A, const void* B, void* D, void* 
   float best = -1.0f;
   int best_cfg = p->config;
   for (int c = 0; c < kNumConfigs && err == hipSuccess; ++c) {
+    if (!grid_fits(p->m, p->n, c)) continue;
     err = launch_plan(p, c, A, B, D, aux, ws, s);
     if (err != hipSuccess) break;
     err = hipEventRecord(e0, s);
@@ -335,12 +345,11 @@ egm_status_t plan_impl(egm_plan_t* out, int64_t m, int64_t n, int64_t k, egm_dty
   p->b_transposed = b_transposed;
   p->fused = fused;
   p->config = force >= 0 ? force : choose_config(m, n, k);
-  // the grid is one workgroup per output tile and tile ids are 32-bit
-  for (int c = 0; c < kNumConfigs; ++c) {
-    if (cdiv(m, kConfigs[c].bm) * cdiv(n, kConfigs[c].bn) > int64_t(0x7fffffff)) {
-      delete p;
-      return EGM_ERR_NOT_SUPPORTED;
-    }
+  // the launch must fit one grid dimension (autotuning tries only the
+  // configs that fit, and the per-shape choice always fits)
+  if (p->config < 0 || !grid_fits(m, n, p->config)) {
+    delete p;
+    return EGM_ERR_NOT_SUPPORTED;
   }
   p->group_m = group_m;
   p->autotune_pending = tune;
@@ -351,7 +360,7 @@ egm_status_t plan_impl(egm_plan_t* out, int64_t m, int64_t n, int64_t k, egm_dty
   p->grad_len = epilog == EGM_EPILOG_DRELU_BGRAD ? (layout == EGM_BIAS_COL ? n : m) : 0;
   int64_t max_chunks = 0;
   for (int c = 0; c < kNumConfigs; ++c) {
-    if (tune || c == p->config) {
+    if ((tune && grid_fits(m, n, c)) || c == p->config) {
       const int64_t ch = grad_chunks(p, c);
       if (ch > max_chunks) max_chunks = ch;
     }
@@ -525,6 +534,10 @@ egm_status_t egm_layernorm(int64_t rows, int64_t cols, egm_dtype_t dtype, const 
     return EGM_ERR_ALIGNMENT;
   int cfg = 0;
   while (int64_t(egm::kLnConfigs[cfg].tpr) * egm::kLnConfigs[cfg].cpt * 8 < cols) ++cfg;
+  // one grid dimension of 256-thread workgroups: at most 2^32 - 1 work-items
+  const int64_t rows_per_wg = 256 / egm::kLnConfigs[cfg].tpr;
+  const int64_t wgs = cdiv(rows, rows_per_wg);
+  if (wgs * 256 > int64_t(0xffffffff)) return EGM_ERR_NOT_SUPPORTED;
   const egm::LnLaunch launch = dtype == EGM_F16 ? egm::layernorm_launcher_f16(cfg, residual != nullptr)
                                                 : egm::layernorm_launcher_bf16(cfg, residual != nullptr);
   if (launch == nullptr) return EGM_ERR_NOT_SUPPORTED;
@@ -539,9 +552,6 @@ egm_status_t egm_layernorm(int64_t rows, int64_t cols, egm_dtype_t dtype, const 
   a.M = rows;
   a.N = int32_t(cols);
   a.eps = eps;
-  const int64_t rows_per_wg = 256 / egm::kLnConfigs[cfg].tpr;
-  const int64_t wgs = cdiv(rows, rows_per_wg);
-  if (wgs > int64_t(0x7fffffff)) return EGM_ERR_SHAPE;
   launch(dim3(uint32_t(wgs)), reinterpret_cast<hipStream_t>(stream), a);
   return hipGetLastError() == hipSuccess ? EGM_OK : EGM_ERR_HIP;
 }

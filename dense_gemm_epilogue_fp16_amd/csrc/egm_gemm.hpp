@@ -377,9 +377,11 @@ __device__ __forceinline__ void epilogue_store(const GemmArgs& p, f32x16 (&acc)[
     float brow = 0.0f;
     if constexpr (epi_adds_bias(EPI)) {
       if (p.bias_layout == BIAS_ROW) {
-        const auto rbias = make_rsrc(p.bias, (uint64_t)M * 2);
-        const int row = m0 + (int)lrow;
-        brow = to_f32<DT>(buf_load2(rbias, row < M ? (uint32_t)row * 2u : OOB_OFFSET));
+        // range based at the tile's first row: byte offsets stay below 512
+        // whatever M is (a range from bias[0] would cap near 2^31 bytes),
+        // and rows past M fall outside it and read as 0
+        const auto rbias = make_rsrc((const uint8_t*)p.bias + (size_t)m0 * 2, (uint64_t)(M - m0) * 2);
+        brow = to_f32<DT>(buf_load2(rbias, lrow * 2u));
       }
     }
 #pragma unroll

@@ -166,6 +166,11 @@ typedef struct egm_plan_s* egm_plan_t;
  *           and the backward epilogues need n % 8 == 0 (already required) for
  *           whole mask bytes.
  *   opt     NULL for defaults.
+ * A launch is one workgroup per output tile in one grid dimension, which holds
+ * at most 2^32 - 1 work-items: the per-shape choice and autotuning consider
+ * only the configs whose grid fits (for very tall, narrow problems that
+ * excludes the small tiles), and a forced config whose grid does not fit, or
+ * a shape no config fits, gives EGM_ERR_NOT_SUPPORTED.
  * No device work and no HIP call.
  */
 egm_status_t egm_plan(egm_plan_t* out, int64_t m, int64_t n, int64_t k, egm_dtype_t dtype,
@@ -254,6 +259,11 @@ egm_status_t egm_execute_strided(egm_plan_t plan, int64_t batch, const void* A, 
  *   y            [rows, cols] output; may be x itself (in place).
  *   mean, rstd   [rows] fp32 outputs (1 / sqrt(var + eps)), or NULL.
  *   cols a multiple of 8, 8 <= cols <= 32768; rows >= 0 (0 does nothing).
+ *   The launch is one grid dimension of 256-thread workgroups, each covering
+ *   256 / tpr rows (tpr = 64 threads per row up to 4096 columns, else 256);
+ *   a grid dimension holds at most 2^32 - 1 work-items, so rows above
+ *   4 * (2^24 - 1) (cols <= 4096) or 2^24 - 1 (wider rows) give
+ *   EGM_ERR_NOT_SUPPORTED.
  * Device pointers 16-byte aligned (mean, rstd 4-byte).  One launch on the
  * stream, asynchronous; no workspace.  Does not need a plan.
  */

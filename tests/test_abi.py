@@ -187,6 +187,49 @@ def test_per_shape_choice(m, n, k, cfg):
         egm.egm_free(h)
 
 
+def grid_work_items(m, n, cfg):
+    d = dict(kv.split("=") for kv in egm.egm_config_describe(cfg).split())
+    bm, bn = (int(x) for x in d["tile"].split("x"))
+    wm, wn = (int(x) for x in d["waves"].split("x"))
+    return -(-m // bm) * -(-n // bn) * 64 * wm * wn
+
+
+def test_grid_limit_narrows_the_choice():
+    # one workgroup per tile in one grid dimension, at most 2^32 - 1
+    # work-items: for m = 2^31 - 1, n = 8 only the 256x128 tile (4 waves)
+    # fits; every 128- or 64-row tile and the 8-wave 256x256 tile would not
+    m = (1 << 31) - 1
+    fits = [c for c in range(egm.egm_num_configs()) if grid_work_items(m, 8, c) <= 0xFFFFFFFF]
+    assert fits == [1]
+    for kw in (dict(), dict(autotune=1)):
+        h = egm.egm_plan(m, 8, 8, F16, E["BIAS"], FAKE, ROW, **kw)
+        try:
+            assert egm.egm_plan_config(h) == 1
+        finally:
+            egm.egm_free(h)
+    for c in range(egm.egm_num_configs()):
+        assert plan_status(m=m, n=8, k=8, force_config=c) == (egm.EGM_OK if c in fits else egm.EGM_ERR_NOT_SUPPORTED)
+    # just over 2^30 rows (the parity test's shape): the small tiles drop out
+    m = (1 << 30) + 200
+    h = egm.egm_plan(m, 8, 8, F16, E["BIAS"], FAKE, ROW)
+    try:
+        c = egm.egm_plan_config(h)
+        assert grid_work_items(m, 8, c) <= 0xFFFFFFFF
+        assert grid_work_items(m, 8, 4) > 0xFFFFFFFF
+    finally:
+        egm.egm_free(h)
+    # no config fits at all
+    assert plan_status(m=(1 << 31) - 1, n=1 << 21, k=8) == egm.EGM_ERR_NOT_SUPPORTED
+    # the workspace of a DRELU_BGRAD autotune plan covers only configs that fit
+    st, h = egm.egm_plan((1 << 31) - 1, 8, 8, F16, E["DRELU_BGRAD"], 0, COL, bias_grad=FAKE, autotune=1,
+                         raw_status=True)
+    assert st == egm.EGM_OK
+    try:
+        assert egm.egm_plan_workspace_bytes(h) == -(-((1 << 31) - 1) // 256) * 8 * 4
+    finally:
+        egm.egm_free(h)
+
+
 def test_config_table():
     n = egm.egm_num_configs()
     assert n == 5
@@ -342,6 +385,10 @@ def test_layernorm_validation_before_any_hip_call():
     assert st(residual=FAKE + 8) == egm.EGM_ERR_ALIGNMENT
     assert st(mean=FAKE + 2) == egm.EGM_ERR_ALIGNMENT
     assert st(rows=0) == egm.EGM_OK                  # nothing to do, no HIP call
+    # one grid dimension of 256-thread workgroups (2^32 - 1 work-items): 4
+    # rows per workgroup up to 4096 columns, 1 beyond
+    assert st(rows=4 * ((1 << 24) - 1) + 1, cols=4096) == egm.EGM_ERR_NOT_SUPPORTED
+    assert st(rows=(1 << 24), cols=4104) == egm.EGM_ERR_NOT_SUPPORTED
 
 
 def test_b_transposed_option():

@@ -181,6 +181,39 @@ def test_maximum_n_and_k():
         compare(d, y, "bf16", z=z, mask=mask, mask_ref=mref)
 
 
+@pytest.mark.slow
+def test_maximum_m_row_bias():
+    """m = 2^30 + 200 rows, n = k = 8, (m,1) bias, RELU_AUX_BIAS: rows past
+    2^30 sit more than 2^31 bytes into the bias, and the 64x64 tile's grid
+    would exceed 2^32 - 1 work-items.  A repeats a seeded 4096-row block (tiled
+    on the device by torch); the bias is a full seeded draw.  The oracle runs
+    on the sub-problem of sampled rows: every row across the 2^30 boundary,
+    the first and last 256 and 2048 random ones."""
+    import torch
+    import dense_gemm_epilogue_fp16_amd as egm
+    m, n, k, blk = (1 << 30) + 200, 8, 8, 4096
+    ops = W.gemm_operands(blk, n, k, "fp16", seed=5, bias_layout="row")
+    bias_bits = W.normal_bits((m,), 1.0, "fp16", seed=5, tensor_index=7)
+    g = np.random.default_rng(3)
+    rows = np.unique(np.concatenate([
+        np.arange(256), np.arange((1 << 30) - 256, m), g.integers(256, (1 << 30) - 256, 2048)])).astype(np.int64)
+    a = to_device(ops.a, "fp16").repeat(m // blk + 1, 1)[:m]
+    b = to_device(ops.b, "fp16")
+    bias = to_device(bias_bits, "fp16").reshape(-1, 1)
+    sel = torch.from_numpy(rows).cuda()
+    y, z, mref = eo.reference(ops.a[rows % blk], ops.b, "fp16", "RELU_AUX_BIAS", bias_bits[rows], "row")
+    with egm.Matmul(a, b) as mm:
+        with pytest.raises(egm.EgmError):
+            mm.plan("RELU_AUX_BIAS", {"bias": bias}, force_config=4)  # 64x64: grid too large
+        for cfg in (-1, 0, 3):
+            print(f"[maximum m={m} cfg={cfg}]", flush=True)
+            mm.plan("RELU_AUX_BIAS", {"bias": bias}, force_config=cfg)
+            d, mask = mm.execute()
+            ds, ms = to_host_bits(d.index_select(0, sel)), mask.index_select(0, sel).cpu().numpy()
+            del d, mask
+            compare(ds, y, "fp16", z=z, mask=ms, mask_ref=mref)
+
+
 def test_determinism_and_stream():
     import torch
     import dense_gemm_epilogue_fp16_amd as egm
