@@ -324,6 +324,11 @@ class Matmul:
     ``b`` may be a transposed view of a contiguous [n, k] tensor (``w.t()``,
     a linear layer's weight): the plan then reads it in that layout, with no
     copy (the ``b_transposed`` plan option).
+
+    ``execute(stream=s)`` launches on ``s`` and allocates the outputs there.
+    The two-kernel path and DRELU_BGRAD use a workspace that the plan
+    allocates once and every execute of that plan shares: such executes must
+    not overlap in time (keep them on one stream, or order the streams).
     """
 
     def __init__(self, a, b, *, scale_a=None, scale_b=None, out_dtype=None):
@@ -470,14 +475,14 @@ class Matmul:
         elif b is not self.b:
             self._check_rebound(b, (self.k, self.n), self.b.dtype, transposed=self.bt)
         if out is None:
-            d = torch.empty((self.m, self.n), dtype=self.dtype, device=a.device)
+            d = self._new((self.m, self.n), self.dtype, a.device, stream)
         else:
             self._check_output(out, (self.m, self.n), self.dtype, "out")
             d = out
         mask = None
         if self.epilog == "RELU_AUX_BIAS":
             if aux is None:
-                mask = torch.empty((self.m, self.n // 8), dtype=torch.uint8, device=a.device)
+                mask = self._new((self.m, self.n // 8), torch.uint8, a.device, stream)
             else:
                 self._check_output(aux, (self.m, self.n // 8), torch.uint8, "aux")
                 mask = aux
@@ -490,6 +495,8 @@ class Matmul:
             raise ValueError(f"{self.epilog} takes no mask")
         raw = stream.cuda_stream if stream is not None else torch._C._cuda_getCurrentRawStream(self._dev)
         ws = self._ws
+        if ws is not None and stream is not None:
+            ws.record_stream(stream)  # the allocator must not reuse it before this launch ends
         st = _EXECUTE(plan, a.data_ptr(), b.data_ptr(), d.data_ptr(), mask.data_ptr() if mask is not None else None,
                       ws.data_ptr() if ws is not None else None, ws.numel() if ws is not None else 0, raw)
         if st != EGM_OK:
@@ -499,6 +506,15 @@ class Matmul:
         if self.epilog == "DRELU":
             return d
         return (d, mask) if mask is not None else d
+
+    @staticmethod
+    def _new(shape, dtype, device, stream):
+        # outputs belong to the stream the launch runs on, as torch's own ops do
+        import torch
+        if stream is None:
+            return torch.empty(shape, dtype=dtype, device=device)
+        with torch.cuda.stream(stream):
+            return torch.empty(shape, dtype=dtype, device=device)
 
     def _check_rebound(self, t, shape, dtype, transposed=False):
         self._check_operand(t, "operand", fp8=self.fp8 is not None, transposed=transposed)
@@ -547,13 +563,12 @@ class Matmul:
                              "advances with D and must be [batch, m, n]")
         if out is not None:
             self._check_output(out, (batch, self.m, self.n), self.dtype, "out")
-        d = out if out is not None else torch.empty((batch, self.m, self.n), dtype=self.dtype, device=a.device)
+        d = out if out is not None else self._new((batch, self.m, self.n), self.dtype, a.device, stream)
         mask = None
         if self.epilog == "RELU_AUX_BIAS":
             if aux is not None:
                 self._check_output(aux, (batch, self.m, self.n // 8), torch.uint8, "aux")
-            mask = aux if aux is not None else torch.empty((batch, self.m, self.n // 8), dtype=torch.uint8,
-                                                           device=a.device)
+            mask = aux if aux is not None else self._new((batch, self.m, self.n // 8), torch.uint8, a.device, stream)
         elif self.epilog == "DRELU":
             if aux is None:
                 raise ValueError("DRELU takes the forward masks: aux = uint8 [batch, m, n/8] on the GPU")

@@ -228,6 +228,17 @@ def test_determinism_and_stream():
             d2, m2 = mm.execute()
         torch.cuda.synchronize()
     assert torch.equal(d1, d2) and torch.equal(m1, m2)
+    # the stream argument: outputs are allocated on that stream and a plan's
+    # workspace (two-kernel path) is recorded on it
+    with egm.Matmul(a, b) as mm:
+        mm.plan("RELU_AUX_BIAS", {"bias": bias}, fused=False)
+        d3, m3 = mm.execute()
+        torch.cuda.synchronize()
+        d4, m4 = mm.execute(stream=s)
+        s.synchronize()
+    assert torch.equal(d3, d4) and torch.equal(m3, m4)
+    y, z, mref = oracle_for(ops, "RELU_AUX_BIAS")
+    compare(to_host_bits(d4), y, "bf16", z=z, mask=m4.cpu().numpy(), mask_ref=mref, unfused=True)
 
 
 def test_wrapper_rejects_bad_inputs():
