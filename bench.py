@@ -107,6 +107,9 @@ def main():
                     help="instead of the bench line: run the fused step back to back for this many seconds and "
                          "print one JSON line per second with its throughput and the board power and clocks "
                          "that amd-smi reports meanwhile")
+    ap.add_argument("--sustain-vendor", action="store_true",
+                    help="with --sustain, 16-bit workloads: then run the vendor GEMM alone (torch.matmul into "
+                         "the same outputs) the same way, for the clock and power it sustains (context only)")
     args = ap.parse_args()
     if args.ingest_pmc:
         ingest_pmc(args.workload, *args.ingest_pmc, copy_mib=args.copy_mib or 1024)
@@ -244,6 +247,18 @@ def main():
     probe_ms, _ = timed(fused_plans, 1, 1)
     if args.sustain > 0:
         sustain(lambda: step(fused_plans), probe_ms, flops, args.sustain, dev, stream)
+        if args.sustain_vendor:
+            if fp8:
+                raise SystemExit("--sustain-vendor covers the 16-bit workloads")
+            print(json.dumps({"leg": "vendor GEMM alone (torch.matmul), context only"}), flush=True)
+
+            def vendor_step():
+                for (aa, bb), _, _, out, _, _ in specs:
+                    torch.matmul(aa, bb, out=out["out"])
+
+            vendor_step()
+            torch.cuda.synchronize(dev)
+            sustain(vendor_step, probe_ms, flops, args.sustain, dev, stream)
         for mm, *_ in fused_plans + unfused_plans:
             mm.free()
         return
