@@ -161,7 +161,12 @@ typedef int32_t i32x4 __attribute__((ext_vector_type(4)));
 
 __device__ __forceinline__ i32x4 make_srd(const void* base, uint64_t bytes) {
   const uint64_t a = (uint64_t)(uintptr_t)base;
-  const uint32_t n = bytes > MAX_RECORDS ? MAX_RECORDS : (uint32_t)bytes;
+  // the clamp in 32-bit halves: scalar compares (gfx9 has no 64-bit scalar
+  // less-than, and the compiler would merge the halves back into a vector
+  // one).  Every caller passes wave-uniform values.
+  uint32_t hi = (uint32_t)(bytes >> 32);
+  asm("" : "+s"(hi));
+  const uint32_t n = hi != 0u || (uint32_t)bytes > MAX_RECORDS ? MAX_RECORDS : (uint32_t)bytes;
   return i32x4{(int32_t)(uint32_t)a, (int32_t)(uint32_t)((a >> 32) & 0xffffu), (int32_t)n, RSRC_FLAGS};
 }
 
@@ -552,6 +557,10 @@ __global__ void __launch_bounds__(C::NT, 1) gemm_epilogue_kernel(GemmArgs p) {
   }
   int tm, tn;
   tile_coords(blockIdx.x, p.tiles_m, p.tiles_n, p.group_m, tm, tn);
+  // uniform by construction; in scalar registers the tile's buffer ranges and
+  // bounds stay scalar arithmetic in the main loop
+  tm = __builtin_amdgcn_readfirstlane(tm);
+  tn = __builtin_amdgcn_readfirstlane(tn);
   const int m0 = tm * C::BM;
   const int n0 = tn * C::BN;
   const int KT = (K + C::BK - 1) / C::BK;
@@ -611,21 +620,24 @@ __global__ void __launch_bounds__(C::NT, 1) gemm_epilogue_kernel(GemmArgs p) {
   struct SlabSrd {
     i32x4 a, b;
     uint32_t kbase;
+    bool full;  // the whole slab lies below K: the A copies need no per-lane k check
   };
+  // The tile's first row (m0 < M) and column (n0 < N) exist, so a slab's start
+  // lies inside its operand exactly when kbase < K: one 32-bit scalar compare
+  // instead of 64-bit ones (which gfx9 scalar units lack).
   auto slab_srd = [&](int kt) {
     SlabSrd r;
     r.kbase = (uint32_t)kt * C::BK;
+    const bool in_k = r.kbase < (uint32_t)K;
+    r.full = r.kbase + C::BK <= (uint32_t)K;
     const uint64_t a_start = (uint64_t)m0 * K + r.kbase, a_size = (uint64_t)M * K;
-    r.a = make_srd((const uint8_t*)p.A + (a_start < a_size ? a_start : 0) * C::ES,
-                   a_start < a_size && r.kbase < (uint32_t)K ? (a_size - a_start) * C::ES : 0);
+    r.a = make_srd((const uint8_t*)p.A + (in_k ? a_start : 0) * C::ES, in_k ? (a_size - a_start) * C::ES : 0);
     if constexpr (BT) {
       const uint64_t b_start = (uint64_t)n0 * K + r.kbase, b_size = (uint64_t)N * K;
-      r.b = make_srd((const uint8_t*)p.B + (b_start < b_size ? b_start : 0) * C::ES,
-                     b_start < b_size && r.kbase < (uint32_t)K ? (b_size - b_start) * C::ES : 0);
+      r.b = make_srd((const uint8_t*)p.B + (in_k ? b_start : 0) * C::ES, in_k ? (b_size - b_start) * C::ES : 0);
     } else {
       const uint64_t b_start = (uint64_t)r.kbase * N + n0, b_size = (uint64_t)K * N;
-      r.b = make_srd((const uint8_t*)p.B + (b_start < b_size ? b_start : 0) * C::ES,
-                     b_start < b_size ? (b_size - b_start) * C::ES : 0);
+      r.b = make_srd((const uint8_t*)p.B + (in_k ? b_start : 0) * C::ES, in_k ? (b_size - b_start) * C::ES : 0);
     }
     return r;
   };
@@ -704,6 +716,38 @@ __global__ void __launch_bounds__(C::NT, 1) gemm_epilogue_kernel(GemmArgs p) {
       bt_off[ks][h] = C::A_BYTES + (uint32_t)(wn0 + lr) * C::A_ROW + ((chunk ^ a_swz<C::A_CHUNKS>(lr)) << 4);
     }
 
+  // Per-buffer copies of the 16-bit fragment offsets, kept in registers: a
+  // ring buffer lies STAGE_BYTES (64 KiB for the 256x256 tile) above the
+  // previous one, beyond the 16-bit offset of an LDS read, so without them
+  // every read address of a slab would be recomputed beside the MFMAs.  The
+  // main loop runs whole turns of the ring, so the buffer index is a
+  // compile-time constant.  (fp8 tiles keep the per-slab additions: there the
+  // extra registers measured slower.)
+  constexpr int S16 = C::ES == 2 ? C::STAGES : 1;
+  auto in_buffer = [](uint32_t off, int s) {
+    uint32_t v = off + (uint32_t)(s * C::STAGE_BYTES);
+    if (s > 0) asm volatile("" : "+v"(v));  // a register of its own, not re-derived in the loop
+    return v;
+  };
+  uint32_t a_fo[S16][C::NS], b_fo[S16][2][C::FN], bt_fo[S16][C::NS];
+  if constexpr (C::ES == 2) {
+#pragma unroll
+    for (int s = 0; s < C::STAGES; ++s) {
+#pragma unroll
+      for (int ks = 0; ks < C::NS; ++ks) {
+        a_fo[s][ks] = in_buffer(a_frag_off[ks], s);
+        if constexpr (BT) bt_fo[s][ks] = in_buffer(bt_off[ks][0], s);
+      }
+      if constexpr (!BT) {
+#pragma unroll
+        for (int j = 0; j < C::FN; ++j) {
+          b_fo[s][0][j] = in_buffer(b_frag_off[0][j], s);
+          b_fo[s][1][j] = in_buffer(b_frag_off[1][j], s);
+        }
+      }
+    }
+  }
+
   f32x16 acc[C::FM][C::FN];
 #pragma unroll
   for (int i = 0; i < C::FM; ++i)
@@ -732,15 +776,17 @@ __global__ void __launch_bounds__(C::NT, 1) gemm_epilogue_kernel(GemmArgs p) {
       const int t = piece < RA ? piece : piece - RB * C::FN;
       const int i = t / RA, h = t % RA;
       if constexpr (C::ES == 2)
-        fa[set][i][0] = *(const u32x4*)(st + a_frag_off[ks] + i * 32 * C::A_ROW);
+        fa[set][i][0] = *(const u32x4*)(smem + a_fo[stage][ks] + i * 32 * C::A_ROW);
       else
         fa[set][i][h] = *(const u32x4*)(st + a8_off[ks][h] + i * 32 * C::A_ROW);
     } else {
       const int j = (piece - RA) / RB, t = (piece - RA) % RB;
-      if constexpr (BT)
+      if constexpr (BT && C::ES == 2)
+        fbt[set][j][t] = *(const u32x4*)(smem + bt_fo[stage][ks] + j * 32 * C::A_ROW);
+      else if constexpr (BT)
         fbt[set][j][t] = *(const u32x4*)(st + bt_off[ks][t] + j * 32 * C::A_ROW);
       else if constexpr (C::ES == 2)
-        fb[set][j][t] = lds_read_tr<DT>(st + b_frag_off[t][j] + ks * 16 * C::B_ROW);
+        fb[set][j][t] = lds_read_tr<DT>(smem + b_fo[stage][t][j] + ks * 16 * C::B_ROW);
       else
         fb[set][j][t] = lds_read_tr8(st + b8_off[j] + (ks * 64 + 8 * t) * C::B_ROW);
     }
@@ -810,8 +856,9 @@ __global__ void __launch_bounds__(C::NT, 1) gemm_epilogue_kernel(GemmArgs p) {
     wait_vmcnt<(C::STAGES - 1) * C::PW>();
     __syncthreads();
     read_slice(0, 0, 0);
-    int st = 0;
-    for (int kt = 0; kt < KT; ++kt) {
+    // slab kt sits in ring buffer st = kt % STAGES (a constant in each copy
+    // of the body below)
+    auto slab = [&](int kt, int st) {
       const int st_next = st + 1 == C::STAGES ? 0 : st + 1;
 #pragma unroll
       for (int ks = 0; ks < C::NS - 1; ++ks) {
@@ -836,8 +883,18 @@ __global__ void __launch_bounds__(C::NT, 1) gemm_epilogue_kernel(GemmArgs p) {
         mfmas((C::NS - 1) & 1);
         interleave();
         __builtin_amdgcn_sched_barrier(0);
+        // (a uniform branch: the k check of the A copies only in a slab that
+        // crosses K)
+        if (r.full) {
+          const uint32_t sa = smem_lds + (uint32_t)(st * C::STAGE_BYTES);
 #pragma unroll
-        for (int q = 0; q < C::PW; ++q) issue_one(r, st, q);
+          for (int q = 0; q < C::A_PW; ++q) dma16(r.a, sa + (wave * C::A_PW + q) * 1024u, a_off[q]);
+#pragma unroll
+          for (int q = C::A_PW; q < C::PW; ++q) issue_one(r, st, q);
+        } else {
+#pragma unroll
+          for (int q = 0; q < C::PW; ++q) issue_one(r, st, q);
+        }
         __builtin_amdgcn_sched_barrier(0);
       } else {
         // one wave per SIMD: the refill loads go out one at a time between the
@@ -853,8 +910,15 @@ __global__ void __launch_bounds__(C::NT, 1) gemm_epilogue_kernel(GemmArgs p) {
         interleave();
         __builtin_amdgcn_sched_barrier(0);
       }
-      st = st_next;
+    };
+    int kt = 0;
+    for (; kt + C::STAGES <= KT; kt += C::STAGES) {
+#pragma unroll
+      for (int s = 0; s < C::STAGES; ++s) slab(kt + s, s);
     }
+#pragma unroll
+    for (int s = 0; s < C::STAGES - 1; ++s)
+      if (kt + s < KT) slab(kt + s, s);
   }
 
   // fp8: the product of the two per-tensor scales (uniform; NULL reads as 1),
