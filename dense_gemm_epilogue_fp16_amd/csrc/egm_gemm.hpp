@@ -876,35 +876,72 @@ __global__ void __launch_bounds__(C::NT, 1) gemm_epilogue_kernel(GemmArgs p) {
       __builtin_amdgcn_sched_barrier(0);
       const SlabSrd r = slab_srd(kt + C::STAGES);
       if constexpr (C::NW == 8) {
-        // two waves per SIMD: the last k-slice's MFMAs go out first and the
-        // refill loads after them, while the SIMD partner keeps the MFMA pipe
-        // busy (measured faster than interleaving for this layout)
-        read_slice(0, st_next, 0);
-        mfmas((C::NS - 1) & 1);
-        interleave();
-        __builtin_amdgcn_sched_barrier(0);
-        // (a uniform branch: the k check of the A copies only in a slab that
-        // crosses K)
-        if (r.full) {
+        // two waves per SIMD.  16-bit tiles: the A refill goes out right
+        // after the barrier, the last k-slice's reads and MFMAs next, the B
+        // refill after them (measured 1.5-2 % faster on the large shapes than
+        // the whole refill after the MFMAs, which is faster than the whole
+        // refill first or interleaved).  fp8 tiles issue the whole refill
+        // after the MFMAs: their registers are fully used, and holding the A
+        // copies' operands across the slice made the compiler spill.
+        // (A uniform branch drops the per-lane k check of the A copies in
+        // every slab below K.)
+        if constexpr (C::ES == 2) {
           const uint32_t sa = smem_lds + (uint32_t)(st * C::STAGE_BYTES);
+          if (r.full) {
 #pragma unroll
-          for (int q = 0; q < C::A_PW; ++q) dma16(r.a, sa + (wave * C::A_PW + q) * 1024u, a_off[q]);
+            for (int q = 0; q < C::A_PW; ++q) dma16(r.a, sa + (wave * C::A_PW + q) * 1024u, a_off[q]);
+          } else {
+#pragma unroll
+            for (int q = 0; q < C::A_PW; ++q) issue_one(r, st, q);
+          }
+          __builtin_amdgcn_sched_barrier(0);
+          read_slice(0, st_next, 0);
+          mfmas((C::NS - 1) & 1);
+          interleave();
+          __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
           for (int q = C::A_PW; q < C::PW; ++q) issue_one(r, st, q);
         } else {
+          read_slice(0, st_next, 0);
+          mfmas((C::NS - 1) & 1);
+          interleave();
+          __builtin_amdgcn_sched_barrier(0);
+          if (r.full) {
+            const uint32_t sa = smem_lds + (uint32_t)(st * C::STAGE_BYTES);
 #pragma unroll
-          for (int q = 0; q < C::PW; ++q) issue_one(r, st, q);
+            for (int q = 0; q < C::A_PW; ++q) dma16(r.a, sa + (wave * C::A_PW + q) * 1024u, a_off[q]);
+#pragma unroll
+            for (int q = C::A_PW; q < C::PW; ++q) issue_one(r, st, q);
+          } else {
+#pragma unroll
+            for (int q = 0; q < C::PW; ++q) issue_one(r, st, q);
+          }
         }
         __builtin_amdgcn_sched_barrier(0);
       } else {
         // one wave per SIMD: the refill loads go out one at a time between the
         // reads of the next k-slice (and so between the MFMAs), never as a
         // burst that would back up the address unit and stall MFMA issue
+        // (64x64 tiles: in slabs below K the A copies skip their per-lane k
+        // check; measured 4 % faster there, and no faster for 128x128)
+        if (C::BM * C::BN <= 64 * 64 && r.full) {
+          const uint32_t sa = smem_lds + (uint32_t)(st * C::STAGE_BYTES);
 #pragma unroll
-        for (int q = 0; q < C::PW; ++q) {
-          issue_one(r, st, q);
+          for (int q = 0; q < C::PW; ++q) {
+            if (q < C::A_PW)
+              dma16(r.a, sa + (wave * C::A_PW + q) * 1024u, a_off[q]);
+            else
+              issue_one(r, st, q);
 #pragma unroll
-          for (int pc = q * NRD / C::PW; pc < (q + 1) * NRD / C::PW; ++pc) read_piece(0, st_next, 0, pc);
+            for (int pc = q * NRD / C::PW; pc < (q + 1) * NRD / C::PW; ++pc) read_piece(0, st_next, 0, pc);
+          }
+        } else {
+#pragma unroll
+          for (int q = 0; q < C::PW; ++q) {
+            issue_one(r, st, q);
+#pragma unroll
+            for (int pc = q * NRD / C::PW; pc < (q + 1) * NRD / C::PW; ++pc) read_piece(0, st_next, 0, pc);
+          }
         }
         mfmas((C::NS - 1) & 1);
         interleave();
