@@ -54,6 +54,25 @@ def test_integer_exact_bits(dtype, epilog, cfg):
 
 
 @pytest.mark.parametrize("cfg", CONFIGS)
+def test_ring_turns_and_partial_slab(cfg):
+    """The main loop runs whole turns of its ring of k-slabs, then the slabs
+    left over, and skips the A copies' per-lane k check in slabs wholly below
+    K: every count of 64-deep slabs from 1 to past two turns of the deepest
+    ring (4), with and without a partial last slab, bit-exact on
+    small-integer operands."""
+    m, n = 72, 264
+    for kt in range(1, 11):
+        for k in (64 * kt, 64 * kt - 56):
+            ops = W.integer_operands(m, n, k, "bf16", seed=100 * cfg + k, lo=-1, hi=1, bias_layout="row",
+                                     residual=True)
+            d, mask = run(ops, "RELU_AUX_BIAS", force_config=cfg)
+            y, z, mref = oracle_for(ops, "RELU_AUX_BIAS")
+            bad = d != exact_bits(y, "bf16")
+            assert not bad.any(), f"k={k}: {int(bad.sum())} outputs differ; first {tuple(np.argwhere(bad)[0])}"
+            assert np.array_equal(mask, mref), f"k={k}: mask differs"
+
+
+@pytest.mark.parametrize("cfg", CONFIGS)
 @pytest.mark.parametrize("epilog", ALL_EPILOGS)
 @pytest.mark.parametrize("dtype", ["fp16", "bf16"])
 def test_normal_within_tolerance(dtype, epilog, cfg):
