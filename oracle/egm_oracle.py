@@ -201,10 +201,14 @@ def round_to_bits(y: np.ndarray, dtype: str) -> np.ndarray:
 
 
 def ulp(y: np.ndarray, dtype: str) -> np.ndarray:
-    """Spacing of the 16-bit format at |y| (for the double-rounding bound)."""
+    """Spacing of the 16-bit format at |y| (for the double-rounding bound): the
+    gap above the binade |y| lies in; zero and the subnormals share the
+    subnormal spacing 2^(emin - (sig - 1))."""
     sig, emin, _ = _FORMAT[dtype]
-    _, e = np.frexp(np.asarray(y, dtype=np.float64))
-    return np.ldexp(1.0, np.maximum(e - 1, emin) - (sig - 1))
+    y = np.asarray(y, dtype=np.float64)
+    _, e = np.frexp(y)                      # |y| in [2^(e-1), 2^e); frexp(0) gives e = 0
+    lead = np.where(y == 0.0, emin, np.maximum(e - 1, emin))
+    return np.ldexp(1.0, lead - (sig - 1))
 
 
 # ---------------------------------------------------------------------------

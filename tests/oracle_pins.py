@@ -639,4 +639,76 @@ def pin_layernorm_invariants(o):
     assert np.allclose(yg, y0 * g[None, :] + b[None, :] + r, rtol=0, atol=1e-12)
 
 
+def _golden_ulps():
+    rows = []
+    with open(os.path.join(GOLDEN, "ulp_spacings.txt")) as f:
+        for line in f:
+            if line.strip() and not line.startswith("#"):
+                dt, v, q, *_ = line.split()
+                rows.append((dt, float.fromhex(v), float.fromhex(q)))
+    return rows
+
+
+def pin_ulp_golden(o):
+    """Hand-derived spacings of binary16 and bfloat16 (tests/golden), at either
+    sign of the value."""
+    rows = _golden_ulps()
+    assert len(rows) >= 16 and {r[0] for r in rows} == {F16, BF16}
+    for dt, v, q in rows:
+        got = o.ulp(np.array([v, -v]), dt)
+        assert np.array_equal(got, np.array([q, q])), (dt, v.hex(), [float(g).hex() for g in got], q.hex())
+
+
+def pin_ulp_library(o):
+    """Every finite value of each format, zero included, against numpy's
+    spacing: np.spacing of the fp16 value itself, and for bfloat16 (the upper
+    half of a binary32 whose low 16 bits are zero) the binary32 spacing times
+    2^16, since both share the exponent range and bfloat16 keeps 16 fewer
+    fraction bits.  Zero has the subnormal spacing."""
+    bits = np.arange(1 << 16, dtype=np.uint32).astype(np.uint16)
+    h = bits.view(np.float16)
+    # numpy steps past the largest finite value to infinity; the golden file
+    # holds the spacing there
+    fin = np.isfinite(h) & (np.abs(h) < np.float16(65504))
+    want = np.abs(np.spacing(np.abs(h[fin]))).astype(np.float64)
+    assert np.array_equal(o.ulp(h[fin].astype(np.float64), F16), want)
+    f = (bits.astype(np.uint32) << np.uint32(16)).view(np.float32)
+    fin = np.isfinite(f) & (np.abs(f) < np.float32(float.fromhex("0x1.fep127")))
+    want = np.abs(np.spacing(np.abs(f[fin]))).astype(np.float64) * 65536.0
+    assert np.array_equal(o.ulp(f[fin].astype(np.float64), BF16), want)
+
+
+def _bits_of(values, dtype):
+    """Exactly representable values -> 16-bit patterns, by numpy's own casts
+    (a binary16 array, or the upper half of a binary32)."""
+    v = np.asarray(values, dtype=np.float64)
+    if dtype == F16:
+        h = v.astype(np.float16)
+        assert np.array_equal(h.astype(np.float64), v)
+        return h.view(np.uint16)
+    f = v.astype(np.float32)
+    b = f.view(np.uint32)
+    assert np.array_equal(f.astype(np.float64), v) and not np.any(b & np.uint32(0xFFFF))
+    return (b >> np.uint32(16)).astype(np.uint16)
+
+
+def pin_layernorm_reference_golden(o):
+    """The 16-bit entry point of the LayerNorm oracle on the hand-worked rows,
+    passed as bit patterns in both formats: x, gamma, beta and the residual must
+    each land in its own place."""
+    cases = _golden_layernorm()
+    for dtype in (F16, BF16):
+        for c in cases:
+            rb = _bits_of(c["R"], dtype)[None, :] if "R" in c else None
+            y, mean, rstd = o.layer_norm_reference(_bits_of(c["X"], dtype)[None, :], dtype,
+                                                   _bits_of(c["GAMMA"], dtype), _bits_of(c["BETA"], dtype),
+                                                   c["eps"], rb)
+            assert np.array_equal(y[0], c["Y"]), (dtype, c["name"], y[0], c["Y"])
+            assert mean[0] == c["X"].mean()
+        # gamma and beta omitted mean 1 and 0
+        c = cases[0]
+        y, _, _ = o.layer_norm_reference(_bits_of(c["X"], dtype)[None, :], dtype, None, None, c["eps"])
+        assert np.array_equal(y[0], c["Y"])
+
+
 PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_")]

@@ -185,7 +185,68 @@ def _ln_column_stats(x64, gamma64=None, beta64=None, eps=1e-5, r64=None):
     return (y if r64 is None else y + r64), mean, rstd
 
 
+def _ulp_doubled(y, dtype):
+    return 2.0 * _orig["ulp"](y, dtype)
+
+
+def _ulp_one_binade_low(y, dtype):
+    return 0.5 * _orig["ulp"](y, dtype)
+
+
+def _ln_ref_gamma_beta_swapped(x_bits, dtype, gamma_bits=None, beta_bits=None, eps=1e-5, residual_bits=None):
+    return _orig["layer_norm_reference"](x_bits, dtype, beta_bits, gamma_bits, eps, residual_bits)
+
+
+def _ln_ref_residual_dropped(x_bits, dtype, gamma_bits=None, beta_bits=None, eps=1e-5, residual_bits=None):
+    return _orig["layer_norm_reference"](x_bits, dtype, gamma_bits, beta_bits, eps, None)
+
+
+def _ln_ref_default_eps(x_bits, dtype, gamma_bits=None, beta_bits=None, eps=1e-5, residual_bits=None):
+    return _orig["layer_norm_reference"](x_bits, dtype, gamma_bits, beta_bits, 1e-5, residual_bits)
+
+
+def _reference_rows_unsliced_bias(a_bits, b_bits, dtype, epilog, bias_bits=None, bias_layout=None,
+                                  residual_bits=None, rows=None):
+    # a sampled-row reference that forgets to slice a per-row bias: it uses the
+    # first len(rows) bias values instead of the sampled rows' own
+    if rows is not None and bias_layout == "row" and bias_bits is not None:
+        rows = np.asarray(rows)
+        y, z, m = _orig["reference"](np.asarray(a_bits)[rows], b_bits, dtype, epilog,
+                                     np.asarray(bias_bits).reshape(-1)[: len(rows)], bias_layout,
+                                     None if residual_bits is None else np.asarray(residual_bits)[rows])
+        return y, z, m
+    return _orig["reference"](a_bits, b_bits, dtype, epilog, bias_bits, bias_layout, residual_bits, rows)
+
+
+def _reference_mask_after_relu(a_bits, b_bits, dtype, epilog, bias_bits=None, bias_layout=None,
+                               residual_bits=None, rows=None):
+    # the mask taken from the activated output with >= (every bit set)
+    y, z, m = _orig["reference"](a_bits, b_bits, dtype, epilog, bias_bits, bias_layout, residual_bits, rows)
+    if m is not None:
+        m = np.packbits(y >= 0.0, axis=1, bitorder="little")
+    return y, z, m
+
+
+def _backward_reference_no_mask(a_bits, b_bits, dtype, epilog, mask, bias_layout=None):
+    full = np.full_like(np.asarray(mask, dtype=np.uint8), 0xFF)
+    return _orig["backward_reference"](a_bits, b_bits, dtype, epilog, full, bias_layout)
+
+
+def _backward_reference_axis_swapped(a_bits, b_bits, dtype, epilog, mask, bias_layout=None):
+    swapped = None if bias_layout is None else ("row" if bias_layout == "col" else "col")
+    return _orig["backward_reference"](a_bits, b_bits, dtype, epilog, mask, swapped)
+
+
 MUTANTS = {
+    "reference_rows_unsliced_bias": ("reference", _reference_rows_unsliced_bias),
+    "reference_mask_after_relu": ("reference", _reference_mask_after_relu),
+    "backward_reference_no_mask": ("backward_reference", _backward_reference_no_mask),
+    "backward_reference_axis_swapped": ("backward_reference", _backward_reference_axis_swapped),
+    "ulp_doubled": ("ulp", _ulp_doubled),
+    "ulp_halved": ("ulp", _ulp_one_binade_low),
+    "ln_ref_gamma_beta_swapped": ("layer_norm_reference", _ln_ref_gamma_beta_swapped),
+    "ln_ref_residual_dropped": ("layer_norm_reference", _ln_ref_residual_dropped),
+    "ln_ref_eps_ignored": ("layer_norm_reference", _ln_ref_default_eps),
     "ln_unbiased_variance": ("layer_norm", _ln_unbiased),
     "ln_eps_outside_sqrt": ("layer_norm", _ln_eps_outside),
     "ln_residual_before_norm": ("layer_norm", _ln_residual_before),
