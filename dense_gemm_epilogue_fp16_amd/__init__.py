@@ -21,7 +21,9 @@ import ctypes
 import os
 
 HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(HERE, "libegm.so")
+# EGM_LIBRARY names another build of the same library (the tests load the
+# host-sanitized one this way); there is no other compute path
+LIB_PATH = os.environ.get("EGM_LIBRARY") or os.path.join(HERE, "libegm.so")
 
 # status codes (egm_status_t)
 EGM_OK = 0

@@ -4,27 +4,41 @@
 
 Translation units: egm_kernels.hip once per 16-bit dtype (fp16, bf16) and
 once per (fp8 format pair, output dtype), and the host API egm_api.hip,
-compiled in parallel, then linked into one shared library next to this file.
+compiled in parallel (objects under _build/), then linked into one shared
+library next to this file.
+
+    python dense_gemm_epilogue_fp16_amd/build.py --host-sanitized
+
+builds _build/libegm_host_sanitized.so: the same kernels, with the host API
+unit compiled under AddressSanitizer and UndefinedBehaviorSanitizer (host
+code only: each -fsanitize= goes behind -Xarch_host, so no device code is
+instrumented).  It is for CPU runs of the ABI tests, with the sanitizer
+runtime preloaded into the Python process (see host_sanitizer_runtime()).
 """
 from __future__ import annotations
 
 import os
+import glob
 import shutil
 import subprocess
 import sys
-import tempfile
 from concurrent.futures import ThreadPoolExecutor
 
 HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 INCLUDE = os.path.join(os.path.dirname(HERE), "include")
 LIB = os.path.join(HERE, "libegm.so")
+OBJ_DIR = os.path.join(HERE, "_build")
+SANITIZED_LIB = os.path.join(OBJ_DIR, "libegm_host_sanitized.so")
 ARCH = "gfx950"
 
 # Packed fp32 ops (v_pk_*_f32) are disabled for all device code.
 DEVICE_FLAGS = ["-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
 COMMON = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}", "-I", INCLUDE, "-Wall",
           "-Wno-unused-command-line-argument"]
+# host-side sanitizers for the host API unit (never applied to device code)
+HOST_SANITIZE = ["-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fsanitize=undefined",
+                 "-Xarch_host", "-fno-sanitize-recover=undefined", "-Xarch_host", "-fno-omit-frame-pointer", "-g"]
 
 
 def hipcc() -> str:
@@ -64,16 +78,52 @@ def build(verbose: bool = False, extra_flags=None) -> str:
     """Compile every HIP translation unit for gfx950 and link libegm.so."""
     cc = hipcc()
     extra = list(extra_flags or [])
-    with tempfile.TemporaryDirectory(prefix="egm_build_") as obj_dir:
-        units = _units(obj_dir)
-        cmds = [[cc, *COMMON, *DEVICE_FLAGS, *defs, *extra, "-c", src, "-o", obj] for src, obj, defs in units]
-        with ThreadPoolExecutor(min(len(cmds), max(1, os.cpu_count() or 1))) as ex:
-            list(ex.map(lambda c: _run(c, verbose), cmds))
-        tmp = LIB + ".tmp"
-        _run([cc, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *[o for _, o, _ in units]], verbose)
-        os.replace(tmp, LIB)
+    os.makedirs(OBJ_DIR, exist_ok=True)
+    units = _units(OBJ_DIR)
+    cmds = [[cc, *COMMON, *DEVICE_FLAGS, *defs, *extra, "-c", src, "-o", obj] for src, obj, defs in units]
+    with ThreadPoolExecutor(min(len(cmds), max(1, os.cpu_count() or 1))) as ex:
+        list(ex.map(lambda c: _run(c, verbose), cmds))
+    tmp = LIB + ".tmp"
+    _run([cc, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *[o for _, o, _ in units]], verbose)
+    os.replace(tmp, LIB)
     return LIB
 
 
+def host_sanitizer_runtime() -> str:
+    """Path of clang's AddressSanitizer runtime (it carries the
+    UndefinedBehaviorSanitizer handlers too), to preload into the process
+    that loads the sanitized library."""
+    cc = os.path.realpath(hipcc())
+    roots = [os.path.join(os.path.dirname(os.path.dirname(cc)), "llvm"), "/opt/rocm/llvm",
+             os.path.dirname(os.path.dirname(cc))]
+    for root in roots:
+        hits = sorted(glob.glob(os.path.join(root, "lib", "clang", "*", "lib", "linux",
+                                             "libclang_rt.asan-x86_64.so")))
+        if hits:
+            return hits[-1]
+    raise RuntimeError("clang's AddressSanitizer runtime (libclang_rt.asan-x86_64.so) not found")
+
+
+def build_host_sanitized(verbose: bool = False) -> str:
+    """The library with its host API unit under ASan + UBSan (host code only)
+    and the kernel objects of the last build(); builds those first if absent."""
+    cc = hipcc()
+    units = _units(OBJ_DIR)
+    kernel_objs = [o for src, o, _ in units if not src.endswith("egm_api.hip")]
+    if not all(os.path.exists(o) for o in kernel_objs):
+        build(verbose)
+    api_src = os.path.join(CSRC, "egm_api.hip")
+    api_obj = os.path.join(OBJ_DIR, "egm_api_host_sanitized.o")
+    _run([cc, *COMMON, *DEVICE_FLAGS, *HOST_SANITIZE, "-c", api_src, "-o", api_obj], verbose)
+    tmp = SANITIZED_LIB + ".tmp"
+    _run([cc, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-Xarch_host", "-fsanitize=address",
+          "-Xarch_host", "-fsanitize=undefined", "-shared-libsan", "-o", tmp, api_obj, *kernel_objs], verbose)
+    os.replace(tmp, SANITIZED_LIB)
+    return SANITIZED_LIB
+
+
 if __name__ == "__main__":
-    print(build(verbose="-v" in sys.argv))
+    if "--host-sanitized" in sys.argv:
+        print(build_host_sanitized(verbose="-v" in sys.argv))
+    else:
+        print(build(verbose="-v" in sys.argv))

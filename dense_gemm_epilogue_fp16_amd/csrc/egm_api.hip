@@ -13,10 +13,14 @@
 
 #include <hip/hip_runtime.h>
 
+#include <atomic>
 #include <cstdio>
 #include <cstdlib>
 #include <cstring>
+#include <memory>
+#include <mutex>
 #include <new>
+#include <unordered_map>
 
 #include "egm.h"
 #include "egm_epilogue.hpp"
@@ -31,8 +35,6 @@ using egm::EpiLaunch;
 using egm::GemmArgs;
 using egm::GemmLaunch;
 
-constexpr uint32_t kPlanMagic = 0x45474d31u;  // "EGM1"
-constexpr uint32_t kFreedMagic = 0xdeadbeefu;
 constexpr int kNumEpi = 8;
 // keeps every in-tile buffer offset (256 rows x n or k elements) below 2^30
 constexpr int64_t kMaxNK = int64_t(1) << 21;
@@ -85,7 +87,6 @@ bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) ==
 }  // namespace
 
 struct egm_plan_s {
-  uint32_t magic;
   int64_t m, n, k;
   egm_dtype_t dtype;
   egm_epilog_t epilog;
@@ -94,9 +95,10 @@ struct egm_plan_s {
   const void* residual;
   void* bias_grad;           // DRELU_BGRAD output (fp32)
   int32_t fused;
-  int32_t config;
+  std::atomic<int32_t> config;            // rewritten once by a pending autotune
   int32_t group_m;
-  int32_t autotune_pending;
+  std::atomic<int32_t> autotune_pending;
+  std::mutex tune_mu;                     // one autotune per plan, even from several threads
   size_t workspace_bytes;
   size_t product_bytes;      // the two-kernel path's P at the start of the workspace
   int64_t grad_len;          // DRELU_BGRAD: length of the gradient (n or m)
@@ -108,7 +110,49 @@ struct egm_plan_s {
 
 namespace {
 
-bool valid_plan(egm_plan_t p) { return p != nullptr && p->magic == kPlanMagic; }
+// Live plans.  A handle is a number handed out once and never again, not the
+// plan's address: a NULL, freed or foreign handle is recognised by a lookup
+// that never touches freed memory, and a stale handle cannot alias a later
+// plan.  Each call holds a reference for its duration, so an egm_free of the
+// same handle from another thread cannot release the plan under it.
+struct Registry {
+  std::mutex mu;
+  std::unordered_map<uintptr_t, std::shared_ptr<egm_plan_s>> live;
+  uintptr_t next = 0x1000;  // handles start well away from NULL
+};
+Registry& registry() {
+  static Registry* r = new Registry();  // never destroyed: usable from exit handlers
+  return *r;
+}
+
+egm_plan_t register_plan(std::shared_ptr<egm_plan_s> p) {
+  Registry& r = registry();
+  std::lock_guard<std::mutex> lock(r.mu);
+  const uintptr_t h = r.next;
+  r.live.emplace(h, std::move(p));
+  r.next += 0x10;
+  return reinterpret_cast<egm_plan_t>(h);
+}
+
+std::shared_ptr<egm_plan_s> lookup(egm_plan_t handle) {
+  if (handle == nullptr) return nullptr;
+  Registry& r = registry();
+  std::lock_guard<std::mutex> lock(r.mu);
+  const auto it = r.live.find(reinterpret_cast<uintptr_t>(handle));
+  return it == r.live.end() ? nullptr : it->second;
+}
+
+// removes the handle; the plan itself goes when the last call using it returns
+bool unregister(egm_plan_t handle) {
+  std::shared_ptr<egm_plan_s> dead;  // released after the lock
+  Registry& r = registry();
+  std::lock_guard<std::mutex> lock(r.mu);
+  const auto it = r.live.find(reinterpret_cast<uintptr_t>(handle));
+  if (it == r.live.end()) return false;
+  dead = std::move(it->second);
+  r.live.erase(it);
+  return true;
+}
 
 // DRELU_BGRAD partial-sum rows a launch writes: one per tile row ((1,n)
 // bias) or tile column ((m,1) bias) on the fused path, one per 32-row or
@@ -259,10 +303,25 @@ hipError_t autotune(egm_plan_s* p, const void* A, const void* B, void* D, void* 
   (void)hipEventDestroy(e0);
   (void)hipEventDestroy(e1);
   if (err == hipSuccess) {
-    p->config = best_cfg;
-    p->autotune_pending = 0;
+    p->config.store(best_cfg, std::memory_order_relaxed);
+    p->autotune_pending.store(0, std::memory_order_release);
   }
   return err;
+}
+
+// The first execute of an autotune plan times every config and waits for the
+// events on the host, so it cannot be recorded into a graph: on a capturing
+// stream it is refused (EGM_ERR_NOT_SUPPORTED) and the plan stays pending.
+// Executes from several threads run the tuning once.
+egm_status_t tune_if_pending(egm_plan_s* p, const void* A, const void* B, void* D, void* aux, void* ws,
+                             hipStream_t s) {
+  if (!p->autotune_pending.load(std::memory_order_acquire)) return EGM_OK;
+  hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+  if (hipStreamIsCapturing(s, &cs) != hipSuccess) return EGM_ERR_HIP;
+  if (cs != hipStreamCaptureStatusNone) return EGM_ERR_NOT_SUPPORTED;
+  std::lock_guard<std::mutex> lock(p->tune_mu);
+  if (!p->autotune_pending.load(std::memory_order_acquire)) return EGM_OK;
+  return autotune(p, A, B, D, aux, ws, s) == hipSuccess ? EGM_OK : EGM_ERR_HIP;
 }
 
 // Validation and construction shared by egm_plan (f8 = 0) and egm_plan_fp8.
@@ -327,9 +386,13 @@ egm_status_t plan_impl(egm_plan_t* out, int64_t m, int64_t n, int64_t k, egm_dty
     group_m = opt->group_m;
   }
 
-  egm_plan_s* p = new (std::nothrow) egm_plan_s();
-  if (p == nullptr) return EGM_ERR_NO_MEMORY;
-  p->magic = kPlanMagic;
+  std::shared_ptr<egm_plan_s> owner;
+  try {
+    owner = std::make_shared<egm_plan_s>();
+  } catch (const std::bad_alloc&) {
+    return EGM_ERR_NO_MEMORY;
+  }
+  egm_plan_s* p = owner.get();
   p->m = m;
   p->n = n;
   p->k = k;
@@ -347,10 +410,7 @@ egm_status_t plan_impl(egm_plan_t* out, int64_t m, int64_t n, int64_t k, egm_dty
   p->config = force >= 0 ? force : choose_config(m, n, k);
   // the launch must fit one grid dimension (autotuning tries only the
   // configs that fit, and the per-shape choice always fits)
-  if (p->config < 0 || !grid_fits(m, n, p->config)) {
-    delete p;
-    return EGM_ERR_NOT_SUPPORTED;
-  }
+  if (p->config < 0 || !grid_fits(m, n, p->config)) return EGM_ERR_NOT_SUPPORTED;
   p->group_m = group_m;
   p->autotune_pending = tune;
   // workspace: the two-kernel path's product P, then (DRELU_BGRAD) the fp32
@@ -371,7 +431,11 @@ egm_status_t plan_impl(egm_plan_t* out, int64_t m, int64_t n, int64_t k, egm_dty
     describe(p, buf, sizeof(buf));
     std::fprintf(stderr, "[egm] plan: %s\n", buf);
   }
-  *out = p;
+  try {
+    *out = register_plan(std::move(owner));
+  } catch (const std::bad_alloc&) {
+    return EGM_ERR_NO_MEMORY;
+  }
   return EGM_OK;
 }
 
@@ -398,8 +462,9 @@ egm_status_t egm_plan_fp8(egm_plan_t* out, int64_t m, int64_t n, int64_t k, egm_
 
 egm_status_t egm_execute(egm_plan_t plan, const void* A, const void* B, void* D, void* aux, void* workspace,
                          size_t workspace_bytes, void* stream) {
-  if (!valid_plan(plan)) return EGM_ERR_INVALID_PLAN;
-  egm_plan_s* p = plan;
+  const std::shared_ptr<egm_plan_s> ref = lookup(plan);
+  if (ref == nullptr) return EGM_ERR_INVALID_PLAN;
+  egm_plan_s* p = ref.get();
   const bool need_aux = p->epilog == EGM_EPILOG_RELU_AUX_BIAS || p->epilog == EGM_EPILOG_DRELU ||
                         p->epilog == EGM_EPILOG_DRELU_BGRAD;
   const bool empty = p->m == 0 || p->n == 0;
@@ -430,20 +495,18 @@ egm_status_t egm_execute(egm_plan_t plan, const void* A, const void* B, void* D,
   if (std::getenv("EGM_FAIL_INJECT") != nullptr && std::strcmp(std::getenv("EGM_FAIL_INJECT"), "launch") == 0)
     return EGM_ERR_HIP;  // host-forced launch-error path, for tests of the error handling
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
-  hipError_t err;
-  if (p->autotune_pending) {
-    err = autotune(p, A, B, D, aux, workspace, s);
-    if (err != hipSuccess) return EGM_ERR_HIP;
-  }
-  err = launch_plan(p, p->config, A, B, D, aux, workspace, s);
+  const egm_status_t tuned = tune_if_pending(p, A, B, D, aux, workspace, s);
+  if (tuned != EGM_OK) return tuned;
+  const hipError_t err = launch_plan(p, p->config, A, B, D, aux, workspace, s);
   return err == hipSuccess ? EGM_OK : EGM_ERR_HIP;
 }
 
 egm_status_t egm_execute_strided(egm_plan_t plan, int64_t batch, const void* A, int64_t stride_a, const void* B,
                                  int64_t stride_b, void* D, int64_t stride_d, void* aux, int64_t stride_aux,
                                  void* stream) {
-  if (!valid_plan(plan)) return EGM_ERR_INVALID_PLAN;
-  egm_plan_s* p = plan;
+  const std::shared_ptr<egm_plan_s> ref = lookup(plan);
+  if (ref == nullptr) return EGM_ERR_INVALID_PLAN;
+  egm_plan_s* p = ref.get();
   if (batch < 0 || batch > 65535) return EGM_ERR_INVALID_VALUE;
   if (!p->fused || p->epilog == EGM_EPILOG_DRELU_BGRAD) return EGM_ERR_NOT_SUPPORTED;
   const bool need_aux = p->epilog == EGM_EPILOG_RELU_AUX_BIAS || p->epilog == EGM_EPILOG_DRELU;
@@ -462,33 +525,36 @@ egm_status_t egm_execute_strided(egm_plan_t plan, int64_t batch, const void* A, 
       (stride_a * es) % 16 != 0 || (stride_b * es) % 16 != 0 || (stride_d * 2) % 16 != 0 || stride_aux % 16 != 0)
     return EGM_ERR_ALIGNMENT;
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
-  hipError_t err;
-  if (p->autotune_pending) {  // tuned on the first problem
-    err = autotune(p, A, B, D, aux, nullptr, s);
-    if (err != hipSuccess) return EGM_ERR_HIP;
-  }
-  err = launch_plan(p, p->config, A, B, D, aux, nullptr, s, Batch{batch, stride_a, stride_b, stride_d, stride_aux});
+  // tuned on the first problem
+  const egm_status_t tuned = tune_if_pending(p, A, B, D, aux, nullptr, s);
+  if (tuned != EGM_OK) return tuned;
+  const hipError_t err =
+      launch_plan(p, p->config, A, B, D, aux, nullptr, s, Batch{batch, stride_a, stride_b, stride_d, stride_aux});
   return err == hipSuccess ? EGM_OK : EGM_ERR_HIP;
 }
 
 egm_status_t egm_free(egm_plan_t plan) {
   if (plan == nullptr) return EGM_OK;
-  if (plan->magic != kPlanMagic) return EGM_ERR_INVALID_PLAN;
-  plan->magic = kFreedMagic;
-  delete plan;
-  return EGM_OK;
+  return unregister(plan) ? EGM_OK : EGM_ERR_INVALID_PLAN;
 }
 
-size_t egm_plan_workspace_bytes(egm_plan_t plan) { return valid_plan(plan) ? plan->workspace_bytes : 0; }
+size_t egm_plan_workspace_bytes(egm_plan_t plan) {
+  const std::shared_ptr<egm_plan_s> p = lookup(plan);
+  return p != nullptr ? p->workspace_bytes : 0;
+}
 
 egm_status_t egm_plan_describe(egm_plan_t plan, char* buf, size_t len) {
-  if (!valid_plan(plan)) return EGM_ERR_INVALID_PLAN;
+  const std::shared_ptr<egm_plan_s> p = lookup(plan);
+  if (p == nullptr) return EGM_ERR_INVALID_PLAN;
   if (buf == nullptr || len == 0) return EGM_ERR_INVALID_VALUE;
-  describe(plan, buf, len);
+  describe(p.get(), buf, len);
   return EGM_OK;
 }
 
-int32_t egm_plan_config(egm_plan_t plan) { return valid_plan(plan) ? plan->config : -1; }
+int32_t egm_plan_config(egm_plan_t plan) {
+  const std::shared_ptr<egm_plan_s> p = lookup(plan);
+  return p != nullptr ? p->config.load(std::memory_order_relaxed) : -1;
+}
 
 int32_t egm_num_configs(void) { return kNumConfigs; }
 
@@ -509,7 +575,7 @@ const char* egm_status_string(egm_status_t s) {
     case EGM_ERR_SHAPE: return "EGM_ERR_SHAPE: invalid shape (dims >= 0, n and k multiples of 8 (16 for fp8), n,k <= 2^21)";
     case EGM_ERR_DTYPE: return "EGM_ERR_DTYPE: dtype must be fp16 or bf16";
     case EGM_ERR_ALIGNMENT: return "EGM_ERR_ALIGNMENT: device pointers must be 16-byte aligned";
-    case EGM_ERR_INVALID_PLAN: return "EGM_ERR_INVALID_PLAN: invalid or freed plan";
+    case EGM_ERR_INVALID_PLAN: return "EGM_ERR_INVALID_PLAN: NULL, freed or foreign plan handle";
     case EGM_ERR_HIP: return "EGM_ERR_HIP: HIP runtime error at launch";
     case EGM_ERR_NO_MEMORY: return "EGM_ERR_NO_MEMORY: host allocation failed";
     case EGM_ERR_WORKSPACE: return "EGM_ERR_WORKSPACE: workspace missing or too small";

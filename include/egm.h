@@ -37,8 +37,9 @@
  * implicit dtype conversion.  egm_execute is asynchronous and stream-ordered:
  * it returns EGM_ERR_HIP only when the launch itself fails; a device fault
  * shows at the caller's next synchronisation of the stream.  Plans are
- * immutable after egm_plan, so executes of one plan on several streams may
- * overlap (their outputs must not).
+ * immutable after egm_plan (but for the one-time choice of a pending
+ * autotune), so executes of one plan on several streams may overlap (their
+ * outputs must not).
  */
 #ifndef EGM_H_
 #define EGM_H_
@@ -50,9 +51,19 @@
 extern "C" {
 #endif
 
-#define EGM_ABI_VERSION 6
+#define EGM_ABI_VERSION 7
 
-typedef enum egm_status_t {
+/* Every enum of this interface is int32_t-sized.  A C caller may pass any
+ * int32_t where one is expected (unknown values are rejected with a status);
+ * the C++ side fixes the underlying type so that such values are well-defined
+ * there too. */
+#ifdef __cplusplus
+#define EGM_ENUM(name) enum name : int32_t
+#else
+#define EGM_ENUM(name) enum name
+#endif
+
+typedef EGM_ENUM(egm_status_t) {
   EGM_OK = 0,
   EGM_ERR_INVALID_VALUE = 1, /* NULL pointer, unknown enum, bad option */
   EGM_ERR_NOT_SUPPORTED = 2, /* valid request outside what v1 implements */
@@ -65,13 +76,13 @@ typedef enum egm_status_t {
   EGM_ERR_WORKSPACE = 9      /* workspace missing or smaller than egm_plan_workspace_bytes */
 } egm_status_t;
 
-typedef enum egm_dtype_t {
+typedef EGM_ENUM(egm_dtype_t) {
   EGM_F16 = 0,  /* IEEE binary16 */
   EGM_BF16 = 1  /* bfloat16 (upper half of binary32) */
 } egm_dtype_t;
 
 /* fp8 operand formats of egm_plan_fp8 (the OCP 8-bit floats gfx950 implements). */
-typedef enum egm_fp8_format_t {
+typedef EGM_ENUM(egm_fp8_format_t) {
   EGM_E4M3 = 0, /* 4 exponent bits (bias 7), 3 mantissa bits; no infinities; largest 448 */
   EGM_E5M2 = 1  /* 5 exponent bits (bias 15), 2 mantissa bits; IEEE inf / NaN; largest 57344 */
 } egm_fp8_format_t;
@@ -102,7 +113,7 @@ typedef enum egm_fp8_format_t {
  *                  egm_epilog_inputs_t.bias_grad
  * No bias is added in either backward epilogue.
  */
-typedef enum egm_epilog_t {
+typedef EGM_ENUM(egm_epilog_t) {
   EGM_EPILOG_DEFAULT = 0,
   EGM_EPILOG_BIAS = 1,
   EGM_EPILOG_RELU_BIAS = 2,
@@ -115,7 +126,7 @@ typedef enum egm_epilog_t {
 
 /* Bias shapes accepted by the pages ([bias-fusion] body, shape item of the
  * checklist): (m,1) adds bias[i] to row i, (1,n) adds bias[j] to column j. */
-typedef enum egm_bias_layout_t {
+typedef EGM_ENUM(egm_bias_layout_t) {
   EGM_BIAS_NONE = 0,
   EGM_BIAS_ROW = 1, /* shape (m,1): m elements */
   EGM_BIAS_COL = 2  /* shape (1,n): n elements */
@@ -140,9 +151,15 @@ typedef struct egm_plan_options_t {
                             workspace, a second kernel applies the epilogue). */
   int32_t force_config;  /* -1 (default): per-shape choice; else a tile-config id
                             0 .. egm_num_configs()-1 */
-  int32_t autotune;      /* 0 (default); 1: time every tile config on the first
-                            execute and keep the fastest (that execute is not
-                            thread-safe) */
+  int32_t autotune;      /* 0 (default); 1: the first execute times every tile
+                            config that fits on the caller's stream and
+                            buffers (each launched 4 times), keeps the fastest,
+                            then launches it: that execute waits on the host
+                            for the timings, and on a stream that is being
+                            captured into a graph it returns
+                            EGM_ERR_NOT_SUPPORTED with the plan still pending
+                            (run it once before capture).  Concurrent first
+                            executes tune once. */
   int32_t group_m;       /* 0 (default): per-shape choice; else tile rows per
                             L2-sharing group in the workgroup order */
   int32_t b_transposed;  /* 0 (default): B is [k,n] row-major.  1: B is given
@@ -204,7 +221,10 @@ egm_status_t egm_plan_fp8(egm_plan_t* out, int64_t m, int64_t n, int64_t k, egm_
                           const egm_plan_options_t* opt);
 
 /*
- * egm_execute - enqueue the plan on a HIP stream (asynchronous).
+ * egm_execute - enqueue the plan on a HIP stream (asynchronous)
+ * ([bias-fusion] body, code example: execute() after plan(); [bindings] body,
+ * checklist item 2: execute is non-blocking and ordered on the caller's
+ * stream, which the caller synchronises).
  *   A     [m,k] device, row-major.          B [k,n] device, row-major ([n,k] row-major
  *         with the b_transposed option).
  *   D     [m,n] device, row-major output.
@@ -222,6 +242,12 @@ egm_status_t egm_plan_fp8(egm_plan_t* out, int64_t m, int64_t n, int64_t k, egm_
  * the bias gradient must not alias anything else.  DRELU_BGRAD is two
  * launches on the stream (the GEMM with its per-tile sums, then their
  * reduction); the result is deterministic for a given plan.
+ * Errors: EGM_ERR_INVALID_PLAN for a NULL, freed or foreign handle;
+ * EGM_ERR_INVALID_VALUE for a missing or unexpected aux, D or operand;
+ * EGM_ERR_WORKSPACE; EGM_ERR_ALIGNMENT; EGM_ERR_HIP if a launch fails;
+ * EGM_ERR_NOT_SUPPORTED for a pending autotune on a capturing stream (see
+ * egm_plan_options_t.autotune).  Nothing is enqueued on an error found by the
+ * host checks.
  */
 egm_status_t egm_execute(egm_plan_t plan, const void* A, const void* B, void* D, void* aux,
                          void* workspace, size_t workspace_bytes, void* stream);
@@ -271,11 +297,18 @@ egm_status_t egm_layernorm(int64_t rows, int64_t cols, egm_dtype_t dtype, const 
                            const void* gamma, const void* beta, float eps, void* y, float* mean, float* rstd,
                            void* stream);
 
-/* egm_free - release a plan.  NULL is accepted (EGM_OK).  A plan must not be
- * used after it is freed; work already enqueued is unaffected. */
+/* egm_free - release a plan ([bias-fusion] body, checklist: free() releases
+ * the plan's resources).  NULL is accepted (EGM_OK).  Handles are never
+ * reused: after egm_free, the handle gives EGM_ERR_INVALID_PLAN in every call,
+ * a second egm_free included.  Work already enqueued is unaffected; a call of
+ * the same plan still running in another thread finishes with the plan. */
 egm_status_t egm_free(egm_plan_t plan);
 
-/* Bytes of workspace egm_execute needs for this plan (0 if the plan is invalid). */
+/* Bytes of workspace egm_execute needs for this plan (0 if the handle is NULL,
+ * freed or foreign).  The workspace is the caller-owned scratch that stands in
+ * for the memory the library would otherwise allocate: the two-kernel path's
+ * intermediate product ([bias-fusion] body: the unfused form's extra global
+ * write and read) and the bias gradient's per-tile partial sums. */
 size_t egm_plan_workspace_bytes(egm_plan_t plan);
 
 /* Write a one-line description of the chosen configuration into buf (always
@@ -283,17 +316,26 @@ size_t egm_plan_workspace_bytes(egm_plan_t plan);
  * algorithm choice).  EGM_LOG=1 in the environment also prints it at plan time. */
 egm_status_t egm_plan_describe(egm_plan_t plan, char* buf, size_t len);
 
-/* Tile-config id the plan will launch (after autotune, the chosen one), or -1. */
+/* Tile-config id the plan will launch (after autotune, the chosen one), or -1
+ * for a NULL, freed or foreign handle ([bindings] body, checklist item 3: the
+ * algorithm choice can be inspected). */
 int32_t egm_plan_config(egm_plan_t plan);
 
-/* Number of tile configurations, and a description of one of them. */
+/* Number of tile configurations, and a description of one of them (the
+ * candidates plan() chooses among: [bindings] body, checklist item 2).
+ * egm_config_describe gives EGM_ERR_INVALID_VALUE for an unknown id or an
+ * empty buffer; the text is always NUL-terminated when len > 0. */
 int32_t egm_num_configs(void);
 egm_status_t egm_config_describe(int32_t config, char* buf, size_t len);
 
-/* Static text for a status code (never NULL). */
+/* Static text for a status code, any int32_t value (never NULL); the pages'
+ * interface reports failures as errors ([bias-fusion] body, checklist: a dtype
+ * mismatch or a bad bias shape is an error), which this C interface returns
+ * as the status codes above. */
 const char* egm_status_string(egm_status_t status);
 
-/* EGM_ABI_VERSION of the built library. */
+/* EGM_ABI_VERSION of the built library (a caller compares it with the header
+ * it was compiled against). */
 int32_t egm_abi_version(void);
 
 #ifdef __cplusplus

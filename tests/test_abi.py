@@ -32,7 +32,7 @@ def test_every_declared_symbol_is_exported():
 
 
 def test_abi_version_and_status_strings():
-    assert egm.egm_abi_version() == 6
+    assert egm.egm_abi_version() == 7
     for s in range(10):
         assert egm.status_string(s).startswith("EGM_")
     assert "unknown" in egm.status_string(12345)
@@ -111,6 +111,39 @@ def test_free_and_invalid_handles():
     assert egm.egm_plan_workspace_bytes(0) == 0
     assert egm.egm_plan_config(0) == -1
     assert egm.LIB.egm_plan_describe(None, ctypes.create_string_buffer(8), 8) == egm.EGM_ERR_INVALID_PLAN
+
+
+def test_freed_handles_are_rejected_and_never_reused():
+    """A freed handle is refused by every call (double free included) without
+    the library touching the freed plan; a later plan gets a new handle."""
+    h = egm.egm_plan(64, 64, 64, F16, E["BIAS"], FAKE, ROW)
+    assert egm.egm_free(h, raw_status=True) == egm.EGM_OK
+    assert egm.egm_free(h, raw_status=True) == egm.EGM_ERR_INVALID_PLAN
+    assert egm.egm_execute(h, FAKE, FAKE, FAKE, raw_status=True) == egm.EGM_ERR_INVALID_PLAN
+    assert egm.egm_execute_strided(h, 1, FAKE, 0, FAKE, 0, FAKE, 0, raw_status=True) == egm.EGM_ERR_INVALID_PLAN
+    assert egm.egm_plan_workspace_bytes(h) == 0
+    assert egm.egm_plan_config(h) == -1
+    assert egm.LIB.egm_plan_describe(h, ctypes.create_string_buffer(64), 64) == egm.EGM_ERR_INVALID_PLAN
+    seen = {h}
+    for _ in range(64):
+        h2 = egm.egm_plan(64, 64, 64, F16, E["BIAS"], FAKE, ROW)
+        assert h2 not in seen
+        seen.add(h2)
+        assert egm.egm_free(h2, raw_status=True) == egm.EGM_OK
+    # a foreign value that was never a handle
+    for bogus in (1, 0x1008, FAKE):
+        assert egm.egm_free(bogus, raw_status=True) == egm.EGM_ERR_INVALID_PLAN
+        assert egm.egm_plan_config(bogus) == -1
+
+
+def test_out_of_range_enum_values_are_rejected():
+    """Any int32 may arrive where an enum is expected; unknown ones give a status."""
+    for dt in (2, -1, 1 << 30):
+        assert plan_status(dtype=dt) == egm.EGM_ERR_DTYPE
+    for ep in (8, -7, 1 << 30):
+        assert plan_status(epilog=ep) == egm.EGM_ERR_INVALID_VALUE
+    for st in (10, -1, (1 << 31) - 1):
+        assert "unknown" in egm.status_string(st)
 
 
 def test_workspace_and_describe():
