@@ -9,10 +9,14 @@ up- and down-projection launches).  The deliberately unfused two-kernel path
 is timed the same way in the same run for the fused-vs-unfused speedup.
 
 The large shapes run the MI355X at its board power limit, where the clock
-settles only after the first launches; so, unless given, the warm-up covers
-about 1.5 s and the timed region about 2 s of work (step counts derived from
-one probe step).  The timed region is exactly K steps; the speedup comes from
-further alternating unfused / fused legs of K steps each.
+settles only after about a second of load; so every run first pre-heats with
+1.5 s of fused steps (reported as preheat_s, also when --warmup is given),
+then runs the W warm-up steps (unless given: about 1.5 s of work) and the
+timed region (unless given: about 2 s of work; step counts derived from one
+probe step).  The timed region is exactly K steps (ms_per_step is their mean);
+a second leg of K steps with an event between consecutive steps gives the
+median; the speedup comes from further alternating unfused / fused legs of K
+steps each.
 
 Prints ONE JSON line: metric = fused TFLOP/s (value), % of the fp16/bf16 dense
 MFMA peak (roofline.frac), fused vs unfused speedup; roofline of the dominant
@@ -26,6 +30,7 @@ import argparse
 import hashlib
 import json
 import os
+import statistics
 import sys
 import time
 
@@ -265,10 +270,18 @@ def main():
     warmup = args.warmup if args.warmup is not None else max(3, int(1500.0 / max(probe_ms, 1e-3)))
     steps = args.steps if args.steps is not None else max(10, int(2000.0 / max(probe_ms, 1e-3)))
     args.warmup, args.steps = warmup, steps
+    # Pre-heat, always (also when --warmup is given): the board needs about a
+    # second of load to reach its steady power and clock, so a short timed
+    # region that follows only a few warm-up steps would time the ramp.
+    preheat_s = preheat(lambda: step(fused_plans), probe_ms, PREHEAT_SECONDS, dev)
     for _ in range(warmup):
         step(fused_plans)
     # the timed region: exactly `steps` fused steps
     fused_ms, fused_wall = timed(fused_plans, steps, 0)
+    # per-step event times in a leg of the same length right after it (events
+    # between the steps of the timed region itself would add host work to
+    # every launch of the small workloads): their median and spread
+    per_step = per_step_ms(lambda: step(fused_plans), steps, stream, dev)
     # fused-vs-unfused: alternating legs of the same length after it
     unfused_legs, fused_legs = [], [fused_ms]
     for _ in range(2):
@@ -324,6 +337,9 @@ def main():
                      "kernel": f"gemm_epilogue_kernel {dm}x{dn}x{dk} {dom[3]}",
                      "avg_launch_ms": round(dom_ms, 4), "flops_per_launch": dom_flops,
                      "algorithmic_bytes_per_launch": algorithmic_bytes(dm, dn, dk, dom[3], dom[4], ob)},
+        "median_ms_per_step": round(statistics.median(per_step), 4),
+        "per_step_ms_min_max": [round(min(per_step), 4), round(max(per_step), 4)],
+        "preheat_s": round(preheat_s, 2),
         "setup_s": round(setup_s, 1),
         "timed_wall_s": round(fused_wall, 3),
     }
@@ -345,6 +361,68 @@ def main():
     for mm, *_ in fused_plans + unfused_plans:
         mm.free()
     print(json.dumps(result), flush=True)
+
+
+PREHEAT_SECONDS = 1.5
+
+
+def preheat(run_step, probe_ms, seconds, dev):
+    """Run steps back to back for at least ``seconds`` of wall time (in
+    batches of about 50 ms of GPU work, synchronising between batches so the
+    queue never runs far ahead); returns the seconds spent."""
+    import torch
+    batch = max(1, int(50.0 / max(probe_ms, 1e-3)))
+    t0 = time.perf_counter()
+    while time.perf_counter() - t0 < seconds:
+        for _ in range(batch):
+            run_step()
+        torch.cuda.synchronize(dev)
+    return time.perf_counter() - t0
+
+
+def per_step_ms(run_step, steps, stream, dev):
+    """Event time of each of ``steps`` back-to-back steps (one event between
+    consecutive steps, recorded on the launch stream)."""
+    import torch
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
+    ev[0].record(stream)
+    for i in range(steps):
+        run_step()
+        ev[i + 1].record(stream)
+    torch.cuda.synchronize(dev)
+    return [ev[i].elapsed_time(ev[i + 1]) for i in range(steps)]
+
+
+def host_description():
+    """CPU model (with family / model numbers, since virtual machines may
+    report a generic name) and numpy's BLAS library and thread count."""
+    info = {}
+    try:
+        with open("/proc/cpuinfo") as f:
+            for ln in f:
+                key, _, val = ln.partition(":")
+                key = key.strip()
+                if key in ("model name", "cpu family", "model") and key not in info:
+                    info[key] = val.strip()
+                if len(info) == 3:
+                    break
+    except OSError:  # pragma: no cover
+        pass
+    cpu = info.get("model name")
+    if cpu is not None and ("cpu family" in info or "model" in info):
+        cpu = f"{cpu} (family {info.get('cpu family', '?')}, model {info.get('model', '?')})"
+    blas = None
+    try:
+        import numpy  # noqa: F401  (loads its BLAS, which threadpoolctl then sees)
+        from threadpoolctl import threadpool_info
+        libs = [i for i in threadpool_info() if i.get("user_api") == "blas"]
+        if libs:
+            i = libs[0]
+            blas = (f"{i.get('internal_api')} {i.get('version')} ({i.get('prefix')}, kernels for "
+                    f"{i.get('architecture')}, {i.get('num_threads')} threads)")
+    except Exception:  # pragma: no cover
+        pass
+    return cpu, blas
 
 
 def torch_context(specs, timed, steps, warmup, flops):
@@ -802,7 +880,9 @@ def _cpu_baseline_backward(name, ops, keep, target_s, cores):
     sel = gpu_d.index_select(0, torch.from_numpy(rows).to(gpu_d.device)).cpu()
     d = eo.widen(sel.view(torch.int16).numpy().view(np.uint16), ops.dtype)
     flops = 2.0 * len(rows) * ops.n * ops.k
+    cpu_model, blas = host_description()
     return {"value": round(flops / secs / 1e12, 4), "unit": "TFLOP/s", "cores": int(cores), "kind": "oracle",
+            "cpu": cpu_model, "blas": blas,
             "sample": f"{len(rows)} of {ops.m} output rows x all {ops.n} columns (k={ops.k}), DRELU part of "
                       f"{W.BACKWARD_WORKLOADS[name].epilogs[-1]}, fp64 numpy oracle; {secs:.1f} s",
             "seconds": round(secs, 2), "parity_max_abs_err": float(np.abs(d - dz).max()),
@@ -839,7 +919,9 @@ def _cpu_baseline_fp8(name, ops, keep, target_s, cores):
     sel = gpu_d.index_select(0, torch.from_numpy(rows).to(gpu_d.device)).cpu()
     d = eo.widen(sel.view(torch.int16).numpy().view(np.uint16), ops.out_dtype)
     flops = 2.0 * len(rows) * ops.n * ops.k
+    cpu_model, blas = host_description()
     return {"value": round(flops / secs / 1e12, 4), "unit": "TFLOP/s", "cores": int(cores), "kind": "oracle",
+            "cpu": cpu_model, "blas": blas,
             "sample": f"{len(rows)} of {ops.m} output rows x all {ops.n} columns (k={ops.k}), {epilog} on "
                       f"{ops.a_fmt} x {ops.b_fmt} operands, fp64 numpy oracle; {secs:.1f} s",
             "seconds": round(secs, 2), "parity_max_abs_err": float(np.abs(d - y).max()),
@@ -889,14 +971,9 @@ def cpu_baseline(name, ops, keep, target_s):
     y, _, _ = eo.reference(a, b, dtype, epilog, bias, layout, rows=rows)
     secs = time.perf_counter() - t0
     flops = 2.0 * len(rows) * n * k
-    cpu_model = None
-    try:
-        with open("/proc/cpuinfo") as f:
-            cpu_model = next((ln.split(":", 1)[1].strip() for ln in f if ln.startswith("model name")), None)
-    except OSError:  # pragma: no cover
-        pass
+    cpu_model, blas = host_description()
     out = {"value": round(flops / secs / 1e12, 4), "unit": "TFLOP/s", "cores": int(cores), "kind": "oracle",
-           "cpu": cpu_model, "full_workload_seconds_extrapolated": round(secs * m / len(rows), 1),
+           "cpu": cpu_model, "blas": blas, "full_workload_seconds_extrapolated": round(secs * m / len(rows), 1),
            "sample": f"{len(rows)} of {m} output rows x all {n} columns (k={k}), {epilog}, fp64 numpy oracle; "
                      f"{secs:.1f} s",
            "seconds": round(secs, 2)}
