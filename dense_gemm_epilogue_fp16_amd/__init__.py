@@ -36,6 +36,10 @@ EGM_ERR_INVALID_PLAN = 6
 EGM_ERR_HIP = 7
 EGM_ERR_NO_MEMORY = 8
 EGM_ERR_WORKSPACE = 9
+EGM_ERR_SCRATCH_LIMIT = 10
+
+#: bytes of the static scratch behind egm_execute_no_alloc (per GPU)
+EGM_NO_ALLOC_SCRATCH_BYTES = 32 << 20
 
 # dtypes (egm_dtype_t)
 EGM_F16 = 0
@@ -65,7 +69,8 @@ EGM_BIAS_COL = 2  # shape (1, n)
 
 #: every symbol include/egm.h declares
 EXPORTS = (
-    "egm_plan", "egm_plan_fp8", "egm_execute", "egm_execute_strided", "egm_layernorm", "egm_free",
+    "egm_plan", "egm_plan_fp8", "egm_execute", "egm_execute_no_alloc", "egm_execute_strided", "egm_layernorm",
+    "egm_free",
     "egm_plan_workspace_bytes",
     "egm_plan_describe",
     "egm_plan_config", "egm_num_configs", "egm_config_describe", "egm_status_string", "egm_abi_version",
@@ -110,6 +115,8 @@ def _load() -> ctypes.CDLL:
     lib.egm_plan_fp8.restype = i32
     lib.egm_execute.argtypes = [vp, vp, vp, vp, vp, vp, sz, vp]
     lib.egm_execute.restype = i32
+    lib.egm_execute_no_alloc.argtypes = [vp, vp, vp, vp, vp, vp]
+    lib.egm_execute_no_alloc.restype = i32
     lib.egm_execute_strided.argtypes = [vp, i64, vp, i64, vp, i64, vp, i64, vp, i64, vp]
     lib.egm_execute_strided.restype = i32
     lib.egm_layernorm.argtypes = [i64, i64, i32, vp, vp, vp, vp, ctypes.c_float, vp, vp, vp, vp]
@@ -188,6 +195,17 @@ def egm_execute(plan: int, A: int, B: int, D: int, aux: int = 0, workspace: int 
     if raw_status:
         return st
     _check(st, "egm_execute")
+    return None
+
+
+def egm_execute_no_alloc(plan: int, A: int, B: int, D: int, aux: int = 0, stream: int = 0,
+                         raw_status: bool = False):
+    """egm_execute with the library's static scratch as the workspace (no
+    device allocation anywhere on the call)."""
+    st = LIB.egm_execute_no_alloc(plan, A or None, B or None, D or None, aux or None, stream or None)
+    if raw_status:
+        return st
+    _check(st, "egm_execute_no_alloc")
     return None
 
 

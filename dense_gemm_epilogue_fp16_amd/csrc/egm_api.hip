@@ -439,6 +439,90 @@ egm_status_t plan_impl(egm_plan_t* out, int64_t m, int64_t n, int64_t k, egm_dty
   return EGM_OK;
 }
 
+// Scratch of egm_execute_no_alloc: the workspace (the two-kernel path's
+// product, the bias gradient's per-tile partial sums) for callers that cannot
+// allocate device memory.  Each GPU that runs the library holds its own copy
+// until the process ends.  Host code never passes this name to a kernel or a
+// copy (on the host it is only a stand-in for the symbol): it uses the
+// device address that scratch_address() obtains once per device.
+static __device__ __align__(256) uint8_t scratch[EGM_NO_ALLOC_SCRATCH_BYTES];
+
+constexpr int kMaxDevices = 64;
+
+// Device address of `scratch` on the calling thread's current device, looked
+// up on the first call from that device (with it current) and kept.
+hipError_t scratch_address(void** out) {
+  static std::mutex mu;
+  static void* addr[kMaxDevices] = {};
+  int dev = -1;
+  hipError_t err = hipGetDevice(&dev);
+  if (err != hipSuccess) return err;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(mu);
+  if (addr[dev] == nullptr) {
+    void* ptr = nullptr;
+    err = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (err != hipSuccess) return err;
+    if (ptr == nullptr) return hipErrorInvalidSymbol;
+    addr[dev] = ptr;
+  }
+  *out = addr[dev];
+  return hipSuccess;
+}
+
+// egm_execute (own_scratch = false: the caller's workspace) and
+// egm_execute_no_alloc (own_scratch = true: the library's static scratch on
+// the current device, which the stream must belong to).
+egm_status_t execute_impl(egm_plan_s* p, const void* A, const void* B, void* D, void* aux, void* workspace,
+                          size_t workspace_bytes, void* stream, bool own_scratch) {
+  // (own_scratch: the workspace arguments are unused)
+  const bool need_aux = p->epilog == EGM_EPILOG_RELU_AUX_BIAS || p->epilog == EGM_EPILOG_DRELU ||
+                        p->epilog == EGM_EPILOG_DRELU_BGRAD;
+  const bool empty = p->m == 0 || p->n == 0;
+  // an empty problem has an empty mask, which may come as NULL
+  if (need_aux ? (aux == nullptr && !empty) : aux != nullptr) return EGM_ERR_INVALID_VALUE;
+  if (own_scratch) {
+    if (p->workspace_bytes > size_t(EGM_NO_ALLOC_SCRATCH_BYTES)) return EGM_ERR_SCRATCH_LIMIT;
+    // tuning creates and waits on events
+    if (p->autotune_pending.load(std::memory_order_acquire)) return EGM_ERR_NOT_SUPPORTED;
+  } else if (p->workspace_bytes > 0 && (workspace == nullptr || workspace_bytes < p->workspace_bytes)) {
+    return EGM_ERR_WORKSPACE;
+  }
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  if (empty) {
+    // empty output: nothing to compute, but a bias gradient of a non-empty
+    // axis is a sum of nothing: zeros
+    // (written by the finish kernel over zero chunks, not a memset, so the
+    // call stays capturable in a graph)
+    if (p->bias_grad != nullptr && p->grad_len > 0) {
+      if (!aligned16(p->bias_grad)) return EGM_ERR_ALIGNMENT;
+      int64_t blocks = cdiv(p->grad_len, 64);
+      if (blocks > 4096) blocks = 4096;
+      egm::launch_bias_grad_finish(dim3(uint32_t(blocks)), s, nullptr, 0, p->grad_len,
+                                   static_cast<float*>(p->bias_grad));
+      return hipGetLastError() == hipSuccess ? EGM_OK : EGM_ERR_HIP;
+    }
+    return EGM_OK;
+  }
+  if (D == nullptr) return EGM_ERR_INVALID_VALUE;
+  if (p->k > 0 && (A == nullptr || B == nullptr)) return EGM_ERR_INVALID_VALUE;
+  if ((A && !aligned16(A)) || (B && !aligned16(B)) || !aligned16(D) || (aux && !aligned16(aux)) ||
+      (!own_scratch && p->workspace_bytes > 0 && !aligned16(workspace)))
+    return EGM_ERR_ALIGNMENT;
+  if (std::getenv("EGM_FAIL_INJECT") != nullptr && std::strcmp(std::getenv("EGM_FAIL_INJECT"), "launch") == 0)
+    return EGM_ERR_HIP;  // host-forced launch-error path, for tests of the error handling
+  if (own_scratch && p->workspace_bytes > 0) {
+    int cur = -1, sdev = -1;
+    if (hipGetDevice(&cur) != hipSuccess || hipStreamGetDevice(s, &sdev) != hipSuccess) return EGM_ERR_HIP;
+    if (sdev != cur) return EGM_ERR_INVALID_VALUE;  // the scratch used is the current device's
+    if (scratch_address(&workspace) != hipSuccess) return EGM_ERR_HIP;
+  }
+  const egm_status_t tuned = tune_if_pending(p, A, B, D, aux, workspace, s);
+  if (tuned != EGM_OK) return tuned;
+  const hipError_t err = launch_plan(p, p->config, A, B, D, aux, workspace, s);
+  return err == hipSuccess ? EGM_OK : EGM_ERR_HIP;
+}
+
 }  // namespace
 
 extern "C" {
@@ -464,41 +548,14 @@ egm_status_t egm_execute(egm_plan_t plan, const void* A, const void* B, void* D,
                          size_t workspace_bytes, void* stream) {
   const std::shared_ptr<egm_plan_s> ref = lookup(plan);
   if (ref == nullptr) return EGM_ERR_INVALID_PLAN;
-  egm_plan_s* p = ref.get();
-  const bool need_aux = p->epilog == EGM_EPILOG_RELU_AUX_BIAS || p->epilog == EGM_EPILOG_DRELU ||
-                        p->epilog == EGM_EPILOG_DRELU_BGRAD;
-  const bool empty = p->m == 0 || p->n == 0;
-  // an empty problem has an empty mask, which may come as NULL
-  if (need_aux ? (aux == nullptr && !empty) : aux != nullptr) return EGM_ERR_INVALID_VALUE;
-  if (p->workspace_bytes > 0 && (workspace == nullptr || workspace_bytes < p->workspace_bytes))
-    return EGM_ERR_WORKSPACE;
-  if (empty) {
-    // empty output: nothing to compute, but a bias gradient of a non-empty
-    // axis is a sum of nothing: zeros
-    // (written by the finish kernel over zero chunks, not a memset, so the
-    // call stays capturable in a graph)
-    if (p->bias_grad != nullptr && p->grad_len > 0) {
-      if (!aligned16(p->bias_grad)) return EGM_ERR_ALIGNMENT;
-      int64_t blocks = cdiv(p->grad_len, 64);
-      if (blocks > 4096) blocks = 4096;
-      egm::launch_bias_grad_finish(dim3(uint32_t(blocks)), reinterpret_cast<hipStream_t>(stream), nullptr, 0,
-                                   p->grad_len, static_cast<float*>(p->bias_grad));
-      return hipGetLastError() == hipSuccess ? EGM_OK : EGM_ERR_HIP;
-    }
-    return EGM_OK;
-  }
-  if (D == nullptr) return EGM_ERR_INVALID_VALUE;
-  if (p->k > 0 && (A == nullptr || B == nullptr)) return EGM_ERR_INVALID_VALUE;
-  if ((A && !aligned16(A)) || (B && !aligned16(B)) || !aligned16(D) || (aux && !aligned16(aux)) ||
-      (p->workspace_bytes > 0 && !aligned16(workspace)))
-    return EGM_ERR_ALIGNMENT;
-  if (std::getenv("EGM_FAIL_INJECT") != nullptr && std::strcmp(std::getenv("EGM_FAIL_INJECT"), "launch") == 0)
-    return EGM_ERR_HIP;  // host-forced launch-error path, for tests of the error handling
-  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
-  const egm_status_t tuned = tune_if_pending(p, A, B, D, aux, workspace, s);
-  if (tuned != EGM_OK) return tuned;
-  const hipError_t err = launch_plan(p, p->config, A, B, D, aux, workspace, s);
-  return err == hipSuccess ? EGM_OK : EGM_ERR_HIP;
+  return execute_impl(ref.get(), A, B, D, aux, workspace, workspace_bytes, stream, false);
+}
+
+egm_status_t egm_execute_no_alloc(egm_plan_t plan, const void* A, const void* B, void* D, void* aux,
+                                  void* stream) {
+  const std::shared_ptr<egm_plan_s> ref = lookup(plan);
+  if (ref == nullptr) return EGM_ERR_INVALID_PLAN;
+  return execute_impl(ref.get(), A, B, D, aux, nullptr, 0, stream, true);
 }
 
 egm_status_t egm_execute_strided(egm_plan_t plan, int64_t batch, const void* A, int64_t stride_a, const void* B,
@@ -579,6 +636,9 @@ const char* egm_status_string(egm_status_t s) {
     case EGM_ERR_HIP: return "EGM_ERR_HIP: HIP runtime error at launch";
     case EGM_ERR_NO_MEMORY: return "EGM_ERR_NO_MEMORY: host allocation failed";
     case EGM_ERR_WORKSPACE: return "EGM_ERR_WORKSPACE: workspace missing or too small";
+    case EGM_ERR_SCRATCH_LIMIT:
+      return "EGM_ERR_SCRATCH_LIMIT: the plan needs more workspace than the static scratch of "
+             "egm_execute_no_alloc holds (EGM_NO_ALLOC_SCRATCH_BYTES)";
   }
   return "EGM: unknown status";
 }

@@ -73,8 +73,13 @@ typedef EGM_ENUM(egm_status_t) {
   EGM_ERR_INVALID_PLAN = 6,  /* NULL, freed or foreign plan handle */
   EGM_ERR_HIP = 7,           /* the HIP runtime reported an error at launch */
   EGM_ERR_NO_MEMORY = 8,     /* host allocation of the plan failed */
-  EGM_ERR_WORKSPACE = 9      /* workspace missing or smaller than egm_plan_workspace_bytes */
+  EGM_ERR_WORKSPACE = 9,     /* workspace missing or smaller than egm_plan_workspace_bytes */
+  EGM_ERR_SCRATCH_LIMIT = 10 /* egm_execute_no_alloc: the plan needs more workspace than
+                                EGM_NO_ALLOC_SCRATCH_BYTES */
 } egm_status_t;
+
+/* Bytes of the static scratch behind egm_execute_no_alloc (per GPU). */
+#define EGM_NO_ALLOC_SCRATCH_BYTES (32u << 20)
 
 typedef EGM_ENUM(egm_dtype_t) {
   EGM_F16 = 0,  /* IEEE binary16 */
@@ -251,6 +256,29 @@ egm_status_t egm_plan_fp8(egm_plan_t* out, int64_t m, int64_t n, int64_t k, egm_
  */
 egm_status_t egm_execute(egm_plan_t plan, const void* A, const void* B, void* D, void* aux,
                          void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * egm_execute_no_alloc - egm_execute for callers that cannot allocate device
+ * memory (code under HIP graph capture, tight serving loops, harnesses that
+ * forbid hipMalloc): the same launches, with the workspace taken from a
+ * static scratch array of EGM_NO_ALLOC_SCRATCH_BYTES that the library holds
+ * on each GPU it runs on (from the first call on that GPU until the process
+ * ends).  It calls no hipMalloc / hipFree and no allocating routine.
+ *   A, B, D, aux, stream  as egm_execute; the stream must belong to the
+ *         calling thread's current device, whose scratch is used.
+ * Errors: as egm_execute, and EGM_ERR_SCRATCH_LIMIT when the plan's
+ * egm_plan_workspace_bytes exceeds EGM_NO_ALLOC_SCRATCH_BYTES (nothing is
+ * enqueued); EGM_ERR_NOT_SUPPORTED while an autotune is pending (tuning
+ * creates events; run one egm_execute first, or plan without autotune);
+ * EGM_ERR_INVALID_VALUE if the stream is on another device.
+ * Every call on a GPU shares that GPU's scratch, which keeps whatever the last
+ * call left there (the kernels write every scratch byte they later read, so
+ * nothing needs clearing): calls whose executions overlap in time on one GPU
+ * (different streams, or threads) race on it and must be ordered by the
+ * caller.  A plan with no workspace (a fused forward plan) touches no scratch.
+ */
+egm_status_t egm_execute_no_alloc(egm_plan_t plan, const void* A, const void* B, void* D, void* aux,
+                                  void* stream);
 
 /*
  * egm_execute_strided - launch amortisation: the plan on `batch` independent

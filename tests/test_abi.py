@@ -24,7 +24,7 @@ def declared_functions():
 
 def test_every_declared_symbol_is_exported():
     names = declared_functions()
-    assert len(names) == 13
+    assert len(names) == 14
     assert sorted(egm.EXPORTS) == names
     lib = ctypes.CDLL(egm.LIB_PATH)
     for name in names:
@@ -33,7 +33,7 @@ def test_every_declared_symbol_is_exported():
 
 def test_abi_version_and_status_strings():
     assert egm.egm_abi_version() == 7
-    for s in range(10):
+    for s in range(11):
         assert egm.status_string(s).startswith("EGM_")
     assert "unknown" in egm.status_string(12345)
 
@@ -142,7 +142,7 @@ def test_out_of_range_enum_values_are_rejected():
         assert plan_status(dtype=dt) == egm.EGM_ERR_DTYPE
     for ep in (8, -7, 1 << 30):
         assert plan_status(epilog=ep) == egm.EGM_ERR_INVALID_VALUE
-    for st in (10, -1, (1 << 31) - 1):
+    for st in (11, -1, (1 << 31) - 1):
         assert "unknown" in egm.status_string(st)
 
 
@@ -436,3 +436,29 @@ def test_b_transposed_option():
                              raw_status=True)
     assert st == egm.EGM_OK
     egm.egm_free(h)
+
+
+def test_execute_no_alloc_validation_before_any_hip_call():
+    """The no-allocation entry point checks its arguments on the host first:
+    handles, masks, pointers, the static scratch's size and a pending autotune
+    (no GPU: none of these cases reaches a HIP call)."""
+    assert egm.egm_execute_no_alloc(0, FAKE, FAKE, FAKE, raw_status=True) == egm.EGM_ERR_INVALID_PLAN
+    h = egm.egm_plan(4096, 8192, 64, F16, E["BIAS"], FAKE, ROW, fused=0)  # 64 MiB product
+    try:
+        assert egm.egm_plan_workspace_bytes(h) > egm.EGM_NO_ALLOC_SCRATCH_BYTES
+        assert egm.egm_execute_no_alloc(h, FAKE, FAKE, FAKE, raw_status=True) == egm.EGM_ERR_SCRATCH_LIMIT
+    finally:
+        egm.egm_free(h)
+    h = egm.egm_plan(256, 256, 64, F16, E["BIAS"], FAKE, ROW, fused=0, autotune=1)
+    try:
+        assert egm.egm_execute_no_alloc(h, FAKE, FAKE, FAKE, raw_status=True) == egm.EGM_ERR_NOT_SUPPORTED
+    finally:
+        egm.egm_free(h)
+    h = egm.egm_plan(256, 256, 64, F16, E["RELU_AUX_BIAS"], FAKE, ROW)
+    try:
+        assert egm.egm_execute_no_alloc(h, FAKE, FAKE, FAKE, 0, raw_status=True) == egm.EGM_ERR_INVALID_VALUE
+        assert egm.egm_execute_no_alloc(h, FAKE, FAKE, FAKE + 8, FAKE, raw_status=True) == egm.EGM_ERR_ALIGNMENT
+        assert egm.egm_execute_no_alloc(h, FAKE, FAKE, 0, FAKE, raw_status=True) == egm.EGM_ERR_INVALID_VALUE
+    finally:
+        egm.egm_free(h)
+    assert egm.egm_execute_no_alloc(h, FAKE, FAKE, FAKE, FAKE, raw_status=True) == egm.EGM_ERR_INVALID_PLAN
