@@ -62,15 +62,19 @@ bool grid_fits(int64_t m, int64_t n, int c) {
   return tiles * 64 * kConfigs[c].wm * kConfigs[c].wn <= int64_t(0xffffffff);
 }
 
+// Configs built for the operand type: 16x16 MFMA blocks exist for 16-bit
+// operands only.
+bool config_built(int c, bool fp8) { return !fp8 || kConfigs[c].mi == 32; }
+
 // Per-shape choice: among the configs whose grid fits, the one with the
 // smallest estimated time, counting whole waves of tiles over the 256 CUs,
-// scaled by the config's relative efficiency.  Ties go to the larger tile
-// (lower id).  -1 when no config fits.
-int choose_config(int64_t m, int64_t n, int64_t k) {
+// scaled by the config's relative efficiency.  Ties go to the lower id.  -1
+// when no config fits.
+int choose_config(int64_t m, int64_t n, int64_t k, bool fp8) {
   int best = -1;
   double best_t = 0;
   for (int c = 0; c < kNumConfigs; ++c) {
-    if (!grid_fits(m, n, c)) continue;
+    if (!grid_fits(m, n, c) || !config_built(c, fp8)) continue;
     const int64_t tiles = cdiv(m, kConfigs[c].bm) * cdiv(n, kConfigs[c].bn);
     const int64_t waves = cdiv(tiles, kNumCUs);
     const double t = double(waves) * kConfigs[c].bm * kConfigs[c].bn * double(k > 0 ? k : 1) / kConfigs[c].rel_eff;
@@ -185,7 +189,7 @@ void describe(const egm_plan_s* p, char* buf, size_t len) {
            p->dtype == EGM_F16 ? "fp16" : "bf16",
            epilog_name(p->epilog), p->bias_layout == EGM_BIAS_ROW ? "row(m,1)" : p->bias_layout == EGM_BIAS_COL ? "col(1,n)" : "none",
            p->fused ? "fused" : "unfused(gemm+epilogue)", c.bm, c.bn, p->f8 != 0 ? 2 * c.bk : c.bk, c.wm, c.wn,
-           p->f8 != 0 ? "32x32x64" : "32x32x16", c.stages, effective_group_m(p, p->config),
+           p->f8 != 0 ? "32x32x64" : c.mi == 16 ? "16x16x32" : "32x32x16", c.stages, effective_group_m(p, p->config),
            (long long)(cdiv(p->m, c.bm) * cdiv(p->n, c.bn)), p->workspace_bytes,
            p->autotune_pending ? " autotune=pending" : "");
 }
@@ -286,7 +290,7 @@ hipError_t autotune(egm_plan_s* p, const void* A, const void* B, void* D, void* 
   float best = -1.0f;
   int best_cfg = p->config;
   for (int c = 0; c < kNumConfigs && err == hipSuccess; ++c) {
-    if (!grid_fits(p->m, p->n, c)) continue;
+    if (!grid_fits(p->m, p->n, c) || !config_built(c, p->f8 != 0)) continue;
     err = launch_plan(p, c, A, B, D, aux, ws, s);
     if (err != hipSuccess) break;
     err = hipEventRecord(e0, s);
@@ -407,10 +411,12 @@ egm_status_t plan_impl(egm_plan_t* out, int64_t m, int64_t n, int64_t k, egm_dty
   p->scale_b = scale_b;
   p->b_transposed = b_transposed;
   p->fused = fused;
-  p->config = force >= 0 ? force : choose_config(m, n, k);
-  // the launch must fit one grid dimension (autotuning tries only the
-  // configs that fit, and the per-shape choice always fits)
-  if (p->config < 0 || !grid_fits(m, n, p->config)) return EGM_ERR_NOT_SUPPORTED;
+  p->config = force >= 0 ? force : choose_config(m, n, k, f8 != 0);
+  // the launch must fit one grid dimension and the config exist for the
+  // operand type (autotuning tries only such configs, and the per-shape
+  // choice always is one)
+  if (p->config < 0 || !grid_fits(m, n, p->config) || !config_built(p->config, f8 != 0))
+    return EGM_ERR_NOT_SUPPORTED;
   p->group_m = group_m;
   p->autotune_pending = tune;
   // workspace: the two-kernel path's product P, then (DRELU_BGRAD) the fp32
@@ -420,7 +426,7 @@ egm_status_t plan_impl(egm_plan_t* out, int64_t m, int64_t n, int64_t k, egm_dty
   p->grad_len = epilog == EGM_EPILOG_DRELU_BGRAD ? (layout == EGM_BIAS_COL ? n : m) : 0;
   int64_t max_chunks = 0;
   for (int c = 0; c < kNumConfigs; ++c) {
-    if ((tune && grid_fits(m, n, c)) || c == p->config) {
+    if ((tune && grid_fits(m, n, c) && config_built(c, f8 != 0)) || c == p->config) {
       const int64_t ch = grad_chunks(p, c);
       if (ch > max_chunks) max_chunks = ch;
     }
@@ -619,8 +625,9 @@ egm_status_t egm_config_describe(int32_t config, char* buf, size_t len) {
   if (config < 0 || config >= kNumConfigs) return EGM_ERR_INVALID_VALUE;
   if (buf == nullptr || len == 0) return EGM_ERR_INVALID_VALUE;
   const ConfigInfo& c = kConfigs[config];
-  snprintf(buf, len, "tile=%dx%d kslab=%d waves=%dx%d wave_tile=%dx%d mfma=32x32x16 lds_ring=%d lds_bytes=%d", c.bm,
-           c.bn, c.bk, c.wm, c.wn, c.bm / c.wm, c.bn / c.wn, c.stages, c.stages * (c.bm + c.bn) * c.bk * 2);
+  snprintf(buf, len, "tile=%dx%d kslab=%d waves=%dx%d wave_tile=%dx%d mfma=%s lds_ring=%d lds_bytes=%d%s", c.bm,
+           c.bn, c.bk, c.wm, c.wn, c.bm / c.wm, c.bn / c.wn, c.mi == 16 ? "16x16x32" : "32x32x16", c.stages,
+           c.stages * (c.bm + c.bn) * c.bk * 2, c.mi == 16 ? " operands=16-bit" : "");
   return EGM_OK;
 }
 

@@ -131,6 +131,21 @@ __device__ __forceinline__ f32x16 mfma32(u32x4 a, u32x4 b, f32x16 c) {
   }
 }
 
+// MFMA 16x16x32, fp32 accumulate: a and b hold 8 consecutive k-values of the
+// row (column) l % 16, k-values 8 (l / 16) .. +7; lane l receives rows
+// 4 (l / 16) .. +3 of column l % 16.  Same k per register position in both
+// operands is all the sum needs.
+template <int DT>
+__device__ __forceinline__ f32x4 mfma16(u32x4 a, u32x4 b, f32x4 c) {
+  if constexpr (DT == DT_F16) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, a),
+                                                  __builtin_bit_cast(f16x8, b), c, 0, 0, 0);
+  } else {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a),
+                                                   __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
+  }
+}
+
 // fp8 operands: v_mfma_f32_32x32x64_f8f6f4, 64 k-values per instruction.
 // Each operand is 32 bytes per lane: lane l holds row (column) l % 32 and the
 // k-values 32 (l / 32) .. +31 in byte order (checked on the GPU with an

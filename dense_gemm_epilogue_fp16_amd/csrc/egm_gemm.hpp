@@ -63,15 +63,17 @@ struct GemmArgs {
   int32_t group_m;
 };
 
-template <int BM_, int BN_, int STAGES_ = 4, int WM_ = 2, int WN_ = 2, int BK_ = 32, int ES_ = 2>
+template <int BM_, int BN_, int STAGES_ = 4, int WM_ = 2, int WN_ = 2, int BK_ = 32, int ES_ = 2, int MI_ = 32>
 struct TileCfg {
   static constexpr int BM = BM_, BN = BN_, BK = BK_, STAGES = STAGES_;
   static constexpr int ES = ES_;                      // operand element bytes: 2 (fp16/bf16) or 1 (fp8)
+  static constexpr int MI = MI_;                      // MFMA block: 32 (32x32x16) or 16 (16x16x32, 16-bit only)
   static constexpr int WM = WM_, WN = WN_;            // WM x WN waves
   static constexpr int NW = WM * WN, NT = 64 * NW;
   static constexpr int WTM = BM / WM, WTN = BN / WN;  // wave sub-tile
-  static constexpr int FM = WTM / 32, FN = WTN / 32;  // 32x32 blocks per wave
-  static constexpr int KI = ES == 2 ? 16 : 64;        // k per MFMA instruction
+  static constexpr int FM = WTM / 32, FN = WTN / 32;  // 32x32 blocks per wave (the epilogue's layout)
+  static constexpr int FM16 = WTM / 16, FN16 = WTN / 16;  // 16x16 blocks per wave (MI == 16)
+  static constexpr int KI = ES == 2 ? (MI == 32 ? 16 : 32) : 64;  // k per MFMA instruction
   static constexpr int NS = BK / KI;                  // k-slices per slab
   static constexpr int CE = 16 / ES;                  // elements per 16-byte chunk
   static constexpr int A_ROW = BK * ES;               // bytes per A row in LDS
@@ -102,6 +104,16 @@ struct TileCfg {
   static_assert(BM <= NT && BN <= NT, "one thread per tile row / column for the gradient sums");
   static_assert(STAGES >= 2, "the ring needs a buffer being filled besides the one being read");
   static_assert(LDS_BYTES + 1024 <= 160 * 1024, "LDS ring exceeds 160 KiB");
+  static_assert(MI == 32 || (MI == 16 && ES == 2), "16x16 MFMA blocks are built for 16-bit operands");
+  // Ring buffer s of A and of B.  32x32 blocks: A and B of a slab side by side
+  // (buffer s at s * STAGE_BYTES).  16x16 blocks: all A buffers, then all B
+  // buffers, so that a buffer's distance from buffer 0 of its operand stays
+  // below the 16-bit offset field of an LDS read (at most 3 x 32 KiB) and the
+  // fragment addresses need one register each, whatever the buffer.
+  static constexpr uint32_t a_buf(int s) { return MI == 16 ? (uint32_t)(s * A_BYTES) : (uint32_t)(s * STAGE_BYTES); }
+  static constexpr uint32_t b_buf(int s) {
+    return MI == 16 ? (uint32_t)(STAGES * A_BYTES + s * B_BYTES) : (uint32_t)(s * STAGE_BYTES + A_BYTES);
+  }
 };
 
 // A: the 16-byte chunks of an A row are XOR-ed with row bits, so that the
@@ -117,15 +129,28 @@ __device__ __forceinline__ uint32_t a_swz(uint32_t row) {
   else return (row >> 1) & 7u;
 }
 
-// B, 16-bit: chunk index bits 2..3 are XOR-ed with k mod 4, so the four
-// k-rows a transposing read touches at once land on different 64-byte bank
-// groups.  fp8: one 8-bit transposing read takes a 16-byte chunk pair from 8
-// consecutive k-rows per half-wave; the pair index is XOR-ed with the k-row's
-// position among the rows that share a 256-byte bank window, so the 8 pairs
-// cover all 64 banks (rows of 256, 128 or 64 bytes).
-template <int B_CHUNKS, int ES = 2>
+// B, 16-bit, 32x32 blocks: chunk index bits 2..3 are XOR-ed with k mod 4, so
+// the four k-rows a transposing read touches at once land on different 64-byte
+// bank groups.  16-bit, 16x16 blocks: a transposing read takes 32 bytes (one
+// block's 16 columns) from each of 8 k-rows per half-wave, k-rows q and q + 8
+// (q = 0..3 within a 16-lane group); bits 1..3 of the chunk index are XOR-ed
+// with 8 distinct even values, so the 8 pieces cover all 64 banks: k-row bits
+// 0..1 and 3 where a k-row spans the 256-byte bank window (rows of 256 or 512
+// bytes), bits 1 and 3 where two rows share it (rows of 128 bytes; row parity
+// already picks the window half).  fp8: one 8-bit transposing read takes a
+// 16-byte chunk pair from 8 consecutive k-rows per half-wave; the pair index
+// is XOR-ed with the k-row's position among the rows that share a 256-byte
+// bank window, so the 8 pairs cover all 64 banks (rows of 256, 128 or 64
+// bytes).  Both 16-bit forms leave k-row bit 2 out, so a block's second
+// transposing read (4 k-rows further) keeps the first one's swizzle.
+template <int B_CHUNKS, int ES = 2, int MI = 32>
 __device__ __forceinline__ uint32_t b_swz(uint32_t krow) {
-  if constexpr (ES == 2) {
+  if constexpr (ES == 2 && MI == 16) {
+    if constexpr (B_CHUNKS >= 16)
+      return ((krow & 3u) << 2) | (((krow >> 3) & 1u) << 1);
+    else
+      return ((((krow >> 1) & 1u) << 2) | (((krow >> 3) & 1u) << 1)) & (B_CHUNKS - 1);
+  } else if constexpr (ES == 2) {
     return ((krow & 3u) << 2) & (B_CHUNKS - 1);
   } else {
     constexpr uint32_t RPW = B_CHUNKS >= 16 ? 1 : 16 / B_CHUNKS;  // k-rows per 256-byte window
@@ -287,11 +312,12 @@ __device__ __forceinline__ float block_column_sum(float (&v)[16], int lane) {
 }
 
 // ---------------------------------------------------------------------------
-// Epilogue on the fp32 accumulators of one wave, then the store.
-// lane holds D[m0 + wm0 + 32i + lr][n0 + wn0 + 32j + 8g + 4lh + e] = acc[i][j][4g + e]
+// Epilogue on the fp32 accumulators of one wave, then the store.  The
+// accumulators come one 32-row block-row at a time from block_row(i, row):
+// lane holds D[m0 + wm0 + 32i + lr][n0 + wn0 + 32j + 8g + 4lh + e] = row[j][4g + e]
 // ---------------------------------------------------------------------------
-template <int DT, int EPI, int WM, int WN, bool SCALED, int FM, int FN>
-__device__ __forceinline__ void epilogue_store(const GemmArgs& p, f32x16 (&acc)[FM][FN], int m0, int n0, int wm0,
+template <int DT, int EPI, int WM, int WN, bool SCALED, int FM, int FN, class BlockRow>
+__device__ __forceinline__ void epilogue_store(const GemmArgs& p, BlockRow&& block_row, int m0, int n0, int wm0,
                                                int wn0, int lane, uint8_t* stage,
                                                const uint8_t* bias_lds, float* red, float scale) {
   const int M = p.M, N = p.N;
@@ -379,6 +405,8 @@ __device__ __forceinline__ void epilogue_store(const GemmArgs& p, f32x16 (&acc)[
 #pragma unroll
   for (int i = 0; i < FM; ++i) {
     const uint32_t lrow = wm0 + 32 * i + lr;  // row within the tile
+    f32x16 acc_row[FN];
+    block_row(i, acc_row);
     float brow = 0.0f;
     if constexpr (epi_adds_bias(EPI)) {
       if (p.bias_layout == BIAS_ROW) {
@@ -404,7 +432,7 @@ __device__ __forceinline__ void epilogue_store(const GemmArgs& p, f32x16 (&acc)[
         float z[4];
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-          z[e] = acc[i][j][4 * g + e];
+          z[e] = acc_row[j][4 * g + e];
           if constexpr (SCALED) z[e] *= scale;  // fp8: the two per-tensor scales, before the bias
           if constexpr (epi_adds_bias(EPI)) z[e] += brow + bcol[j][g][e];
           if constexpr (epi_reads_mask(EPI)) z[e] = ((keep[i][j] >> (8 * g + 4 * lh + e)) & 1u) ? z[e] : 0.0f;
@@ -607,7 +635,7 @@ __global__ void __launch_bounds__(C::NT, 1) gemm_epilogue_kernel(GemmArgs p) {
       b_off[u] = (row * (uint32_t)K + lc * C::CE) * C::ES;
     } else {
       const uint32_t krow = q * C::B_ROWS_PER_DMA + lane / C::B_CHUNKS;
-      const uint32_t lc = (lane % C::B_CHUNKS) ^ b_swz<C::B_CHUNKS, C::ES>(krow);
+      const uint32_t lc = (lane % C::B_CHUNKS) ^ b_swz<C::B_CHUNKS, C::ES, C::MI>(krow);
       b_k8[u] = 0;
       b_off[u] = (n0 + (int)lc * C::CE < N) ? (krow * (uint32_t)N + lc * C::CE) * C::ES : OOB_OFFSET;
     }
@@ -643,13 +671,23 @@ __global__ void __launch_bounds__(C::NT, 1) gemm_epilogue_kernel(GemmArgs p) {
   };
   // Load q (0 .. PW-1) of this wave for a slab into ring buffer `stage`: the
   // first A_PW are A loads, the rest B loads.
+  // LDS base of the copies.  With one wave per SIMD (4 waves) the compiler
+  // would otherwise hoist every copy's LDS address (one per copy and ring
+  // buffer) out of the main loop into registers of their own, and spill
+  // them; an opaque base keeps each address a couple of scalar additions at
+  // its copy.
+  auto copy_base = [&]() {
+    uint32_t b = smem_lds;
+    if constexpr (C::NW == 4) asm volatile("" : "+s"(b));
+    return b;
+  };
   auto issue_one = [&](const SlabSrd& r, int stage, int q) {
-    const uint32_t sa = smem_lds + (uint32_t)(stage * C::STAGE_BYTES);
     if (q < C::A_PW) {
-      dma16(r.a, sa + (wave * C::A_PW + q) * 1024u, r.kbase + a_k8[q] < (uint32_t)K ? a_off[q] : OOB_OFFSET);
+      dma16(r.a, copy_base() + C::a_buf(stage) + (wave * C::A_PW + q) * 1024u,
+            r.kbase + a_k8[q] < (uint32_t)K ? a_off[q] : OOB_OFFSET);
     } else {
       const int u = q - C::A_PW;
-      dma16(r.b, sa + C::A_BYTES + (wave * C::B_PW + u) * 1024u,
+      dma16(r.b, copy_base() + C::b_buf(stage) + (wave * C::B_PW + u) * 1024u,
             !BT || r.kbase + b_k8[u] < (uint32_t)K ? b_off[u] : OOB_OFFSET);
     }
   };
@@ -716,6 +754,42 @@ __global__ void __launch_bounds__(C::NT, 1) gemm_epilogue_kernel(GemmArgs p) {
       bt_off[ks][h] = C::A_BYTES + (uint32_t)(wn0 + lr) * C::A_ROW + ((chunk ^ a_swz<C::A_CHUNKS>(lr)) << 4);
     }
 
+  // 16x16 blocks (MI == 16), LDS offsets into buffer 0 of the operand;
+  // another ring buffer, block or k-slice adds a constant that fits the LDS
+  // read's 16-bit offset field.  A fragment of block i, k-slice ks (32 k-values): row
+  // wm0 + 16i + l%16, k-values 32ks + 8(l/16) .. +7, i.e. logical chunk
+  // 4ks + l/16 (a_swz depends on row bits 1..3 only, i.e. on l%16).  B
+  // fragment of block j: within 16-lane group g = l/16 lane r = l%16 addresses
+  // k-row 8g + 4t + r/4 (t = 0, 1: the two transposing reads) and the 4
+  // columns wn0 + 16j + 4(r%4); the reads give lane l the k-values 8(l/16) ..
+  // +7 of column wn0 + 16j + l%16, the operand layout of the 16x16x32 MFMA.
+  // Transposed B: block j is tile row wn0 + 16j + l%16, read like A.
+  constexpr bool M16 = C::MI == 16;
+  const int lr16 = lane & 15;
+  uint32_t a16_off[M16 ? C::NS : 1], bt16_off[M16 ? C::NS : 1], b16_off[M16 ? C::FN16 : 1];
+  if constexpr (M16) {
+    static_assert(BT || C::B_CHUNKS >= 8, "the 16x16 B swizzle covers rows of 128 bytes or more");
+    // the largest constant a read adds: last ring buffer, k-slice and block
+    static_assert((C::STAGES - 1) * C::A_BYTES + (C::FM16 - 1) * 16 * C::A_ROW + 16 * C::A_ROW < 65536 &&
+                      (C::STAGES - 1) * C::B_BYTES +
+                              (BT ? (C::FN16 - 1) * 16 * C::A_ROW : (32 * (C::NS - 1) + 4) * C::B_ROW) <
+                          65536,
+                  "a ring buffer's displacement must fit the LDS read offset");
+#pragma unroll
+    for (int ks = 0; ks < C::NS; ++ks) {
+      const uint32_t chunk = ((4u * ks + (uint32_t)g16) ^ a_swz<C::A_CHUNKS>((uint32_t)lr16)) << 4;
+      a16_off[ks] = C::a_buf(0) + (uint32_t)(wm0 + lr16) * C::A_ROW + chunk;
+      bt16_off[ks] = C::b_buf(0) + (uint32_t)(wn0 + lr16) * C::A_ROW + chunk;
+    }
+#pragma unroll
+    for (int j = 0; j < C::FN16; ++j) {
+      const uint32_t krow = 8 * g16 + (r16 >> 2);
+      const uint32_t col = wn0 + 16 * j + 4 * (r16 & 3);
+      b16_off[j] = C::b_buf(0) + krow * C::B_ROW + (((col >> 3) ^ b_swz<C::B_CHUNKS, C::ES, C::MI>(krow)) << 4) +
+                   (col & 4) * 2;
+    }
+  }
+
   // Per-buffer copies of the 16-bit fragment offsets, kept in registers: a
   // ring buffer lies STAGE_BYTES (64 KiB for the 256x256 tile) above the
   // previous one, beyond the 16-bit offset of an LDS read, so without them
@@ -723,14 +797,14 @@ __global__ void __launch_bounds__(C::NT, 1) gemm_epilogue_kernel(GemmArgs p) {
   // main loop runs whole turns of the ring, so the buffer index is a
   // compile-time constant.  (fp8 tiles keep the per-slab additions: there the
   // extra registers measured slower.)
-  constexpr int S16 = C::ES == 2 ? C::STAGES : 1;
+  constexpr int S16 = C::ES == 2 && !M16 ? C::STAGES : 1;
   auto in_buffer = [](uint32_t off, int s) {
     uint32_t v = off + (uint32_t)(s * C::STAGE_BYTES);
     if (s > 0) asm volatile("" : "+v"(v));  // a register of its own, not re-derived in the loop
     return v;
   };
   uint32_t a_fo[S16][C::NS], b_fo[S16][2][C::FN], bt_fo[S16][C::NS];
-  if constexpr (C::ES == 2) {
+  if constexpr (C::ES == 2 && !M16) {
 #pragma unroll
     for (int s = 0; s < C::STAGES; ++s) {
 #pragma unroll
@@ -748,13 +822,21 @@ __global__ void __launch_bounds__(C::NT, 1) gemm_epilogue_kernel(GemmArgs p) {
     }
   }
 
-  f32x16 acc[C::FM][C::FN];
+  f32x16 acc[M16 ? 1 : C::FM][M16 ? 1 : C::FN];
 #pragma unroll
-  for (int i = 0; i < C::FM; ++i)
+  for (int i = 0; i < (M16 ? 1 : C::FM); ++i)
 #pragma unroll
-    for (int j = 0; j < C::FN; ++j)
+    for (int j = 0; j < (M16 ? 1 : C::FN); ++j)
 #pragma unroll
       for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.0f;
+  // 16x16 blocks: the main loop's accumulators (lane l: row 16i + l%16 of the
+  // wave tile, columns 16j + 4(l/16) .. +3), moved into acc's 32x32 layout
+  // after the loop
+  f32x4 acc16[M16 ? C::FM16 : 1][M16 ? C::FN16 : 1];
+#pragma unroll
+  for (int i = 0; i < (M16 ? C::FM16 : 1); ++i)
+#pragma unroll
+    for (int j = 0; j < (M16 ? C::FN16 : 1); ++j) acc16[i][j] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
 
   // Two fragment sets (k-slice being computed / k-slice being read).
   // 16-bit: A fragment i is one 16-byte read; B fragment j is two transposing
@@ -763,32 +845,49 @@ __global__ void __launch_bounds__(C::NT, 1) gemm_epilogue_kernel(GemmArgs p) {
   // the lane's 32).  A k-slice is read as NRD "pieces", in the order of first
   // use by the MFMAs (i outer, j inner): A0, then B0 .. B(FN-1), then A1 ..
   // A(FM-1).
-  constexpr int NMF = C::FM * C::FN;  // MFMAs per k-slice
+  // (16x16 blocks: the same with FM16 x FN16 blocks of 16-byte A reads and
+  // pairs of transposing B reads.)
+  constexpr int FMB = M16 ? C::FM16 : C::FM, FNB = M16 ? C::FN16 : C::FN;  // fragments per k-slice
+  constexpr int NMF = FMB * FNB;  // MFMAs per k-slice
   constexpr int RA = C::ES == 2 ? 1 : 2;                   // reads per A fragment
   constexpr int RB = BT ? RA : (C::ES == 2 ? 2 : 4);        // reads per B fragment
-  constexpr int NRD = RA * C::FM + RB * C::FN;              // LDS read instructions per k-slice
-  u32x4 fa[2][C::FM][RA];
-  u32x2 fb[2][C::FN][BT ? 1 : RB];
-  u32x4 fbt[2][C::FN][RA];  // transposed B: A-like 16-byte pieces
+  constexpr int NRD = RA * FMB + RB * FNB;                  // LDS read instructions per k-slice
+  u32x4 fa[2][FMB][RA];
+  u32x2 fb[2][FNB][BT ? 1 : RB];
+  u32x4 fbt[2][FNB][RA];  // transposed B: A-like 16-byte pieces
   auto read_piece = [&](int set, int stage, int ks, int piece) {
-    const uint8_t* const st = smem + stage * C::STAGE_BYTES;
-    if (piece < RA || piece >= RA + RB * C::FN) {
-      const int t = piece < RA ? piece : piece - RB * C::FN;
-      const int i = t / RA, h = t % RA;
-      if constexpr (C::ES == 2)
-        fa[set][i][0] = *(const u32x4*)(smem + a_fo[stage][ks] + i * 32 * C::A_ROW);
-      else
-        fa[set][i][h] = *(const u32x4*)(st + a8_off[ks][h] + i * 32 * C::A_ROW);
+    if constexpr (M16) {
+      if (piece < 1 || piece >= 1 + RB * FNB) {
+        const int i = piece < 1 ? 0 : piece - RB * FNB;
+        fa[set][i][0] = *(const u32x4*)(smem + a16_off[ks] + (C::a_buf(stage) - C::a_buf(0)) + i * 16 * C::A_ROW);
+      } else {
+        const int j = (piece - 1) / RB, t = (piece - 1) % RB;
+        constexpr uint32_t kB0 = C::b_buf(0);
+        if constexpr (BT)
+          fbt[set][j][0] = *(const u32x4*)(smem + bt16_off[ks] + (C::b_buf(stage) - kB0) + j * 16 * C::A_ROW);
+        else
+          fb[set][j][t] = lds_read_tr<DT>(smem + b16_off[j] + (C::b_buf(stage) - kB0) + (32 * ks + 4 * t) * C::B_ROW);
+      }
     } else {
-      const int j = (piece - RA) / RB, t = (piece - RA) % RB;
-      if constexpr (BT && C::ES == 2)
-        fbt[set][j][t] = *(const u32x4*)(smem + bt_fo[stage][ks] + j * 32 * C::A_ROW);
-      else if constexpr (BT)
-        fbt[set][j][t] = *(const u32x4*)(st + bt_off[ks][t] + j * 32 * C::A_ROW);
-      else if constexpr (C::ES == 2)
-        fb[set][j][t] = lds_read_tr<DT>(smem + b_fo[stage][t][j] + ks * 16 * C::B_ROW);
-      else
-        fb[set][j][t] = lds_read_tr8(st + b8_off[j] + (ks * 64 + 8 * t) * C::B_ROW);
+      const uint8_t* const st = smem + stage * C::STAGE_BYTES;
+      if (piece < RA || piece >= RA + RB * C::FN) {
+        const int t = piece < RA ? piece : piece - RB * C::FN;
+        const int i = t / RA, h = t % RA;
+        if constexpr (C::ES == 2)
+          fa[set][i][0] = *(const u32x4*)(smem + a_fo[stage][ks] + i * 32 * C::A_ROW);
+        else
+          fa[set][i][h] = *(const u32x4*)(st + a8_off[ks][h] + i * 32 * C::A_ROW);
+      } else {
+        const int j = (piece - RA) / RB, t = (piece - RA) % RB;
+        if constexpr (BT && C::ES == 2)
+          fbt[set][j][t] = *(const u32x4*)(smem + bt_fo[stage][ks] + j * 32 * C::A_ROW);
+        else if constexpr (BT)
+          fbt[set][j][t] = *(const u32x4*)(st + bt_off[ks][t] + j * 32 * C::A_ROW);
+        else if constexpr (C::ES == 2)
+          fb[set][j][t] = lds_read_tr<DT>(smem + b_fo[stage][t][j] + ks * 16 * C::B_ROW);
+        else
+          fb[set][j][t] = lds_read_tr8(st + b8_off[j] + (ks * 64 + 8 * t) * C::B_ROW);
+      }
     }
   };
   auto read_slice = [&](int set, int stage, int ks) {
@@ -796,32 +895,45 @@ __global__ void __launch_bounds__(C::NT, 1) gemm_epilogue_kernel(GemmArgs p) {
     for (int q = 0; q < NRD; ++q) read_piece(set, stage, ks, q);
   };
   auto mfmas = [&](int set) {
+    if constexpr (M16) {
 #pragma unroll
-    for (int i = 0; i < C::FM; ++i)
+      for (int i = 0; i < C::FM16; ++i)
 #pragma unroll
-      for (int j = 0; j < C::FN; ++j) {
-        if constexpr (BT && C::ES == 2) {
-          acc[i][j] = mfma32<DT>(fbt[set][j][0], fa[set][i][0], acc[i][j]);
-        } else if constexpr (BT) {
-          constexpr int FA = (F8 - 1) & 1, FB = (F8 - 1) >> 1;
-          const u32x8 b8{fbt[set][j][0][0], fbt[set][j][0][1], fbt[set][j][0][2], fbt[set][j][0][3],
-                         fbt[set][j][1][0], fbt[set][j][1][1], fbt[set][j][1][2], fbt[set][j][1][3]};
-          const u32x8 a8{fa[set][i][0][0], fa[set][i][0][1], fa[set][i][0][2], fa[set][i][0][3],
-                         fa[set][i][1][0], fa[set][i][1][1], fa[set][i][1][2], fa[set][i][1][3]};
-          acc[i][j] = mfma32_f8<FB, FA>(b8, a8, acc[i][j]);
-        } else if constexpr (C::ES == 2) {
-          acc[i][j] = mfma32<DT>(u32x4{fb[set][j][0][0], fb[set][j][0][1], fb[set][j][1][0], fb[set][j][1][1]},
-                                 fa[set][i][0], acc[i][j]);
-        } else {
-          // B is the first operand (format FB), A the second (format FA)
-          constexpr int FA = (F8 - 1) & 1, FB = (F8 - 1) >> 1;
-          const u32x8 b8{fb[set][j][0][0], fb[set][j][0][1], fb[set][j][1][0], fb[set][j][1][1],
-                         fb[set][j][2][0], fb[set][j][2][1], fb[set][j][3][0], fb[set][j][3][1]};
-          const u32x8 a8{fa[set][i][0][0], fa[set][i][0][1], fa[set][i][0][2], fa[set][i][0][3],
-                         fa[set][i][RA - 1][0], fa[set][i][RA - 1][1], fa[set][i][RA - 1][2], fa[set][i][RA - 1][3]};
-          acc[i][j] = mfma32_f8<FB, FA>(b8, a8, acc[i][j]);
+        for (int j = 0; j < C::FN16; ++j) {
+          if constexpr (BT)
+            acc16[i][j] = mfma16<DT>(fbt[set][j][0], fa[set][i][0], acc16[i][j]);
+          else
+            acc16[i][j] = mfma16<DT>(u32x4{fb[set][j][0][0], fb[set][j][0][1], fb[set][j][1][0], fb[set][j][1][1]},
+                                     fa[set][i][0], acc16[i][j]);
         }
-      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < C::FM; ++i)
+#pragma unroll
+        for (int j = 0; j < C::FN; ++j) {
+          if constexpr (BT && C::ES == 2) {
+            acc[i][j] = mfma32<DT>(fbt[set][j][0], fa[set][i][0], acc[i][j]);
+          } else if constexpr (BT) {
+            constexpr int FA = (F8 - 1) & 1, FB = (F8 - 1) >> 1;
+            const u32x8 b8{fbt[set][j][0][0], fbt[set][j][0][1], fbt[set][j][0][2], fbt[set][j][0][3],
+                           fbt[set][j][1][0], fbt[set][j][1][1], fbt[set][j][1][2], fbt[set][j][1][3]};
+            const u32x8 a8{fa[set][i][0][0], fa[set][i][0][1], fa[set][i][0][2], fa[set][i][0][3],
+                           fa[set][i][1][0], fa[set][i][1][1], fa[set][i][1][2], fa[set][i][1][3]};
+            acc[i][j] = mfma32_f8<FB, FA>(b8, a8, acc[i][j]);
+          } else if constexpr (C::ES == 2) {
+            acc[i][j] = mfma32<DT>(u32x4{fb[set][j][0][0], fb[set][j][0][1], fb[set][j][1][0], fb[set][j][1][1]},
+                                   fa[set][i][0], acc[i][j]);
+          } else {
+            // B is the first operand (format FB), A the second (format FA)
+            constexpr int FA = (F8 - 1) & 1, FB = (F8 - 1) >> 1;
+            const u32x8 b8{fb[set][j][0][0], fb[set][j][0][1], fb[set][j][1][0], fb[set][j][1][1],
+                           fb[set][j][2][0], fb[set][j][2][1], fb[set][j][3][0], fb[set][j][3][1]};
+            const u32x8 a8{fa[set][i][0][0], fa[set][i][0][1], fa[set][i][0][2], fa[set][i][0][3],
+                           fa[set][i][RA - 1][0], fa[set][i][RA - 1][1], fa[set][i][RA - 1][2], fa[set][i][RA - 1][3]};
+            acc[i][j] = mfma32_f8<FB, FA>(b8, a8, acc[i][j]);
+          }
+        }
+    }
   };
   // Scheduling hint for one k-slice: alternate the MFMAs with the LDS reads
   // of the next k-slice, reads first, so neither the MFMA pipe nor the LDS
@@ -886,7 +998,7 @@ __global__ void __launch_bounds__(C::NT, 1) gemm_epilogue_kernel(GemmArgs p) {
         // (A uniform branch drops the per-lane k check of the A copies in
         // every slab below K.)
         if constexpr (C::ES == 2) {
-          const uint32_t sa = smem_lds + (uint32_t)(st * C::STAGE_BYTES);
+          const uint32_t sa = smem_lds + C::a_buf(st);
           if (r.full) {
 #pragma unroll
             for (int q = 0; q < C::A_PW; ++q) dma16(r.a, sa + (wave * C::A_PW + q) * 1024u, a_off[q]);
@@ -907,7 +1019,7 @@ __global__ void __launch_bounds__(C::NT, 1) gemm_epilogue_kernel(GemmArgs p) {
           interleave();
           __builtin_amdgcn_sched_barrier(0);
           if (r.full) {
-            const uint32_t sa = smem_lds + (uint32_t)(st * C::STAGE_BYTES);
+            const uint32_t sa = smem_lds + C::a_buf(st);
 #pragma unroll
             for (int q = 0; q < C::A_PW; ++q) dma16(r.a, sa + (wave * C::A_PW + q) * 1024u, a_off[q]);
 #pragma unroll
@@ -925,7 +1037,7 @@ __global__ void __launch_bounds__(C::NT, 1) gemm_epilogue_kernel(GemmArgs p) {
         // (64x64 tiles: in slabs below K the A copies skip their per-lane k
         // check; measured 4 % faster there, and no faster for 128x128)
         if (C::BM * C::BN <= 64 * 64 && r.full) {
-          const uint32_t sa = smem_lds + (uint32_t)(st * C::STAGE_BYTES);
+          const uint32_t sa = copy_base() + C::a_buf(st);
 #pragma unroll
           for (int q = 0; q < C::PW; ++q) {
             if (q < C::A_PW)
@@ -958,6 +1070,36 @@ __global__ void __launch_bounds__(C::NT, 1) gemm_epilogue_kernel(GemmArgs p) {
       if (kt + s < KT) slab(kt + s, s);
   }
 
+  // The epilogue takes the accumulators one 32-row block-row at a time, in
+  // the 32x32 layout.  16x16 blocks are moved into it there, so that only one
+  // block-row's converted values are live: region (I, J) of 32 x 32 holds
+  // blocks (2I + r, 2J + c).  For fixed c and register e, the value of block
+  // row r that lane (s, bit4 = h, bit5 = t) holds (row 16r + s, column
+  // 16c + 8t + 4h + e) belongs to lane (s, bit4 = r, bit5 = h), at register
+  // 4(2c + t) + e (row s + 16r, column 8(2c + t) + 4h + e): the three bits
+  // (register r, lane bit 4, lane bit 5) rotate, which is a swap of the
+  // register with lane bit 4 (v_permlane16_swap) followed by a swap with lane
+  // bit 5 (v_permlane32_swap).
+  auto block_row = [&](int I, f32x16 (&row)[C::FN]) {
+    if constexpr (M16) {
+#pragma unroll
+      for (int J = 0; J < C::FN; ++J)
+#pragma unroll
+        for (int c = 0; c < 2; ++c)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            float x = acc16[2 * I][2 * J + c][e], y = acc16[2 * I + 1][2 * J + c][e];
+            swap16(x, y);
+            swap32(x, y);
+            row[J][4 * (2 * c) + e] = x;
+            row[J][4 * (2 * c + 1) + e] = y;
+          }
+    } else {
+#pragma unroll
+      for (int J = 0; J < C::FN; ++J) row[J] = acc[I][J];
+    }
+  };
+
   // fp8: the product of the two per-tensor scales (uniform; NULL reads as 1),
   // loaded only now so that no register holds it through the main loop
   float scale = 1.0f;
@@ -970,8 +1112,9 @@ __global__ void __launch_bounds__(C::NT, 1) gemm_epilogue_kernel(GemmArgs p) {
   wait_vmcnt<0>();
   // the ring is free once every wave is past its last fragment read
   __syncthreads();
-  epilogue_store<DT, EPI, C::WM, C::WN, F8 != 0>(p, acc, m0, n0, wm0, wn0, lane, smem + wave * C::EPI_STAGE,
-                                                 bias_lds, (float*)(smem + C::RED_OFF), scale);
+  epilogue_store<DT, EPI, C::WM, C::WN, F8 != 0, C::FM, C::FN>(p, block_row, m0, n0, wm0, wn0, lane,
+                                                               smem + wave * C::EPI_STAGE, bias_lds,
+                                                               (float*)(smem + C::RED_OFF), scale);
 }
 
 }  // namespace egm

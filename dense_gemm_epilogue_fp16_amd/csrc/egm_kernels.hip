@@ -4,6 +4,8 @@
 // -DEGM_F8=1..4, once per (fp8 format pair, 16-bit output dtype): the forward
 // epilogues only, on one-byte tiles with 128-deep k-slabs (the same bytes per
 // slab row as the 64-deep 16-bit slabs).
+#include <utility>
+
 #include "egm_epilogue.hpp"
 #include "egm_gemm.hpp"
 #include "egm_launch.hpp"
@@ -26,8 +28,22 @@ constexpr int ES = F8 == 0 ? 2 : 1;
 template <int EPI, int CFG, bool BT>
 void launch_gemm(dim3 grid, hipStream_t s, const GemmArgs& a) {
   constexpr ConfigInfo ci = kConfigs[CFG];
-  using C = TileCfg<ci.bm, ci.bn, ci.stages, ci.wm, ci.wn, ci.bk * (2 / ES), ES>;
+  using C = TileCfg<ci.bm, ci.bn, ci.stages, ci.wm, ci.wn, ci.bk * (2 / ES), ES, ci.mi>;
   hipLaunchKernelGGL((gemm_epilogue_kernel<DT, EPI, C, F8, BT>), grid, dim3(C::NT), 0, s, a);
+}
+
+// configs this unit builds: 16x16 MFMA blocks are 16-bit only
+template <int CFG>
+constexpr bool built_here() {
+  return F8 == 0 || kConfigs[CFG].mi == 32;
+}
+
+template <int EPI, bool BT, int... CFG>
+GemmLaunch pick_gemm(int cfg, std::integer_sequence<int, CFG...>) {
+  GemmLaunch out = nullptr;
+  ((cfg == CFG ? (out = built_here<CFG>() ? &launch_gemm<EPI, (built_here<CFG>() ? CFG : 0), BT> : nullptr) : out),
+   ...);
+  return out;
 }
 
 #if EGM_F8 == 0
@@ -64,15 +80,7 @@ LnLaunch ln_row(int cfg) {
 
 template <int EPI, bool BT>
 GemmLaunch gemm_row(int cfg) {
-  static_assert(kNumConfigs == 5, "update the launch table with the config table");
-  switch (cfg) {
-    case 0: return &launch_gemm<EPI, 0, BT>;
-    case 1: return &launch_gemm<EPI, 1, BT>;
-    case 2: return &launch_gemm<EPI, 2, BT>;
-    case 3: return &launch_gemm<EPI, 3, BT>;
-    case 4: return &launch_gemm<EPI, 4, BT>;
-    default: return nullptr;
-  }
+  return pick_gemm<EPI, BT>(cfg, std::make_integer_sequence<int, kNumConfigs>{});
 }
 
 template <bool BT>

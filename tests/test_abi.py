@@ -205,8 +205,8 @@ def test_execute_validation_before_any_hip_call(monkeypatch):
 
 
 @pytest.mark.parametrize("m,n,k,cfg", [
-    (256, 256, 512, 4),       # small square: 16 tiles of 64x64
-    (1024, 512, 2048, 4),     # the bias-fusion page's example shape
+    (256, 256, 512, 5),       # small square: 16 tiles of 64x64 (16x16x32 blocks for 16-bit operands)
+    (1024, 512, 2048, 5),     # the bias-fusion page's example shape
     (4096, 4096, 1024, 0),    # FFN up-projection: 256 tiles of 256x256, one per CU
     (4096, 1024, 4096, 3),    # FFN down-projection: 256 tiles of 128x128
     (8192, 8192, 8192, 0),
@@ -229,11 +229,12 @@ def grid_work_items(m, n, cfg):
 
 def test_grid_limit_narrows_the_choice():
     # one workgroup per tile in one grid dimension, at most 2^32 - 1
-    # work-items: for m = 2^31 - 1, n = 8 only the 256x128 tile (4 waves)
-    # fits; every 128- or 64-row tile and the 8-wave 256x256 tile would not
+    # work-items: for m = 2^31 - 1, n = 8 only the 256-row tiles of 4 waves
+    # fit; every 128- or 64-row tile and the 8-wave 256x256 tile would not
     m = (1 << 31) - 1
     fits = [c for c in range(egm.egm_num_configs()) if grid_work_items(m, 8, c) <= 0xFFFFFFFF]
-    assert fits == [1]
+    described = [dict(kv.split("=") for kv in egm.egm_config_describe(c).split()) for c in fits]
+    assert 1 in fits and all(d["tile"].startswith("256x") and d["waves"] == "2x2" for d in described)
     for kw in (dict(), dict(autotune=1)):
         h = egm.egm_plan(m, 8, 8, F16, E["BIAS"], FAKE, ROW, **kw)
         try:
@@ -265,8 +266,17 @@ def test_grid_limit_narrows_the_choice():
 
 def test_config_table():
     n = egm.egm_num_configs()
-    assert n == 5
+    assert n == 6
     assert egm.egm_config_describe(0).startswith("tile=256x256 kslab=64 waves=4x2")
+    # configs of 16x16x32 MFMA blocks exist for 16-bit operands only
+    for c in range(n):
+        d = dict(kv.split("=") for kv in egm.egm_config_describe(c).split())
+        st = egm.egm_plan_fp8(256, 256, 256, egm.EGM_E4M3, egm.EGM_E4M3, BF16, 0, 0, E["BIAS"], FAKE, COL,
+                              force_config=c, raw_status=True)[0]
+        if d["mfma"] == "16x16x32":
+            assert d["operands"] == "16-bit" and st == egm.EGM_ERR_NOT_SUPPORTED
+        else:
+            assert d["mfma"] == "32x32x16" and st == egm.EGM_OK
     for c in range(n):
         d = dict(kv.split("=") for kv in egm.egm_config_describe(c).split())
         bm, bn = (int(x) for x in d["tile"].split("x"))
@@ -462,3 +472,14 @@ def test_execute_no_alloc_validation_before_any_hip_call():
     finally:
         egm.egm_free(h)
     assert egm.egm_execute_no_alloc(h, FAKE, FAKE, FAKE, FAKE, raw_status=True) == egm.EGM_ERR_INVALID_PLAN
+
+
+def test_fp8_small_shapes_take_the_32x32_tile():
+    """The 16x16x32 tile exists for 16-bit operands only: fp8 plans of the
+    small shapes fall back to the 64x64 tile of 32x32x64 blocks."""
+    for m, n, k in ((256, 256, 512), (1024, 512, 2048)):
+        h = egm.egm_plan_fp8(m, n, k, egm.EGM_E4M3, egm.EGM_E4M3, BF16, 0, 0, E["BIAS"], FAKE, COL)
+        try:
+            assert egm.egm_plan_config(h) == 4
+        finally:
+            egm.egm_free(h)

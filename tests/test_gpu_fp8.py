@@ -9,7 +9,7 @@ from parity import compare, exact_bits, run_fp8
 
 pytestmark = pytest.mark.gpu
 
-CONFIGS = (0, 1, 2, 3, 4)
+CONFIGS = (0, 1, 2, 3, 4)  # the configs built for fp8 operands (32x32x64 MFMA blocks)
 PAIRS = [("e4m3", "e4m3"), ("e4m3", "e5m2"), ("e5m2", "e4m3"), ("e5m2", "e5m2")]
 FORWARD = ("DEFAULT", "BIAS", "RELU_BIAS", "GELU_BIAS", "RELU_AUX_BIAS", "BIAS_RESIDUAL")
 # product, bias and residual stds that keep |Y| well below 4, where bf16's half

@@ -14,7 +14,7 @@ pytestmark = pytest.mark.gpu
 
 EPILOGS_EXACT = ("DEFAULT", "BIAS", "RELU_BIAS", "RELU_AUX_BIAS", "BIAS_RESIDUAL")
 ALL_EPILOGS = EPILOGS_EXACT + ("GELU_BIAS",)
-CONFIGS = (0, 1, 2, 3, 4)
+CONFIGS = tuple(range(6))  # every tile config (5: 16x16x32 MFMA blocks)
 RAGGED = (300, 264, 136)  # m = 256+44, n = 256+8, k = 2*64+8
 
 
