@@ -49,6 +49,7 @@ inline constexpr ConfigInfo kConfigs[] = {
     {128, 128, 2, 2, 4, 64, 0.75, 32},
     {64, 64, 2, 2, 4, 64, 0.40, 32},
     {64, 64, 2, 2, 4, 64, 0.41, 16},
+    {32, 64, 1, 2, 4, 64, 0.25, 16},
 };
 inline constexpr int kNumConfigs = int(sizeof(kConfigs) / sizeof(kConfigs[0]));
 

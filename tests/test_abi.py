@@ -205,8 +205,8 @@ def test_execute_validation_before_any_hip_call(monkeypatch):
 
 
 @pytest.mark.parametrize("m,n,k,cfg", [
-    (256, 256, 512, 5),       # small square: 16 tiles of 64x64 (16x16x32 blocks for 16-bit operands)
-    (1024, 512, 2048, 5),     # the bias-fusion page's example shape
+    (256, 256, 512, 6),       # small square: 32 tiles of 32x64 (16x16x32 blocks, 16-bit operands)
+    (1024, 512, 2048, 6),     # the bias-fusion page's example shape: 256 tiles of 32x64, one per CU
     (4096, 4096, 1024, 0),    # FFN up-projection: 256 tiles of 256x256, one per CU
     (4096, 1024, 4096, 3),    # FFN down-projection: 256 tiles of 128x128
     (8192, 8192, 8192, 0),
@@ -266,7 +266,7 @@ def test_grid_limit_narrows_the_choice():
 
 def test_config_table():
     n = egm.egm_num_configs()
-    assert n == 6
+    assert n == 7
     assert egm.egm_config_describe(0).startswith("tile=256x256 kslab=64 waves=4x2")
     # configs of 16x16x32 MFMA blocks exist for 16-bit operands only
     for c in range(n):
@@ -307,10 +307,10 @@ def test_backward_workspace_and_execute_validation():
         assert egm.egm_execute(h, FAKE, FAKE, FAKE, FAKE, 0, 0, raw_status=True) == egm.EGM_ERR_WORKSPACE
     finally:
         egm.egm_free(h)
-    # autotuning may pick any tile: room for the smallest (64 x 64)
+    # autotuning may pick any tile: room for the shortest (32 rows: ceil(100/32) = 4 partial rows)
     h = egm.egm_plan(100, 64, 32, BF16, E["DRELU_BGRAD"], 0, COL, bias_grad=FAKE, autotune=1)
     try:
-        assert egm.egm_plan_workspace_bytes(h) == 2 * 64 * 4
+        assert egm.egm_plan_workspace_bytes(h) == 4 * 64 * 4
     finally:
         egm.egm_free(h)
     # (m,1) gradient, two-kernel path: one row of m per 32-column block of D, after P

@@ -24,7 +24,7 @@ def _stack(arrs, dtype):
     return torch.stack([to_device(a, dtype) for a in arrs])
 
 
-@pytest.mark.parametrize("cfg", list(range(6)))
+@pytest.mark.parametrize("cfg", list(range(7)))
 def test_strided_batch_shared_weight(cfg):
     """Five problems with their own A and one shared B (a weight), RELU_AUX_BIAS."""
     import torch
