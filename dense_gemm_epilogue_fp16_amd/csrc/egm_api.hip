@@ -69,13 +69,14 @@ bool config_built(int c, bool fp8) { return !fp8 || kConfigs[c].mi == 32; }
 // Per-shape choice: among the configs whose grid fits, the one with the
 // smallest estimated time, counting whole waves of tiles over the 256 CUs,
 // scaled by the config's relative efficiency.  Ties go to the lower id.  -1
-// when no config fits.
-int choose_config(int64_t m, int64_t n, int64_t k, bool fp8) {
+// when no config fits.  batch > 1: a strided batch of that many problems in
+// one launch (grid.y), whose tiles fill the CUs together.
+int choose_config(int64_t m, int64_t n, int64_t k, bool fp8, int64_t batch = 1) {
   int best = -1;
   double best_t = 0;
   for (int c = 0; c < kNumConfigs; ++c) {
     if (!grid_fits(m, n, c) || !config_built(c, fp8)) continue;
-    const int64_t tiles = cdiv(m, kConfigs[c].bm) * cdiv(n, kConfigs[c].bn);
+    const int64_t tiles = cdiv(m, kConfigs[c].bm) * cdiv(n, kConfigs[c].bn) * batch;
     const int64_t waves = cdiv(tiles, kNumCUs);
     const double t = double(waves) * kConfigs[c].bm * kConfigs[c].bn * double(k > 0 ? k : 1) / kConfigs[c].rel_eff;
     if (best < 0 || t < best_t * 0.999) {
@@ -101,6 +102,7 @@ struct egm_plan_s {
   int32_t fused;
   std::atomic<int32_t> config;            // rewritten once by a pending autotune
   int32_t group_m;
+  int32_t chosen_per_shape;               // config from the per-shape choice (not forced, not autotuned)
   std::atomic<int32_t> autotune_pending;
   std::mutex tune_mu;                     // one autotune per plan, even from several threads
   size_t workspace_bytes;
@@ -412,6 +414,7 @@ egm_status_t plan_impl(egm_plan_t* out, int64_t m, int64_t n, int64_t k, egm_dty
   p->b_transposed = b_transposed;
   p->fused = fused;
   p->config = force >= 0 ? force : choose_config(m, n, k, f8 != 0);
+  p->chosen_per_shape = force < 0 && !tune;
   // the launch must fit one grid dimension and the config exist for the
   // operand type (autotuning tries only such configs, and the per-shape
   // choice always is one)
@@ -591,8 +594,15 @@ egm_status_t egm_execute_strided(egm_plan_t plan, int64_t batch, const void* A, 
   // tuned on the first problem
   const egm_status_t tuned = tune_if_pending(p, A, B, D, aux, nullptr, s);
   if (tuned != EGM_OK) return tuned;
+  // a per-shape choice is made again for the whole batch (the tiles of all
+  // its problems share the CUs); a forced or autotuned config is kept
+  int cfg = p->config;
+  if (p->chosen_per_shape && batch > 1) {
+    const int c = choose_config(p->m, p->n, p->k, p->f8 != 0, batch);
+    if (c >= 0) cfg = c;
+  }
   const hipError_t err =
-      launch_plan(p, p->config, A, B, D, aux, nullptr, s, Batch{batch, stride_a, stride_b, stride_d, stride_aux});
+      launch_plan(p, cfg, A, B, D, aux, nullptr, s, Batch{batch, stride_a, stride_b, stride_d, stride_aux});
   return err == hipSuccess ? EGM_OK : EGM_ERR_HIP;
 }
 

@@ -289,7 +289,9 @@ egm_status_t egm_execute_no_alloc(egm_plan_t plan, const void* A, const void* B,
  * D + z*stride_d (output elements) and aux + z*stride_aux (bytes); a
  * BIAS_RESIDUAL residual advances with stride_d; the bias (bound at plan) is
  * shared.  The plan must be fused; DRELU_BGRAD is not supported (its partial
- * sums are per launch).  batch <= 65535; 0 does nothing.  Every problem's
+ * sums are per launch).  A plan whose tile config came from the per-shape
+ * choice (not forced, not autotuned) makes that choice again for the whole
+ * batch, whose tiles share the CUs; a forced or autotuned config is kept.  batch <= 65535; 0 does nothing.  Every problem's
  * pointers must keep 16-byte alignment, and outputs must not overlap
  * (stride_d >= m*n, stride_aux >= m*n/8 for batch > 1).  No workspace is
  * needed.  Asynchronous and stream-ordered like egm_execute.
