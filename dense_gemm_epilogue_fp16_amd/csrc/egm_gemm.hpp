@@ -254,6 +254,16 @@ __device__ __forceinline__ void wait_vmcnt() {
   __builtin_amdgcn_s_waitcnt((N & 0xf) | ((N >> 4) << 14) | (0x7 << 4) | (0xf << 8));
 }
 
+// The lane's index in its wave, computed afresh (v_mbcnt).  The epilogue
+// takes it from here rather than from threadIdx.x, so that its lane-derived
+// offsets are formed after the main loop instead of being kept (or spilled)
+// through it.
+__device__ __forceinline__ int lane_fresh() {
+  int l;
+  asm volatile("v_mbcnt_lo_u32_b32 %0, -1, 0\n\tv_mbcnt_hi_u32_b32 %0, -1, %0" : "=v"(l));
+  return l;
+}
+
 // Cross-lane moves for the bias-gradient sums (VALU only, no LDS traffic).
 // swap16(x, y): for each pair of 16-lane rows (0,1), (2,3), the odd row of x
 // trades places with the even row of y (v_permlane16_swap); swap32 does the
@@ -681,14 +691,31 @@ __global__ void __launch_bounds__(C::NT, 1) gemm_epilogue_kernel(GemmArgs p) {
     if constexpr (C::NW == 4) asm volatile("" : "+s"(b));
     return b;
   };
+  // fp8 tiles of two waves per SIMD use every register in the main loop.
+  // Per-lane k offset of copy u's piece within the slab (A, transposed B):
+  // in the main loop only slabs that end past K check it, and with B given
+  // transposed (the most registers) it is formed afresh from the lane index
+  // at each use there rather than held through the loop.
+  constexpr bool kTight = C::ES == 1 && C::NW == 8;
+  constexpr bool kLazyK = kTight && BT;
+  // q: the load's index among the operand's loads of the slab.
+  auto k_of = [&](const auto& k8, int u, uint32_t q) -> uint32_t {
+    if constexpr (kLazyK) {
+      const uint32_t l = (uint32_t)lane_fresh();
+      const uint32_t row = C::A_ROWS_PER_DMA * q + l / C::A_CHUNKS;
+      return ((l % C::A_CHUNKS) ^ a_swz<C::A_CHUNKS>(row)) * C::CE;
+    } else {
+      return k8[u];
+    }
+  };
   auto issue_one = [&](const SlabSrd& r, int stage, int q) {
     if (q < C::A_PW) {
       dma16(r.a, copy_base() + C::a_buf(stage) + (wave * C::A_PW + q) * 1024u,
-            r.kbase + a_k8[q] < (uint32_t)K ? a_off[q] : OOB_OFFSET);
+            r.kbase + k_of(a_k8, q, wave * C::A_PW + q) < (uint32_t)K ? a_off[q] : OOB_OFFSET);
     } else {
       const int u = q - C::A_PW;
       dma16(r.b, copy_base() + C::b_buf(stage) + (wave * C::B_PW + u) * 1024u,
-            !BT || r.kbase + b_k8[u] < (uint32_t)K ? b_off[u] : OOB_OFFSET);
+            !BT || r.kbase + k_of(b_k8, u, wave * C::B_PW + u) < (uint32_t)K ? b_off[u] : OOB_OFFSET);
     }
   };
 
@@ -970,7 +997,12 @@ __global__ void __launch_bounds__(C::NT, 1) gemm_epilogue_kernel(GemmArgs p) {
     read_slice(0, 0, 0);
     // slab kt sits in ring buffer st = kt % STAGES (a constant in each copy
     // of the body below)
-    auto slab = [&](int kt, int st) {
+    // refill == false (the slabs after the loop; fp8 two-wave tiles with B
+    // given transposed):
+    // the slab kt + STAGES that would be loaded lies past K, and with a
+    // two-slab ring the wait above is for every load anyway, so no empty
+    // loads need to keep the count
+    auto slab = [&](int kt, int st, bool refill) {
       const int st_next = st + 1 == C::STAGES ? 0 : st + 1;
 #pragma unroll
       for (int ks = 0; ks < C::NS - 1; ++ks) {
@@ -1018,12 +1050,18 @@ __global__ void __launch_bounds__(C::NT, 1) gemm_epilogue_kernel(GemmArgs p) {
           mfmas((C::NS - 1) & 1);
           interleave();
           __builtin_amdgcn_sched_barrier(0);
-          if (r.full) {
-            const uint32_t sa = smem_lds + C::a_buf(st);
+          if (!refill) {
+          } else if (r.full) {
+            const uint32_t sa = smem_lds + C::a_buf(st), sb = smem_lds + C::b_buf(st);
 #pragma unroll
             for (int q = 0; q < C::A_PW; ++q) dma16(r.a, sa + (wave * C::A_PW + q) * 1024u, a_off[q]);
 #pragma unroll
-            for (int q = C::A_PW; q < C::PW; ++q) issue_one(r, st, q);
+            for (int u = 0; u < C::B_PW; ++u) {
+              if constexpr (BT)
+                dma16(r.b, sb + (wave * C::B_PW + u) * 1024u, b_off[u]);  // no k check below K
+              else
+                issue_one(r, st, C::A_PW + u);
+            }
           } else {
 #pragma unroll
             for (int q = 0; q < C::PW; ++q) issue_one(r, st, q);
@@ -1063,11 +1101,11 @@ __global__ void __launch_bounds__(C::NT, 1) gemm_epilogue_kernel(GemmArgs p) {
     int kt = 0;
     for (; kt + C::STAGES <= KT; kt += C::STAGES) {
 #pragma unroll
-      for (int s = 0; s < C::STAGES; ++s) slab(kt + s, s);
+      for (int s = 0; s < C::STAGES; ++s) slab(kt + s, s, true);
     }
 #pragma unroll
     for (int s = 0; s < C::STAGES - 1; ++s)
-      if (kt + s < KT) slab(kt + s, s);
+      if (kt + s < KT) slab(kt + s, s, !(kLazyK && C::STAGES == 2));
   }
 
   // The epilogue takes the accumulators one 32-row block-row at a time, in
@@ -1112,7 +1150,7 @@ __global__ void __launch_bounds__(C::NT, 1) gemm_epilogue_kernel(GemmArgs p) {
   wait_vmcnt<0>();
   // the ring is free once every wave is past its last fragment read
   __syncthreads();
-  epilogue_store<DT, EPI, C::WM, C::WN, F8 != 0, C::FM, C::FN>(p, block_row, m0, n0, wm0, wn0, lane,
+  epilogue_store<DT, EPI, C::WM, C::WN, F8 != 0, C::FM, C::FN>(p, block_row, m0, n0, wm0, wn0, kTight ? lane_fresh() : lane,
                                                                smem + wave * C::EPI_STAGE, bias_lds,
                                                                (float*)(smem + C::RED_OFF), scale);
 }

@@ -70,12 +70,15 @@ def test_normal_every_epilog(cfg):
         compare(d, y, "bf16", z=z, mask=mask, mask_ref=mref)
 
 
+@pytest.mark.parametrize("k", [144, 272])
 @pytest.mark.parametrize("cfg", FP8_CONFIGS)
-def test_fp8_pairs(cfg):
+def test_fp8_pairs(cfg, k):
+    """k = 144: two 128-deep k-slabs, the second ragged; k = 272: three, so
+    the two-slab ring of config 0 ends on a slab after its main loop."""
     import torch
     import dense_gemm_epilogue_fp16_amd as egm
     for fa, fb in [("e4m3", "e4m3"), ("e4m3", "e5m2"), ("e5m2", "e4m3"), ("e5m2", "e5m2")]:
-        ops = W.fp8_integer_operands(304, 272, 144, fa, fb, "bf16", seed=cfg, bias_layout="col", scale_a=0.5,
+        ops = W.fp8_integer_operands(304, 272, k, fa, fb, "bf16", seed=cfg + k, bias_layout="col", scale_a=0.5,
                                      scale_b=4.0)
         a = fp8_to_device(ops.a, fa)
         w = fp8_to_device(np.ascontiguousarray(ops.b.T), fb)
