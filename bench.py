@@ -113,8 +113,8 @@ def main():
                          "print one JSON line per second with its throughput and the board power and clocks "
                          "that amd-smi reports meanwhile")
     ap.add_argument("--sustain-vendor", action="store_true",
-                    help="with --sustain, 16-bit workloads: then run the vendor GEMM alone (torch.matmul into "
-                         "the same outputs) the same way, for the clock and power it sustains (context only)")
+                    help="with --sustain: then run the vendor GEMM alone (torch.matmul into the same outputs; "
+                         "torch._scaled_mm for fp8) the same way, for the clock and power it sustains (context only)")
     args = ap.parse_args()
     if args.ingest_pmc:
         ingest_pmc(args.workload, *args.ingest_pmc, copy_mib=args.copy_mib or 1024)
@@ -254,12 +254,20 @@ def main():
         sustain(lambda: step(fused_plans), probe_ms, flops, args.sustain, dev, stream)
         if args.sustain_vendor:
             if fp8:
-                raise SystemExit("--sustain-vendor covers the 16-bit workloads")
-            print(json.dumps({"leg": "vendor GEMM alone (torch.matmul), context only"}), flush=True)
+                print(json.dumps({"leg": "vendor fp8 GEMM alone (torch._scaled_mm, B column-major), context only"}),
+                      flush=True)
+                (aa, bb), _, _, _, _, _ = specs[0]
+                bcm = bb.t().contiguous().t()  # the vendor call wants B column-major
 
-            def vendor_step():
-                for (aa, bb), _, _, out, _, _ in specs:
-                    torch.matmul(aa, bb, out=out["out"])
+                def vendor_step():
+                    torch._scaled_mm(aa, bcm, scale_a=mm_kw["scale_a"], scale_b=mm_kw["scale_b"],
+                                     out_dtype=mm_kw["out_dtype"])
+            else:
+                print(json.dumps({"leg": "vendor GEMM alone (torch.matmul), context only"}), flush=True)
+
+                def vendor_step():
+                    for (aa, bb), _, _, out, _, _ in specs:
+                        torch.matmul(aa, bb, out=out["out"])
 
             vendor_step()
             torch.cuda.synchronize(dev)
