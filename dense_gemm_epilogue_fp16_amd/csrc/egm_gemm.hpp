@@ -403,6 +403,25 @@ __device__ __forceinline__ void epilogue_store(const GemmArgs& p, BlockRow&& blo
         }
       }
   }
+  // the residual: with at most four waves (registers to spare after the main
+  // loop) every piece of the wave tile is requested at once, ahead of the
+  // block-rows, so that the loads' latency is paid once and not once per
+  // block-row (whose stores would otherwise wait behind them); 8-wave tiles
+  // load each block-row's pieces with it
+  constexpr bool kResidAhead = EPI == EPI_RESID && WM * WN <= 4;
+  u32x2 resid[FM][FN][4];
+  if constexpr (kResidAhead) {
+#pragma unroll
+    for (int i = 0; i < FM; ++i)
+#pragma unroll
+      for (int j = 0; j < FN; ++j)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          const int col = n0 + wn0 + 32 * j + 8 * g + 4 * lh;
+          const uint32_t lrow = wm0 + 32 * i + lr;
+          resid[i][j][g] = buf_load8(rR, col < N ? lrow * rowbytes + (uint32_t)col * 2u : OOB_OFFSET);
+        }
+  }
   // bias gradient: this wave's sums of dZ over its rows, one per column of
   // block j and lane (colacc, (1,n) bias), or over its columns, one per row of
   // block i (rowacc, (m,1) bias); added up in a fixed order
@@ -438,7 +457,6 @@ __device__ __forceinline__ void epilogue_store(const GemmArgs& p, BlockRow&& blo
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
         const int col = n0 + wn0 + 32 * j + 8 * g + 4 * lh;
-        const uint32_t off = col < N ? lrow * rowbytes + (uint32_t)col * 2u : OOB_OFFSET;
         float z[4];
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
@@ -452,7 +470,8 @@ __device__ __forceinline__ void epilogue_store(const GemmArgs& p, BlockRow&& blo
           }
         }
         if constexpr (EPI == EPI_RESID) {
-          const u32x2 rv = buf_load8(rR, off);
+          const u32x2 rv = kResidAhead ? resid[i][j][g]
+                                       : buf_load8(rR, col < N ? lrow * rowbytes + (uint32_t)col * 2u : OOB_OFFSET);
           z[0] += lo_f32<DT>(rv[0]);
           z[1] += hi_f32<DT>(rv[0]);
           z[2] += lo_f32<DT>(rv[1]);
