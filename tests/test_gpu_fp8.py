@@ -81,6 +81,34 @@ def test_normal_format_pairs(pair, out):
         compare(d, y, out, unfused=True)
 
 
+def test_random_shapes_sweep():
+    """32 seeded random fp8 cases, bit-exact on small-integer operands with
+    power-of-two scales: m from 1 to 600, n and k multiples of 16 up to 640
+    and 1024, every fp8 config, format pair, output dtype, bias layout and
+    exact epilogue drawn at random."""
+    rng = np.random.default_rng(808)
+    epilogs = ("DEFAULT", "BIAS", "RELU_BIAS", "RELU_AUX_BIAS", "BIAS_RESIDUAL")
+    for case in range(32):
+        m = int(rng.integers(1, 601))
+        n = 16 * int(rng.integers(1, 41))
+        k = 16 * int(rng.integers(1, 65))
+        fa, fb = PAIRS[int(rng.integers(len(PAIRS)))]
+        out = ("fp16", "bf16")[int(rng.integers(2))]
+        epilog = epilogs[int(rng.integers(len(epilogs)))]
+        cfg = CONFIGS[int(rng.integers(len(CONFIGS)))]
+        layout = ("row", "col")[int(rng.integers(2))]
+        tag = f"case {case}: {m}x{n}x{k} {fa}x{fb}->{out} {epilog} cfg={cfg} bias={layout}"
+        print(tag, flush=True)
+        ops = W.fp8_integer_operands(m, n, k, fa, fb, out, seed=900 + case, bias_layout=layout, scale_a=0.5,
+                                     scale_b=2.0, residual=True)
+        y, z, mref = _ref(ops, epilog)
+        d, mask = run_fp8(ops, epilog, force_config=cfg)
+        bad = d != exact_bits(y, out)
+        assert not bad.any(), f"{tag}: {int(bad.sum())} outputs differ; first {tuple(np.argwhere(bad)[0])}"
+        if mref is not None:
+            assert np.array_equal(mask, mref), f"{tag}: mask differs"
+
+
 def test_edges_null_scales_and_k0():
     import torch
     import dense_gemm_epilogue_fp16_amd as egm

@@ -86,6 +86,31 @@ def test_normal_within_tolerance(dtype, epilog, cfg):
     compare(d, y, dtype, z=z, mask=mask, mask_ref=mref)
 
 
+def test_random_shapes_sweep():
+    """48 seeded random cases, bit-exact on small-integer operands: m from 1
+    to 700, n and k multiples of 8 up to 720 and 1040, every config, dtype,
+    bias layout and exact epilogue drawn at random (fp32 sums stay exact, so
+    D is the single correct rounding of the exact result whatever the shape)."""
+    rng = np.random.default_rng(2024)
+    for case in range(48):
+        m = int(rng.integers(1, 701))
+        n = 8 * int(rng.integers(1, 91))
+        k = 8 * int(rng.integers(1, 131))
+        dtype = ("fp16", "bf16")[int(rng.integers(2))]
+        epilog = EPILOGS_EXACT[int(rng.integers(len(EPILOGS_EXACT)))]
+        cfg = int(rng.integers(len(CONFIGS)))
+        layout = ("row", "col")[int(rng.integers(2))]
+        tag = f"case {case}: {m}x{n}x{k} {dtype} {epilog} cfg={cfg} bias={layout}"
+        print(tag, flush=True)
+        ops = W.integer_operands(m, n, k, dtype, seed=500 + case, bias_layout=layout, residual=True)
+        d, mask = run(ops, epilog, force_config=cfg)
+        y, z, mref = oracle_for(ops, epilog)
+        bad = d != exact_bits(y, dtype)
+        assert not bad.any(), f"{tag}: {int(bad.sum())} outputs differ; first {tuple(np.argwhere(bad)[0])}"
+        if epilog == "RELU_AUX_BIAS":
+            assert np.array_equal(mask, mref), f"{tag}: mask differs"
+
+
 @pytest.mark.parametrize("epilog", ["BIAS", "RELU_BIAS", "GELU_BIAS", "RELU_AUX_BIAS", "BIAS_RESIDUAL"])
 @pytest.mark.parametrize("dtype", ["fp16", "bf16"])
 def test_unfused_path(dtype, epilog):

@@ -93,6 +93,57 @@ def test_fp8_pairs(cfg, k):
         assert np.array_equal(mask.cpu().numpy(), mref)
 
 
+def test_random_shapes_sweep():
+    """Seeded random cases with B given transposed, bit-exact on small-integer
+    operands: 24 in 16 bits (m 1..700, n and k multiples of 8 up to 720 and
+    1040, every config) and 16 in fp8 (n and k multiples of 16, the fp8
+    configs, every format pair, power-of-two scales)."""
+    import torch
+    import dense_gemm_epilogue_fp16_amd as egm
+    rng = np.random.default_rng(4242)
+    epilogs = ("DEFAULT", "BIAS", "RELU_BIAS", "RELU_AUX_BIAS", "BIAS_RESIDUAL")
+    for case in range(24):
+        m, n, k = int(rng.integers(1, 701)), 8 * int(rng.integers(1, 91)), 8 * int(rng.integers(1, 131))
+        dtype = ("fp16", "bf16")[int(rng.integers(2))]
+        epilog = epilogs[int(rng.integers(len(epilogs)))]
+        cfg = CONFIGS[int(rng.integers(len(CONFIGS)))]
+        layout = ("row", "col")[int(rng.integers(2))]
+        tag = f"case {case}: {m}x{n}x{k} {dtype} {epilog} cfg={cfg} bias={layout}"
+        print(tag, flush=True)
+        ops = W.integer_operands(m, n, k, dtype, seed=700 + case, bias_layout=layout, residual=True)
+        y, z, mref = eo.reference(ops.a, ops.b, dtype, epilog, None if epilog == "DEFAULT" else ops.bias,
+                                  None if epilog == "DEFAULT" else layout, ops.residual)
+        d, mask = _run_bt(ops, epilog, force_config=cfg)
+        bad = d != exact_bits(y, dtype)
+        assert not bad.any(), f"{tag}: {int(bad.sum())} outputs differ; first {tuple(np.argwhere(bad)[0])}"
+        if mref is not None:
+            assert np.array_equal(mask, mref), f"{tag}: mask differs"
+    pairs = [("e4m3", "e4m3"), ("e4m3", "e5m2"), ("e5m2", "e4m3"), ("e5m2", "e5m2")]
+    for case in range(16):
+        m, n, k = int(rng.integers(1, 601)), 16 * int(rng.integers(1, 41)), 16 * int(rng.integers(1, 65))
+        fa, fb = pairs[int(rng.integers(4))]
+        out = ("fp16", "bf16")[int(rng.integers(2))]
+        cfg = FP8_CONFIGS[int(rng.integers(len(FP8_CONFIGS)))]
+        layout = ("row", "col")[int(rng.integers(2))]
+        tag = f"fp8 case {case}: {m}x{n}x{k} {fa}x{fb}->{out} cfg={cfg} bias={layout}"
+        print(tag, flush=True)
+        ops = W.fp8_integer_operands(m, n, k, fa, fb, out, seed=800 + case, bias_layout=layout, scale_a=2.0,
+                                     scale_b=0.5)
+        a = fp8_to_device(ops.a, fa)
+        w = fp8_to_device(np.ascontiguousarray(ops.b.T), fb)
+        tdt = torch.float16 if out == "fp16" else torch.bfloat16
+        with egm.Matmul(a, w.t(), scale_a=scale_tensor(ops.scale_a), scale_b=scale_tensor(ops.scale_b),
+                        out_dtype=tdt) as mm:
+            mm.plan("RELU_AUX_BIAS", {"bias": bias_tensor(ops.bias, layout, out)}, force_config=cfg)
+            d, mask = mm.execute()
+            torch.cuda.synchronize()
+        y, z, mref = eo.reference_fp8(ops.a, ops.b, fa, fb, ops.scale_a, ops.scale_b, out, "RELU_AUX_BIAS",
+                                      ops.bias, layout)
+        bad = to_host_bits(d) != exact_bits(y, out)
+        assert not bad.any(), f"{tag}: {int(bad.sum())} outputs differ"
+        assert np.array_equal(mask.cpu().numpy(), mref), f"{tag}: mask differs"
+
+
 def test_backward_and_strided_batch():
     import torch
     import dense_gemm_epilogue_fp16_amd as egm
