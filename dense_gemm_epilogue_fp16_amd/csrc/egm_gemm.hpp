@@ -264,6 +264,7 @@ __device__ __forceinline__ int lane_fresh() {
   return l;
 }
 
+
 // Cross-lane moves for the bias-gradient sums (VALU only, no LDS traffic).
 // swap16(x, y): for each pair of 16-lane rows (0,1), (2,3), the odd row of x
 // trades places with the even row of y (v_permlane16_swap); swap32 does the
@@ -638,13 +639,19 @@ __global__ void __launch_bounds__(C::NT, 1) gemm_epilogue_kernel(GemmArgs p) {
   // lane L -> row R*q + L/A_CHUNKS, physical chunk L%A_CHUNKS, which holds
   // logical chunk (L%A_CHUNKS) ^ a_swz(row).  Offsets are relative to the
   // slab's first column; columns past K read 0.
-  uint32_t a_off[C::A_PW], a_k8[C::A_PW];
+  // (fp8 tiles of two waves per SIMD, whose main loop uses every register:
+  // with B given transposed, the logical chunk of every copy sits in one
+  // register, 4 bits each, copy q at bits 4q: k_lc)
+  constexpr bool kTight = C::ES == 1 && C::NW == 8;
+  static_assert(!kTight || C::PW <= 8, "packed chunk indices: at most 8 copies per wave and slab");
+  uint32_t a_off[C::A_PW], a_k8[C::A_PW], k_lc = 0;
 #pragma unroll
   for (int u = 0; u < C::A_PW; ++u) {
     const uint32_t q = wave * C::A_PW + u;
     const uint32_t row = C::A_ROWS_PER_DMA * q + lane / C::A_CHUNKS;
     const uint32_t lc = (lane % C::A_CHUNKS) ^ a_swz<C::A_CHUNKS>(row);
     a_k8[u] = lc * C::CE;
+    if constexpr (kTight && BT) k_lc |= lc << (4 * u);
     a_off[u] = (row * (uint32_t)K + lc * C::CE) * C::ES;
   }
   // B load q fills k-rows q*R .. q*R+R-1 (R = B_ROWS_PER_DMA): lane L -> k-row
@@ -661,6 +668,7 @@ __global__ void __launch_bounds__(C::NT, 1) gemm_epilogue_kernel(GemmArgs p) {
       const uint32_t row = C::A_ROWS_PER_DMA * q + lane / C::A_CHUNKS;
       const uint32_t lc = (lane % C::A_CHUNKS) ^ a_swz<C::A_CHUNKS>(row);
       b_k8[u] = lc * C::CE;
+      if constexpr (kTight && BT) k_lc |= lc << (4 * (C::A_PW + u));
       b_off[u] = (row * (uint32_t)K + lc * C::CE) * C::ES;
     } else {
       const uint32_t krow = q * C::B_ROWS_PER_DMA + lane / C::B_CHUNKS;
@@ -700,41 +708,36 @@ __global__ void __launch_bounds__(C::NT, 1) gemm_epilogue_kernel(GemmArgs p) {
   };
   // Load q (0 .. PW-1) of this wave for a slab into ring buffer `stage`: the
   // first A_PW are A loads, the rest B loads.
-  // LDS base of the copies.  With one wave per SIMD (4 waves) the compiler
-  // would otherwise hoist every copy's LDS address (one per copy and ring
-  // buffer) out of the main loop into registers of their own, and spill
-  // them; an opaque base keeps each address a couple of scalar additions at
-  // its copy.
+  // LDS base of the copies.  With one wave per SIMD (4 waves), and in the
+  // fp8 two-wave tile, the compiler would otherwise hoist every copy's LDS
+  // address (one per copy and ring buffer) out of the main loop into
+  // registers of their own, and spill them; an opaque base keeps each
+  // address a couple of scalar additions at its copy.
   auto copy_base = [&]() {
     uint32_t b = smem_lds;
-    if constexpr (C::NW == 4) asm volatile("" : "+s"(b));
+    if constexpr (C::NW == 4 || kTight) asm volatile("" : "+s"(b));
     return b;
   };
-  // fp8 tiles of two waves per SIMD use every register in the main loop.
-  // Per-lane k offset of copy u's piece within the slab (A, transposed B):
-  // in the main loop only slabs that end past K check it, and with B given
-  // transposed (the most registers) it is formed afresh from the lane index
-  // at each use there rather than held through the loop.
-  constexpr bool kTight = C::ES == 1 && C::NW == 8;
-  constexpr bool kLazyK = kTight && BT;
-  // q: the load's index among the operand's loads of the slab.
-  auto k_of = [&](const auto& k8, int u, uint32_t q) -> uint32_t {
-    if constexpr (kLazyK) {
-      const uint32_t l = (uint32_t)lane_fresh();
-      const uint32_t row = C::A_ROWS_PER_DMA * q + l / C::A_CHUNKS;
-      return ((l % C::A_CHUNKS) ^ a_swz<C::A_CHUNKS>(row)) * C::CE;
-    } else {
+  // Per-lane k offset of copy u's piece within the slab (A, transposed B);
+  // j: the copy's index among this wave's copies of the slab.
+  auto k_of = [&](const auto& k8, int u, int j) -> uint32_t {
+    if constexpr (kTight && BT) {
+      // taken apart at each use (an opaque copy), so that the compiler does
+      // not hoist the eight offsets out of the main loop into registers
+      uint32_t kl = k_lc;
+      asm volatile("" : "+v"(kl));
+      return ((kl >> (4 * j)) & 7u) * C::CE;
+    } else
       return k8[u];
-    }
   };
   auto issue_one = [&](const SlabSrd& r, int stage, int q) {
     if (q < C::A_PW) {
       dma16(r.a, copy_base() + C::a_buf(stage) + (wave * C::A_PW + q) * 1024u,
-            r.kbase + k_of(a_k8, q, wave * C::A_PW + q) < (uint32_t)K ? a_off[q] : OOB_OFFSET);
+            r.kbase + k_of(a_k8, q, q) < (uint32_t)K ? a_off[q] : OOB_OFFSET);
     } else {
       const int u = q - C::A_PW;
       dma16(r.b, copy_base() + C::b_buf(stage) + (wave * C::B_PW + u) * 1024u,
-            !BT || r.kbase + k_of(b_k8, u, wave * C::B_PW + u) < (uint32_t)K ? b_off[u] : OOB_OFFSET);
+            !BT || r.kbase + k_of(b_k8, u, q) < (uint32_t)K ? b_off[u] : OOB_OFFSET);
     }
   };
 
@@ -940,46 +943,43 @@ __global__ void __launch_bounds__(C::NT, 1) gemm_epilogue_kernel(GemmArgs p) {
 #pragma unroll
     for (int q = 0; q < NRD; ++q) read_piece(set, stage, ks, q);
   };
-  auto mfmas = [&](int set) {
+  // MFMA t of a k-slice (i outer, j inner)
+  auto mfma_one = [&](int set, int t) {
     if constexpr (M16) {
-#pragma unroll
-      for (int i = 0; i < C::FM16; ++i)
-#pragma unroll
-        for (int j = 0; j < C::FN16; ++j) {
-          if constexpr (BT)
-            acc16[i][j] = mfma16<DT>(fbt[set][j][0], fa[set][i][0], acc16[i][j]);
-          else
-            acc16[i][j] = mfma16<DT>(u32x4{fb[set][j][0][0], fb[set][j][0][1], fb[set][j][1][0], fb[set][j][1][1]},
-                                     fa[set][i][0], acc16[i][j]);
-        }
+      const int i = t / C::FN16, j = t % C::FN16;
+      if constexpr (BT)
+        acc16[i][j] = mfma16<DT>(fbt[set][j][0], fa[set][i][0], acc16[i][j]);
+      else
+        acc16[i][j] = mfma16<DT>(u32x4{fb[set][j][0][0], fb[set][j][0][1], fb[set][j][1][0], fb[set][j][1][1]},
+                                 fa[set][i][0], acc16[i][j]);
     } else {
-#pragma unroll
-      for (int i = 0; i < C::FM; ++i)
-#pragma unroll
-        for (int j = 0; j < C::FN; ++j) {
-          if constexpr (BT && C::ES == 2) {
-            acc[i][j] = mfma32<DT>(fbt[set][j][0], fa[set][i][0], acc[i][j]);
-          } else if constexpr (BT) {
-            constexpr int FA = (F8 - 1) & 1, FB = (F8 - 1) >> 1;
-            const u32x8 b8{fbt[set][j][0][0], fbt[set][j][0][1], fbt[set][j][0][2], fbt[set][j][0][3],
-                           fbt[set][j][1][0], fbt[set][j][1][1], fbt[set][j][1][2], fbt[set][j][1][3]};
-            const u32x8 a8{fa[set][i][0][0], fa[set][i][0][1], fa[set][i][0][2], fa[set][i][0][3],
-                           fa[set][i][1][0], fa[set][i][1][1], fa[set][i][1][2], fa[set][i][1][3]};
-            acc[i][j] = mfma32_f8<FB, FA>(b8, a8, acc[i][j]);
-          } else if constexpr (C::ES == 2) {
-            acc[i][j] = mfma32<DT>(u32x4{fb[set][j][0][0], fb[set][j][0][1], fb[set][j][1][0], fb[set][j][1][1]},
-                                   fa[set][i][0], acc[i][j]);
-          } else {
-            // B is the first operand (format FB), A the second (format FA)
-            constexpr int FA = (F8 - 1) & 1, FB = (F8 - 1) >> 1;
-            const u32x8 b8{fb[set][j][0][0], fb[set][j][0][1], fb[set][j][1][0], fb[set][j][1][1],
-                           fb[set][j][2][0], fb[set][j][2][1], fb[set][j][3][0], fb[set][j][3][1]};
-            const u32x8 a8{fa[set][i][0][0], fa[set][i][0][1], fa[set][i][0][2], fa[set][i][0][3],
-                           fa[set][i][RA - 1][0], fa[set][i][RA - 1][1], fa[set][i][RA - 1][2], fa[set][i][RA - 1][3]};
-            acc[i][j] = mfma32_f8<FB, FA>(b8, a8, acc[i][j]);
-          }
-        }
+      const int i = t / C::FN, j = t % C::FN;
+      if constexpr (BT && C::ES == 2) {
+        acc[i][j] = mfma32<DT>(fbt[set][j][0], fa[set][i][0], acc[i][j]);
+      } else if constexpr (BT) {
+        constexpr int FA = (F8 - 1) & 1, FB = (F8 - 1) >> 1;
+        const u32x8 b8{fbt[set][j][0][0], fbt[set][j][0][1], fbt[set][j][0][2], fbt[set][j][0][3],
+                       fbt[set][j][1][0], fbt[set][j][1][1], fbt[set][j][1][2], fbt[set][j][1][3]};
+        const u32x8 a8{fa[set][i][0][0], fa[set][i][0][1], fa[set][i][0][2], fa[set][i][0][3],
+                       fa[set][i][1][0], fa[set][i][1][1], fa[set][i][1][2], fa[set][i][1][3]};
+        acc[i][j] = mfma32_f8<FB, FA>(b8, a8, acc[i][j]);
+      } else if constexpr (C::ES == 2) {
+        acc[i][j] = mfma32<DT>(u32x4{fb[set][j][0][0], fb[set][j][0][1], fb[set][j][1][0], fb[set][j][1][1]},
+                               fa[set][i][0], acc[i][j]);
+      } else {
+        // B is the first operand (format FB), A the second (format FA)
+        constexpr int FA = (F8 - 1) & 1, FB = (F8 - 1) >> 1;
+        const u32x8 b8{fb[set][j][0][0], fb[set][j][0][1], fb[set][j][1][0], fb[set][j][1][1],
+                       fb[set][j][2][0], fb[set][j][2][1], fb[set][j][3][0], fb[set][j][3][1]};
+        const u32x8 a8{fa[set][i][0][0], fa[set][i][0][1], fa[set][i][0][2], fa[set][i][0][3],
+                       fa[set][i][RA - 1][0], fa[set][i][RA - 1][1], fa[set][i][RA - 1][2], fa[set][i][RA - 1][3]};
+        acc[i][j] = mfma32_f8<FB, FA>(b8, a8, acc[i][j]);
+      }
     }
+  };
+  auto mfmas = [&](int set) {
+#pragma unroll
+    for (int t = 0; t < NMF; ++t) mfma_one(set, t);
   };
   // Scheduling hint for one k-slice: alternate the MFMAs with the LDS reads
   // of the next k-slice, reads first, so neither the MFMA pipe nor the LDS
@@ -1016,11 +1016,10 @@ __global__ void __launch_bounds__(C::NT, 1) gemm_epilogue_kernel(GemmArgs p) {
     read_slice(0, 0, 0);
     // slab kt sits in ring buffer st = kt % STAGES (a constant in each copy
     // of the body below)
-    // refill == false (the slabs after the loop; fp8 two-wave tiles with B
-    // given transposed):
-    // the slab kt + STAGES that would be loaded lies past K, and with a
-    // two-slab ring the wait above is for every load anyway, so no empty
-    // loads need to keep the count
+    // refill == false (the slabs after the loop; fp8 two-wave tiles): the
+    // slab kt + STAGES that would be loaded lies past K, and with a two-slab
+    // ring the wait above is for every load anyway, so no empty loads need
+    // to keep the count
     auto slab = [&](int kt, int st, bool refill) {
       const int st_next = st + 1 == C::STAGES ? 0 : st + 1;
 #pragma unroll
@@ -1038,54 +1037,49 @@ __global__ void __launch_bounds__(C::NT, 1) gemm_epilogue_kernel(GemmArgs p) {
       asm volatile("" ::: "memory");
       __builtin_amdgcn_sched_barrier(0);
       const SlabSrd r = slab_srd(kt + C::STAGES);
-      if constexpr (C::NW == 8) {
-        // two waves per SIMD.  16-bit tiles: the A refill goes out right
+      if constexpr (kTight) {
+        // fp8, two waves per SIMD: the refill is spread over the last
+        // k-slice, in program order MFMA t, then its share of the next
+        // slab's first-slice reads, then its share of this wave's copies
+        // (one per MFMA).  Issued in one burst after the MFMAs, the copies
+        // of all eight waves kept the address unit's command queue full
+        // (SQ_VMEM_TA_CMD_FIFO_FULL) and stalled the waves behind them:
+        // spread, 8192^3 E4M3 runs 4-5 % faster.  Every copy takes the k
+        // check here: a uniform branch around copies inside the MFMA
+        // sequence made the compiler spill.
+#pragma unroll
+        for (int t = 0; t < NMF; ++t) {
+          mfma_one((C::NS - 1) & 1, t);
+#pragma unroll
+          for (int pc = t * NRD / NMF; pc < (t + 1) * NRD / NMF; ++pc) read_piece(0, st_next, 0, pc);
+          if (refill) {
+#pragma unroll
+            for (int q = t * C::PW / NMF; q < (t + 1) * C::PW / NMF; ++q) issue_one(r, st, q);
+          }
+        }
+      } else if constexpr (C::NW == 8) {
+        // two waves per SIMD, 16-bit tiles: the A refill goes out right
         // after the barrier, the last k-slice's reads and MFMAs next, the B
         // refill after them (measured 1.5-2 % faster on the large shapes than
         // the whole refill after the MFMAs, which is faster than the whole
-        // refill first or interleaved).  fp8 tiles issue the whole refill
-        // after the MFMAs: their registers are fully used, and holding the A
-        // copies' operands across the slice made the compiler spill.
-        // (A uniform branch drops the per-lane k check of the A copies in
-        // every slab below K.)
-        if constexpr (C::ES == 2) {
-          const uint32_t sa = smem_lds + C::a_buf(st);
-          if (r.full) {
+        // refill first; spreading the copies one per MFMA as the fp8 tile
+        // does was 2-4 % slower here).  A uniform branch drops the per-lane
+        // k check of the A copies in every slab below K.
+        const uint32_t sa = smem_lds + C::a_buf(st);
+        if (r.full) {
 #pragma unroll
-            for (int q = 0; q < C::A_PW; ++q) dma16(r.a, sa + (wave * C::A_PW + q) * 1024u, a_off[q]);
-          } else {
-#pragma unroll
-            for (int q = 0; q < C::A_PW; ++q) issue_one(r, st, q);
-          }
-          __builtin_amdgcn_sched_barrier(0);
-          read_slice(0, st_next, 0);
-          mfmas((C::NS - 1) & 1);
-          interleave();
-          __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-          for (int q = C::A_PW; q < C::PW; ++q) issue_one(r, st, q);
+          for (int q = 0; q < C::A_PW; ++q) dma16(r.a, sa + (wave * C::A_PW + q) * 1024u, a_off[q]);
         } else {
-          read_slice(0, st_next, 0);
-          mfmas((C::NS - 1) & 1);
-          interleave();
-          __builtin_amdgcn_sched_barrier(0);
-          if (!refill) {
-          } else if (r.full) {
-            const uint32_t sa = smem_lds + C::a_buf(st), sb = smem_lds + C::b_buf(st);
 #pragma unroll
-            for (int q = 0; q < C::A_PW; ++q) dma16(r.a, sa + (wave * C::A_PW + q) * 1024u, a_off[q]);
-#pragma unroll
-            for (int u = 0; u < C::B_PW; ++u) {
-              if constexpr (BT)
-                dma16(r.b, sb + (wave * C::B_PW + u) * 1024u, b_off[u]);  // no k check below K
-              else
-                issue_one(r, st, C::A_PW + u);
-            }
-          } else {
-#pragma unroll
-            for (int q = 0; q < C::PW; ++q) issue_one(r, st, q);
-          }
+          for (int q = 0; q < C::A_PW; ++q) issue_one(r, st, q);
         }
+        __builtin_amdgcn_sched_barrier(0);
+        read_slice(0, st_next, 0);
+        mfmas((C::NS - 1) & 1);
+        interleave();
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int q = C::A_PW; q < C::PW; ++q) issue_one(r, st, q);
         __builtin_amdgcn_sched_barrier(0);
       } else {
         // one wave per SIMD: the refill loads go out one at a time between the
@@ -1124,7 +1118,7 @@ __global__ void __launch_bounds__(C::NT, 1) gemm_epilogue_kernel(GemmArgs p) {
     }
 #pragma unroll
     for (int s = 0; s < C::STAGES - 1; ++s)
-      if (kt + s < KT) slab(kt + s, s, !(kLazyK && C::STAGES == 2));
+      if (kt + s < KT) slab(kt + s, s, !(kTight && C::STAGES == 2));
   }
 
   // The epilogue takes the accumulators one 32-row block-row at a time, in
