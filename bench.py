@@ -42,13 +42,21 @@ PEAK_TFLOPS_FP8 = 5000.0  # MI355X dense fp8 MFMA (published)
 PEAK_HBM_GBS = 8000.0     # MI355X HBM3E (published)
 DEFAULT_WORKLOAD = "gemm_relu_bias_fp16_65536x16384x16384"
 # device code of the fused kernel and the config table that picks its instance
-KERNEL_SOURCES = ("egm_gemm.hpp", "egm_device.hpp", "egm_kernels.hip", "egm_launch.hpp", "egm_epilogue.hpp",
-                  "egm_layernorm.hpp")
+# the sources each kernel family is built from: a traffic record taken on a
+# family's kernels stays valid until one of these files changes
+KERNEL_SOURCES = {
+    "gemm": ("egm_gemm.hpp", "egm_device.hpp", "egm_kernels.hip", "egm_launch.hpp", "egm_epilogue.hpp"),
+    "layernorm": ("egm_layernorm.hpp", "egm_device.hpp", "egm_kernels.hip", "egm_launch.hpp"),
+}
 
 
-def kernel_source_hash() -> str:
+def kernel_family(workload: str) -> str:
+    return "layernorm" if workload.startswith("layernorm") else "gemm"
+
+
+def kernel_source_hash(workload: str) -> str:
     h = hashlib.sha256()
-    for f in KERNEL_SOURCES:
+    for f in KERNEL_SOURCES[kernel_family(workload)]:
         with open(os.path.join(ROOT, "dense_gemm_epilogue_fp16_amd", "csrc", f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()[:16]
@@ -62,7 +70,7 @@ def traffic_from_profile(workload: str):
         return None
     with open(path) as f:
         t = json.load(f)
-    if t.get("kernel_source_hash") != kernel_source_hash():
+    if t.get("kernel_source_hash") != kernel_source_hash(workload):
         return None
     return t.get("bytes_per_launch")
 
@@ -851,7 +859,7 @@ def ingest_pmc(workload, fetch_dir, write_dir, copy_mib):
     f_scale = copy_bytes / (fetch[ck] * 1024.0)
     w_scale = copy_bytes / (write[ck] * 1024.0)
     gk = max(gemm_k, key=lambda k: fetch[k])  # one kernel name per workload in practice
-    out = {"workload": workload, "kernel": gk, "kernel_source_hash": kernel_source_hash(),
+    out = {"workload": workload, "kernel": gk, "kernel_source_hash": kernel_source_hash(workload),
            "fetch_kib_per_launch": fetch[gk], "write_kib_per_launch": write.get(gk),
            "copy_kernel": ck, "copy_bytes": copy_bytes, "copy_fetch_kib": fetch[ck], "copy_write_kib": write[ck],
            "fetch_scale": f_scale, "write_scale": w_scale,

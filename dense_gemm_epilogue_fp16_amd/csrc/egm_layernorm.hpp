@@ -15,7 +15,8 @@
 //     (d = mb - ma), always with the lower-numbered partner as "a", so every
 //     thread of a row ends with the same mean and M2;
 //   * rstd = 1 / sqrt(M2 / N + eps); each value is normalised, scaled, shifted
-//     (plus the residual) in fp32 and rounded once to the 16-bit type.
+//     (plus the residual) in fp32 and rounded once to the 16-bit type;
+//   * rows owned by a whole workgroup load gamma and beta together with x.
 // Columns past N (a ragged last chunk cannot occur: N is a multiple of 8)
 // read as absent; rows past M are not touched.
 //
@@ -73,6 +74,24 @@ __global__ void __launch_bounds__(256) layernorm_kernel(LnArgs p) {
   for (int q = 0; q < CPT; ++q) {
     const int c = t + TPR * q;
     v[q] = buf_load16(rx, c < chunks ? (uint32_t)c * 16u : OOB_OFFSET);
+  }
+  // gamma and beta: rows of a whole workgroup (256 threads) load theirs with
+  // x, so that their latency is not paid again after the statistics (about
+  // 8 % of a 65536 x 16384 bf16 pass); the shorter rows (a wave each, several
+  // rows per workgroup) keep more rows in flight without the extra registers
+  // and load them after the statistics
+  constexpr bool kGbEarly = TPR == 256 && CPT <= 8;
+  u32x4 gve[kGbEarly ? CPT : 1], bve[kGbEarly ? CPT : 1];
+  if constexpr (kGbEarly) {
+    const auto rg0 = make_rsrc(p.gamma != nullptr ? p.gamma : p.x, p.gamma != nullptr ? row_bytes : 0);
+    const auto rb0 = make_rsrc(p.beta != nullptr ? p.beta : p.x, p.beta != nullptr ? row_bytes : 0);
+#pragma unroll
+    for (int q = 0; q < CPT; ++q) {
+      const int c = t + TPR * q;
+      const uint32_t off = c < chunks ? (uint32_t)c * 16u : OOB_OFFSET;
+      gve[q] = p.gamma != nullptr ? buf_load16(rg0, off) : u32x4{0, 0, 0, 0};
+      bve[q] = p.beta != nullptr ? buf_load16(rb0, off) : u32x4{0, 0, 0, 0};
+    }
   }
   u32x4 rv[CPT];
   if constexpr (RES) {
@@ -140,8 +159,14 @@ __global__ void __launch_bounds__(256) layernorm_kernel(LnArgs p) {
     const int c = t + TPR * q;
     if (c >= chunks) continue;
     const uint32_t off = (uint32_t)c * 16u;
-    const u32x4 gv = p.gamma != nullptr ? buf_load16(rg, off) : u32x4{0, 0, 0, 0};
-    const u32x4 bv = p.beta != nullptr ? buf_load16(rb, off) : u32x4{0, 0, 0, 0};
+    u32x4 gv, bv;
+    if constexpr (kGbEarly) {
+      gv = gve[q];
+      bv = bve[q];
+    } else {
+      gv = p.gamma != nullptr ? buf_load16(rg, off) : u32x4{0, 0, 0, 0};
+      bv = p.beta != nullptr ? buf_load16(rb, off) : u32x4{0, 0, 0, 0};
+    }
     u32x4 out;
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
