@@ -35,15 +35,15 @@ struct ConfigInfo {
 
 // Tile configurations: 64-deep k-slabs (128-byte A rows: whole cache lines
 // per row, half the barriers of 32-deep slabs).  The 256x256 tile runs 8
-// waves (2 per SIMD, 64x128 each) so that one wave's MFMAs can issue while
-// its SIMD partner waits on LDS reads or copies; its 64 KiB slabs leave room
-// for a ring of 2.  The smaller tiles run 4 waves (2 x 2) with deeper rings.
+// waves (2 per SIMD, 2 x 4 of 128x64 each) so that one wave's MFMAs can issue
+// while its SIMD partner waits on LDS reads or copies; its 64 KiB slabs leave
+// room for a ring of 2.  The smaller tiles run 4 waves (2 x 2) with deeper rings.
 // 32x32x16 MFMA blocks, except config 5: the 64x64 tile with 16x16x32 blocks
 // (four independent accumulator chains per 32x32 wave tile instead of one;
 // 16-bit operands only), which the per-shape choice takes over config 4
 // for 16-bit operands.
 inline constexpr ConfigInfo kConfigs[] = {
-    {256, 256, 4, 2, 2, 64, 1.00, 32},
+    {256, 256, 2, 4, 2, 64, 1.00, 32},
     {256, 128, 2, 2, 3, 64, 0.90, 32},
     {128, 256, 2, 2, 3, 64, 0.90, 32},
     {128, 128, 2, 2, 4, 64, 0.75, 32},

@@ -267,7 +267,7 @@ def test_grid_limit_narrows_the_choice():
 def test_config_table():
     n = egm.egm_num_configs()
     assert n == 7
-    assert egm.egm_config_describe(0).startswith("tile=256x256 kslab=64 waves=4x2")
+    assert egm.egm_config_describe(0).startswith("tile=256x256 kslab=64 waves=2x4")
     # configs of 16x16x32 MFMA blocks exist for 16-bit operands only
     for c in range(n):
         d = dict(kv.split("=") for kv in egm.egm_config_describe(c).split())
