@@ -34,6 +34,20 @@ def _ref(ops, epilog):
                             ops.bias, ops.bias_layout, ops.residual)
 
 
+@pytest.mark.parametrize("cfg", CONFIGS)
+def test_residual_every_slab_count(cfg):
+    """fp8 slabs are 128 deep: every slab count from 1 to past two turns of
+    the deepest ring (4), with and without a partial last slab, BIAS_RESIDUAL
+    bit-exact on small-integer operands."""
+    for kt in range(1, 11):
+        for k in (128 * kt, 128 * kt - 112):
+            ops = W.fp8_integer_operands(72, 272, k, "e4m3", "e4m3", "bf16", seed=40 * cfg + k,
+                                         bias_layout="col", scale_a=2.0, scale_b=0.25, residual=True)
+            y, _, _ = _ref(ops, "BIAS_RESIDUAL")
+            d, _ = run_fp8(ops, "BIAS_RESIDUAL", force_config=cfg)
+            assert np.array_equal(d, exact_bits(y, "bf16")), f"k={k}"
+
+
 @pytest.mark.parametrize("out", ["fp16", "bf16"])
 @pytest.mark.parametrize("cfg", CONFIGS)
 @pytest.mark.parametrize("pair", PAIRS, ids=["x".join(p) for p in PAIRS])

@@ -59,17 +59,20 @@ def test_ring_turns_and_partial_slab(cfg):
     left over, and skips the A copies' per-lane k check in slabs wholly below
     K: every count of 64-deep slabs from 1 to past two turns of the deepest
     ring (4), with and without a partial last slab, bit-exact on
-    small-integer operands."""
+    small-integer operands, with the mask epilogue and with the residual."""
     m, n = 72, 264
     for kt in range(1, 11):
         for k in (64 * kt, 64 * kt - 56):
             ops = W.integer_operands(m, n, k, "bf16", seed=100 * cfg + k, lo=-1, hi=1, bias_layout="row",
                                      residual=True)
-            d, mask = run(ops, "RELU_AUX_BIAS", force_config=cfg)
-            y, z, mref = oracle_for(ops, "RELU_AUX_BIAS")
-            bad = d != exact_bits(y, "bf16")
-            assert not bad.any(), f"k={k}: {int(bad.sum())} outputs differ; first {tuple(np.argwhere(bad)[0])}"
-            assert np.array_equal(mask, mref), f"k={k}: mask differs"
+            for epilog in ("RELU_AUX_BIAS", "BIAS_RESIDUAL"):
+                d, mask = run(ops, epilog, force_config=cfg)
+                y, z, mref = oracle_for(ops, epilog)
+                bad = d != exact_bits(y, "bf16")
+                assert not bad.any(), (f"{epilog} k={k}: {int(bad.sum())} outputs differ; "
+                                       f"first {tuple(np.argwhere(bad)[0])}")
+                if epilog == "RELU_AUX_BIAS":
+                    assert np.array_equal(mask, mref), f"k={k}: mask differs"
 
 
 @pytest.mark.parametrize("cfg", CONFIGS)

@@ -45,6 +45,21 @@ def _run_bt(ops, epilog, *, fused=True, force_config=-1):
 
 
 @pytest.mark.parametrize("cfg", CONFIGS)
+def test_residual_every_slab_count(cfg):
+    """BIAS_RESIDUAL with B given transposed at every slab count from 1 to
+    past two turns of the deepest ring, with and without a partial last slab,
+    bit-exact on small-integer operands."""
+    m, n = 72, 264
+    for kt in range(1, 11):
+        for k in (64 * kt, 64 * kt - 56):
+            ops = W.integer_operands(m, n, k, "fp16", seed=300 * cfg + k, lo=-1, hi=1, bias_layout="col",
+                                     residual=True)
+            y, _, _ = eo.reference(ops.a, ops.b, "fp16", "BIAS_RESIDUAL", ops.bias, ops.bias_layout, ops.residual)
+            d, _ = _run_bt(ops, "BIAS_RESIDUAL", force_config=cfg)
+            assert np.array_equal(d, exact_bits(y, "fp16")), f"k={k}"
+
+
+@pytest.mark.parametrize("cfg", CONFIGS)
 @pytest.mark.parametrize("dtype", ["fp16", "bf16"])
 def test_integer_exact(dtype, cfg):
     m, n, k = 300, 264, 136
