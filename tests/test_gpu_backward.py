@@ -118,6 +118,15 @@ def test_edges_and_empty():
         d, grad = mm.execute(aux=torch.empty((0, 2), dtype=torch.uint8, device="cuda"))
     torch.cuda.synchronize()
     assert d.shape == (0, 16) and not grad.cpu().numpy().any()
+    # an empty n: the (m,1) gradient is a sum over no columns, all zeros
+    a = torch.ones((40, 64), dtype=torch.bfloat16, device="cuda")
+    b = torch.empty((64, 0), dtype=torch.bfloat16, device="cuda")
+    g = torch.full((40, 1), float("nan"), device="cuda")
+    with egm.Matmul(a, b) as mm:
+        mm.plan("DRELU_BGRAD", {"bias_grad": g})
+        d, grad = mm.execute(aux=torch.empty((40, 0), dtype=torch.uint8, device="cuda"))
+    torch.cuda.synchronize()
+    assert d.shape == (40, 0) and grad.shape == (40, 1) and not grad.cpu().numpy().any()
 
 
 def test_deterministic_gradient():

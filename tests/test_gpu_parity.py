@@ -218,6 +218,26 @@ def test_empty_m_is_noop():
     assert d.shape == (0, 16)
 
 
+def test_empty_n_is_noop():
+    """n = 0: D and the mask are empty; nothing is launched and the mask may be
+    the empty tensor."""
+    import torch
+    import dense_gemm_epilogue_fp16_amd as egm
+    a = torch.ones((40, 64), dtype=torch.float16, device="cuda")
+    b = torch.empty((64, 0), dtype=torch.float16, device="cuda")
+    for epilog, ins in (("BIAS", {"bias": torch.zeros((40, 1), dtype=torch.float16, device="cuda")}),
+                        ("RELU_AUX_BIAS", {"bias": torch.zeros((40, 1), dtype=torch.float16, device="cuda")}),
+                        ("DEFAULT", {})):
+        with egm.Matmul(a, b) as mm:
+            mm.plan(epilog, ins)
+            out = mm.execute()
+        torch.cuda.synchronize()
+        d = out[0] if isinstance(out, tuple) else out
+        assert d.shape == (40, 0), epilog
+        if isinstance(out, tuple):
+            assert out[1].shape == (40, 0)
+
+
 @pytest.mark.slow
 def test_maximum_n_and_k():
     """n = 2^21 with one row, and k = 2^21 with a single 8x8 output."""
