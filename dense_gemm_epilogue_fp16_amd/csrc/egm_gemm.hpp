@@ -1,8 +1,9 @@
 // egm_gemm.hpp - the fused GEMM + epilogue kernel for gfx950.
 //
 // One workgroup of WM x WN waves computes a BM x BN tile of D = epilogue(A.B)
-// (4 waves, 2 x 2, for the smaller tiles; 8 waves, 4 x 2, two per SIMD, for
-// 256 x 256, so that one wave's MFMAs issue while its partner waits):
+// (4 waves, 2 x 2, for the smaller tiles, 2 waves for 32 x 64; 8 waves, 2 x 4
+// of 128 x 64, two per SIMD, for 256 x 256, so that one wave's MFMAs issue
+// while its partner waits):
 //   * operand streaming: A [BM x BK] and B [BK x BN] k-slabs go from HBM
 //     straight into LDS with the gfx950 buffer-load-to-LDS instruction (16 bytes
 //     per lane, no VGPR staging); out-of-range lanes read 0, so ragged edges
@@ -709,7 +710,7 @@ __global__ void __launch_bounds__(C::NT, 1) gemm_epilogue_kernel(GemmArgs p) {
   // Load q (0 .. PW-1) of this wave for a slab into ring buffer `stage`: the
   // first A_PW are A loads, the rest B loads.
   // LDS base of the copies.  With one wave per SIMD (4 waves), and in the
-  // fp8 two-wave tile, the compiler would otherwise hoist every copy's LDS
+  // fp8 tile of two waves per SIMD, the compiler would otherwise hoist every copy's LDS
   // address (one per copy and ring buffer) out of the main loop into
   // registers of their own, and spill them; an opaque base keeps each
   // address a couple of scalar additions at its copy.
@@ -1016,7 +1017,7 @@ __global__ void __launch_bounds__(C::NT, 1) gemm_epilogue_kernel(GemmArgs p) {
     read_slice(0, 0, 0);
     // slab kt sits in ring buffer st = kt % STAGES (a constant in each copy
     // of the body below)
-    // refill == false (the slabs after the loop; fp8 two-wave tiles): the
+    // refill == false (the slabs after the loop; fp8 tiles of two waves per SIMD): the
     // slab kt + STAGES that would be loaded lies past K, and with a two-slab
     // ring the wait above is for every load anyway, so no empty loads need
     // to keep the count
