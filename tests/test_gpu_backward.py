@@ -45,6 +45,41 @@ def test_integer_exact(dtype, cfg, fused):
         assert np.array_equal(grad, grad_ref), layout
 
 
+def test_random_shapes_sweep():
+    """24 seeded random cases on small-integer operands: m from 1 to 700, n
+    and k multiples of 8 up to 720 and 1040; config, dtype, gradient axis,
+    fused or two-kernel path, and DRELU or DRELU_BGRAD drawn at random.  The
+    fp32 sums stay exact, so dZ is the single correct rounding and the fused
+    gradient equals the oracle's bit for bit; the two-kernel path sums the
+    rounded D, so its gradient is held to the bound that allows for that."""
+    rng = np.random.default_rng(4242)
+    for case in range(24):
+        m = int(rng.integers(1, 701))
+        n = 8 * int(rng.integers(1, 91))
+        k = 8 * int(rng.integers(1, 131))
+        dtype = ("fp16", "bf16")[int(rng.integers(2))]
+        cfg = int(rng.integers(len(CONFIGS)))
+        layout = ("row", "col")[int(rng.integers(2))]
+        fused = bool(rng.integers(2))
+        epilog = ("DRELU", "DRELU_BGRAD")[int(rng.integers(2))]
+        tag = f"case {case}: {m}x{n}x{k} {dtype} {epilog} cfg={cfg} grad={layout} fused={fused}"
+        print(tag, flush=True)
+        ops = W.integer_operands(m, n, k, dtype, seed=900 + case, lo=-1, hi=1)
+        mask = random_mask(m, n, 950 + case)
+        dz, grad_ref, bound = eo.backward_reference(ops.a, ops.b, dtype, epilog, mask,
+                                                    layout if epilog == "DRELU_BGRAD" else None)
+        d, grad = run_backward(ops, epilog, mask, layout if epilog == "DRELU_BGRAD" else None,
+                               force_config=cfg, fused=fused)
+        bad = d != exact_bits(dz, dtype)
+        assert not bad.any(), f"{tag}: {int(bad.sum())} outputs differ; first {tuple(np.argwhere(bad)[0])}"
+        if epilog == "DRELU_BGRAD" and fused:
+            assert np.array_equal(grad, grad_ref), f"{tag}: gradient differs"
+        elif epilog == "DRELU_BGRAD":
+            compare_bias_grad(grad, grad_ref, bound, d_ref=dz, dtype=dtype, layout=layout)
+        else:
+            assert grad is None
+
+
 @pytest.mark.parametrize("cfg", CONFIGS)
 @pytest.mark.parametrize("dtype", ["fp16", "bf16"])
 def test_normal_within_bounds(dtype, cfg):
