@@ -43,6 +43,37 @@ def test_layernorm_vs_oracle(cols, dtype):
         _check_stats(mean, rstd, mr, rr)
 
 
+def test_random_rows_sweep():
+    """24 seeded random cases: rows 1..300, row lengths multiples of 8 up to
+    20000, dtype, residual, gamma/beta present or not, eps, and the row
+    statistics' regime (mean offsets up to 100 standard deviations, which a
+    one-pass sum of squares would lose to cancellation) drawn at random."""
+    import dense_gemm_epilogue_fp16_amd as egm
+    rng = np.random.default_rng(77)
+    for case in range(24):
+        rows = int(rng.integers(1, 301))
+        cols = 8 * int(rng.integers(1, 2501))
+        dtype = ("fp16", "bf16")[int(rng.integers(2))]
+        x_std = float(10.0 ** rng.uniform(-2, 1))
+        x_mean = float(rng.choice([0.0, 1.0, 100.0])) * x_std
+        with_res = bool(rng.integers(2))
+        affine = bool(rng.integers(2))
+        eps = float(10.0 ** rng.uniform(-6, -2))
+        tag = f"case {case}: {rows}x{cols} {dtype} std={x_std:.3g} mean={x_mean:.3g} res={with_res} affine={affine} eps={eps:.2g}"
+        print(tag, flush=True)
+        o = W.layernorm_operands(rows, cols, dtype, seed=1000 + case, x_std=x_std, x_mean=x_mean,
+                                 residual_std=0.3 * x_std if with_res else None)
+        x = to_device(o.x, dtype)
+        g = to_device(o.gamma, dtype) if affine else None
+        b = to_device(o.beta, dtype) if affine else None
+        r = to_device(o.residual, dtype) if with_res else None
+        y, mean, rstd = egm.layer_norm(x, g, b, eps, residual=r, return_stats=True)
+        yr, mr, rr = eo.layer_norm_reference(o.x, dtype, o.gamma if affine else None, o.beta if affine else None, eps,
+                                             o.residual if with_res else None)
+        compare(to_host_bits(y), yr, dtype)
+        _check_stats(mean, rstd, mr, rr)
+
+
 def test_layernorm_options_and_edges():
     import torch
     import dense_gemm_epilogue_fp16_amd as egm
