@@ -42,6 +42,44 @@ def test_strided_batch_shared_weight(cfg):
         compare(to_host_bits(d[z]), y, dtype, z=zz, mask=mask[z].cpu().numpy(), mask_ref=mref)
 
 
+def test_strided_batch_random_sweep():
+    """16 seeded random batches, bit-exact on small-integer operands: batch
+    1..6, m 1..300, n and k multiples of 8 up to 320 and 520, config, dtype,
+    bias layout and epilog (DEFAULT, BIAS, RELU_BIAS) at random, with A per
+    problem and B either per problem or shared."""
+    import torch
+    import dense_gemm_epilogue_fp16_amd as egm
+    from parity import exact_bits
+    rng = np.random.default_rng(31)
+    for case in range(16):
+        batch = int(rng.integers(1, 7))
+        m = int(rng.integers(1, 301))
+        n = 8 * int(rng.integers(1, 41))
+        k = 8 * int(rng.integers(1, 66))
+        dtype = ("fp16", "bf16")[int(rng.integers(2))]
+        cfg = int(rng.integers(7))
+        layout = ("row", "col")[int(rng.integers(2))]
+        epilog = ("DEFAULT", "BIAS", "RELU_BIAS")[int(rng.integers(3))]
+        shared_b = bool(rng.integers(2))
+        tag = f"case {case}: batch {batch} {m}x{n}x{k} {dtype} {epilog} cfg={cfg} bias={layout} shared_b={shared_b}"
+        print(tag, flush=True)
+        probs = [W.integer_operands(m, n, k, dtype, seed=2000 + 10 * case + z, bias_layout=layout) for z in range(batch)]
+        bias = probs[0].bias
+        b_list = [probs[0].b] * batch if shared_b else [p.b for p in probs]
+        ins = {} if epilog == "DEFAULT" else {"bias": bias_tensor(bias, layout, dtype)}
+        with egm.Matmul(to_device(probs[0].a, dtype), to_device(b_list[0], dtype)) as mm:
+            mm.plan(epilog, ins, force_config=cfg)
+            d = mm.execute_batched(_stack([p.a for p in probs], dtype),
+                                   to_device(b_list[0], dtype) if shared_b else _stack(b_list, dtype))
+            torch.cuda.synchronize()
+        assert d.shape == (batch, m, n), tag
+        for z in range(batch):
+            y, _, _ = eo.reference(probs[z].a, b_list[z], dtype, epilog, None if epilog == "DEFAULT" else bias,
+                                   None if epilog == "DEFAULT" else layout)
+            bad = to_host_bits(d[z]) != exact_bits(y, dtype)
+            assert not bad.any(), f"{tag}, problem {z}: {int(bad.sum())} outputs differ"
+
+
 def test_strided_batch_weights_residual_and_drelu():
     import torch
     import dense_gemm_epilogue_fp16_amd as egm
