@@ -123,7 +123,15 @@ def main():
     ap.add_argument("--sustain-vendor", action="store_true",
                     help="with --sustain: then run the vendor GEMM alone (torch.matmul into the same outputs; "
                          "torch._scaled_mm for fp8) the same way, for the clock and power it sustains (context only)")
+    ap.add_argument("--mfma-shape-probe", type=float, default=0.0, metavar="SECONDS",
+                    help="instead of the bench line: run the MFMA-only probe (libegm_probe.so) with each 16-bit "
+                         "MFMA shape (32x32x16, then 16x16x32, twice) back to back on every CU for this many "
+                         "seconds each, printing one JSON line per second with its throughput and the board "
+                         "power and clocks, then one summary line per shape")
     args = ap.parse_args()
+    if args.mfma_shape_probe > 0:
+        mfma_shape_probe(args.mfma_shape_probe)
+        return
     if args.ingest_pmc:
         ingest_pmc(args.workload, *args.ingest_pmc, copy_mib=args.copy_mib or 1024)
         return
@@ -762,6 +770,90 @@ def _smi_sample():
     clks = [int(v) for k, v in row.items() if k and re.fullmatch(r"gfx_\d+_clk", k) and v.isdigit()]
     power = row.get("socket_power")
     return {"power_w": int(power) if power and power.isdigit() else None, "gfx_clk_mhz": clks}
+
+
+def mfma_shape_probe(seconds):
+    """Sustained throughput of the two 16-bit MFMA shapes with no memory
+    traffic (egm_mfma_probe.hip): 4 workgroups of 8 waves per CU, every wave a
+    chain of independent MFMAs on operands that switch between MFMAs.  Each
+    shape runs for `seconds` in windows of about one second, timed with HIP
+    events on the launch stream while amd-smi is sampled in a side thread; the
+    summary takes the windows after the first two (the board's ramp)."""
+    import ctypes
+    import threading
+
+    import torch
+    path = os.path.join(ROOT, "dense_gemm_epilogue_fp16_amd", "libegm_probe.so")
+    if not os.path.exists(path):
+        print(json.dumps({"error": "libegm_probe.so is not built: run __graft_entry__.build()"}), flush=True)
+        sys.exit(1)
+    lib = ctypes.CDLL(path)
+    lib.egm_mfma_probe.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p]
+    lib.egm_mfma_probe.restype = ctypes.c_int
+    dev = torch.device("cuda:0")
+    stream = torch.cuda.current_stream(dev)
+    blocks = 4 * 256
+    out = torch.empty(blocks * 512, dtype=torch.float32, device=dev)
+    per_iter = {32: 8 * 2 * 32 * 32 * 16, 16: 32 * 2 * 16 * 16 * 32}
+    iters = {32: 4000, 16: 2000}  # the same flops per launch for both shapes
+    summary = []
+    for shape in (32, 16, 32, 16):
+        flops = blocks * 8 * iters[shape] * per_iter[shape]
+        samples = []
+        stop = threading.Event()
+
+        def sampler():
+            while not stop.is_set():
+                smp = _smi_sample()
+                if smp is not None:
+                    samples.append((time.perf_counter(), smp))
+                stop.wait(0.5)
+
+        th = threading.Thread(target=sampler, daemon=True)
+        th.start()
+        windows = []
+        t0 = time.perf_counter()
+        while time.perf_counter() - t0 < seconds:
+            e0 = torch.cuda.Event(enable_timing=True)
+            e1 = torch.cuda.Event(enable_timing=True)
+            w0 = time.perf_counter()
+            e0.record(stream)
+            n = 0
+            while time.perf_counter() - w0 < 1.0:
+                rc = lib.egm_mfma_probe(shape, iters[shape], blocks, ctypes.c_void_p(out.data_ptr()),
+                                        ctypes.c_void_p(stream.cuda_stream))
+                if rc != 0:
+                    stop.set()
+                    print(json.dumps({"error": f"egm_mfma_probe returned {rc}"}), flush=True)
+                    sys.exit(1)
+                n += 1
+                if n % 8 == 0:
+                    torch.cuda.synchronize(dev)
+            e1.record(stream)
+            torch.cuda.synchronize(dev)
+            w1 = time.perf_counter()
+            inwin = [smp for (ts, smp) in samples if w0 <= ts <= w1]
+            pw = [smp["power_w"] for smp in inwin if smp["power_w"]]
+            clk = [sum(smp["gfx_clk_mhz"]) / len(smp["gfx_clk_mhz"]) for smp in inwin if smp["gfx_clk_mhz"]]
+            line = {"mfma": f"{shape}x{shape}x{16 if shape == 32 else 32}", "t_s": round(w1 - t0, 2),
+                    "tflops": round(n * flops / (e0.elapsed_time(e1) * 1e-3) / 1e12, 1),
+                    "power_w": round(sum(pw) / len(pw)) if pw else None,
+                    "gfx_clk_mhz_mean": round(sum(clk) / len(clk)) if clk else None}
+            windows.append(line)
+            print(json.dumps(line), flush=True)
+        stop.set()
+        th.join()
+        steady = windows[2:] or windows
+        tf = sum(w["tflops"] for w in steady) / len(steady)
+        clks = [w["gfx_clk_mhz_mean"] for w in steady if w["gfx_clk_mhz_mean"]]
+        pws = [w["power_w"] for w in steady if w["power_w"]]
+        summary.append({"mfma": windows[0]["mfma"], "steady_tflops": round(tf, 1),
+                        "gfx_clk_mhz": round(sum(clks) / len(clks)) if clks else None,
+                        "power_w": round(sum(pws) / len(pws)) if pws else None,
+                        "frac_of_clock_limited_peak": round(tf / (2500.0 * sum(clks) / len(clks) / 2400.0), 3)
+                        if clks else None})
+    for s_ in summary:
+        print(json.dumps({"summary": s_}), flush=True)
 
 
 def sustain(run_step, probe_ms, flops, seconds, dev, stream):

@@ -28,6 +28,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 INCLUDE = os.path.join(os.path.dirname(HERE), "include")
 LIB = os.path.join(HERE, "libegm.so")
+PROBE_LIB = os.path.join(HERE, "libegm_probe.so")  # the MFMA-shape power probe (benchmark only)
 OBJ_DIR = os.path.join(HERE, "_build")
 SANITIZED_LIB = os.path.join(OBJ_DIR, "libegm_host_sanitized.so")
 ARCH = "gfx950"
@@ -86,6 +87,10 @@ def build(verbose: bool = False, extra_flags=None) -> str:
     tmp = LIB + ".tmp"
     _run([cc, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *[o for _, o, _ in units]], verbose)
     os.replace(tmp, LIB)
+    # the measurement probe: a library of its own, loaded only by bench.py --mfma-shape-probe
+    tmp = PROBE_LIB + ".tmp"
+    _run([cc, *COMMON, *DEVICE_FLAGS, "-shared", os.path.join(CSRC, "egm_mfma_probe.hip"), "-o", tmp], verbose)
+    os.replace(tmp, PROBE_LIB)
     return LIB
 
 

@@ -483,3 +483,22 @@ def test_fp8_small_shapes_take_the_32x32_tile():
             assert egm.egm_plan_config(h) == 4
         finally:
             egm.egm_free(h)
+
+
+def test_mfma_probe_library_exports_and_rejects():
+    """The benchmark's MFMA-shape probe is a library of its own; its entry point
+    refuses bad arguments before any HIP call (so this runs without a GPU)."""
+    import ctypes
+    import os
+    path = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))),
+                        "dense_gemm_epilogue_fp16_amd", "libegm_probe.so")
+    if not os.path.exists(path):
+        pytest.skip("libegm_probe.so not built")
+    lib = ctypes.CDLL(path)
+    f = lib.egm_mfma_probe
+    f.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p]
+    f.restype = ctypes.c_int
+    assert f(24, 10, 1, ctypes.c_void_p(16), None) == 1   # unknown shape
+    assert f(32, 0, 1, ctypes.c_void_p(16), None) == 1    # no iterations
+    assert f(16, 10, 0, ctypes.c_void_p(16), None) == 1   # no workgroups
+    assert f(16, 10, 1, None, None) == 1                  # no output
