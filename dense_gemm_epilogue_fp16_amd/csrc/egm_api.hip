@@ -66,6 +66,15 @@ bool grid_fits(int64_t m, int64_t n, int c) {
 // operands only.
 bool config_built(int c, bool fp8) { return !fp8 || kConfigs[c].mi == 32; }
 
+// The per-shape choice takes the lean 256x256 tile (16x16x32 blocks) only
+// when K is long: its epilogue first moves the 16x16 blocks into the 32x32
+// layout, and at K = 8192 that cost ate the MFMA shape's gain (measured
+// 1-3 % slower with the mask epilogue, equal without); from K = 16384 on it
+// was 2-5 % faster on every shape measured.
+bool config_considered(int c, bool fp8, int64_t k) {
+  return config_built(c, fp8) && (!egm::lean_config(c) || k >= egm::kLeanMinK);
+}
+
 // Per-shape choice: among the configs whose grid fits, the one with the
 // smallest estimated time, counting whole waves of tiles over the 256 CUs,
 // scaled by the config's relative efficiency.  Ties go to the lower id.  -1
@@ -75,7 +84,7 @@ int choose_config(int64_t m, int64_t n, int64_t k, bool fp8, int64_t batch = 1) 
   int best = -1;
   double best_t = 0;
   for (int c = 0; c < kNumConfigs; ++c) {
-    if (!grid_fits(m, n, c) || !config_built(c, fp8)) continue;
+    if (!grid_fits(m, n, c) || !config_considered(c, fp8, k)) continue;
     const int64_t tiles = cdiv(m, kConfigs[c].bm) * cdiv(n, kConfigs[c].bn) * batch;
     const int64_t waves = cdiv(tiles, kNumCUs);
     const double t = double(waves) * kConfigs[c].bm * kConfigs[c].bn * double(k > 0 ? k : 1) / kConfigs[c].rel_eff;

@@ -644,7 +644,8 @@ __global__ void __launch_bounds__(C::NT, 1) gemm_epilogue_kernel(GemmArgs p) {
   // with B given transposed, the logical chunk of every copy sits in one
   // register, 4 bits each, copy q at bits 4q: k_lc)
   constexpr bool kTight = C::ES == 1 && C::NW == 8;
-  static_assert(!kTight || C::PW <= 8, "packed chunk indices: at most 8 copies per wave and slab");
+  constexpr bool kLean = C::MI == 16 && C::NW == 8;
+  static_assert(!(kTight || kLean) || C::PW <= 8, "packed chunk indices: at most 8 copies per wave and slab");
   uint32_t a_off[C::A_PW], a_k8[C::A_PW], k_lc = 0;
 #pragma unroll
   for (int u = 0; u < C::A_PW; ++u) {
@@ -652,7 +653,7 @@ __global__ void __launch_bounds__(C::NT, 1) gemm_epilogue_kernel(GemmArgs p) {
     const uint32_t row = C::A_ROWS_PER_DMA * q + lane / C::A_CHUNKS;
     const uint32_t lc = (lane % C::A_CHUNKS) ^ a_swz<C::A_CHUNKS>(row);
     a_k8[u] = lc * C::CE;
-    if constexpr (kTight && BT) k_lc |= lc << (4 * u);
+    if constexpr ((kTight && BT) || (kLean && !BT)) k_lc |= lc << (4 * u);
     a_off[u] = (row * (uint32_t)K + lc * C::CE) * C::ES;
   }
   // B load q fills k-rows q*R .. q*R+R-1 (R = B_ROWS_PER_DMA): lane L -> k-row
@@ -669,7 +670,7 @@ __global__ void __launch_bounds__(C::NT, 1) gemm_epilogue_kernel(GemmArgs p) {
       const uint32_t row = C::A_ROWS_PER_DMA * q + lane / C::A_CHUNKS;
       const uint32_t lc = (lane % C::A_CHUNKS) ^ a_swz<C::A_CHUNKS>(row);
       b_k8[u] = lc * C::CE;
-      if constexpr (kTight && BT) k_lc |= lc << (4 * (C::A_PW + u));
+      if constexpr ((kTight && BT) || (kLean && !BT)) k_lc |= lc << (4 * (C::A_PW + u));
       b_off[u] = (row * (uint32_t)K + lc * C::CE) * C::ES;
     } else {
       const uint32_t krow = q * C::B_ROWS_PER_DMA + lane / C::B_CHUNKS;
@@ -716,13 +717,13 @@ __global__ void __launch_bounds__(C::NT, 1) gemm_epilogue_kernel(GemmArgs p) {
   // address a couple of scalar additions at its copy.
   auto copy_base = [&]() {
     uint32_t b = smem_lds;
-    if constexpr (C::NW == 4 || kTight) asm volatile("" : "+s"(b));
+    if constexpr (C::NW == 4 || kTight || kLean) asm volatile("" : "+s"(b));
     return b;
   };
   // Per-lane k offset of copy u's piece within the slab (A, transposed B);
   // j: the copy's index among this wave's copies of the slab.
   auto k_of = [&](const auto& k8, int u, int j) -> uint32_t {
-    if constexpr (kTight && BT) {
+    if constexpr ((kTight && BT) || (kLean && !BT)) {
       // taken apart at each use (an opaque copy), so that the compiler does
       // not hoist the eight offsets out of the main loop into registers
       uint32_t kl = k_lc;
@@ -731,14 +732,27 @@ __global__ void __launch_bounds__(C::NT, 1) gemm_epilogue_kernel(GemmArgs p) {
     } else
       return k8[u];
   };
+  const uint32_t a_step = 2u * C::A_ROWS_PER_DMA * (uint32_t)K * C::ES;
+  const uint32_t b_step = BT ? a_step : 2u * C::B_ROWS_PER_DMA * (uint32_t)N * C::ES;
+  static_assert(!kLean || (C::A_PW == 4 && C::B_PW == 4 && C::A_ROWS_PER_DMA == 8 && (BT || C::B_ROWS_PER_DMA == 2)),
+                "the lean tile's copy offsets repeat every second copy");
+  auto off_of = [&](const auto& off, int u, uint32_t step) -> uint32_t {
+    if constexpr (kLean) {
+      uint32_t v = off[u & 1];
+      asm volatile("" : "+v"(v));
+      return v + (uint32_t)(u >> 1) * step;
+    } else {
+      return off[u];
+    }
+  };
   auto issue_one = [&](const SlabSrd& r, int stage, int q) {
     if (q < C::A_PW) {
       dma16(r.a, copy_base() + C::a_buf(stage) + (wave * C::A_PW + q) * 1024u,
-            r.kbase + k_of(a_k8, q, q) < (uint32_t)K ? a_off[q] : OOB_OFFSET);
+            r.kbase + k_of(a_k8, q, q) < (uint32_t)K ? off_of(a_off, q, a_step) : OOB_OFFSET);
     } else {
       const int u = q - C::A_PW;
       dma16(r.b, copy_base() + C::b_buf(stage) + (wave * C::B_PW + u) * 1024u,
-            !BT || r.kbase + k_of(b_k8, u, q) < (uint32_t)K ? b_off[u] : OOB_OFFSET);
+            !BT || r.kbase + k_of(b_k8, u, q) < (uint32_t)K ? off_of(b_off, u, b_step) : OOB_OFFSET);
     }
   };
 
@@ -902,21 +916,24 @@ __global__ void __launch_bounds__(C::NT, 1) gemm_epilogue_kernel(GemmArgs p) {
   constexpr int RA = C::ES == 2 ? 1 : 2;                   // reads per A fragment
   constexpr int RB = BT ? RA : (C::ES == 2 ? 2 : 4);        // reads per B fragment
   constexpr int NRD = RA * FMB + RB * FNB;                  // LDS read instructions per k-slice
-  u32x4 fa[2][FMB][RA];
+  u32x4 fa[kLean ? 1 : 2][FMB][RA];
   u32x2 fb[2][FNB][BT ? 1 : RB];
   u32x4 fbt[2][FNB][RA];  // transposed B: A-like 16-byte pieces
   auto read_piece = [&](int set, int stage, int ks, int piece) {
     if constexpr (M16) {
       if (piece < 1 || piece >= 1 + RB * FNB) {
         const int i = piece < 1 ? 0 : piece - RB * FNB;
-        fa[set][i][0] = *(const u32x4*)(smem + a16_off[ks] + (C::a_buf(stage) - C::a_buf(0)) + i * 16 * C::A_ROW);
+        fa[kLean ? 0 : set][i][0] =
+            *(const u32x4*)(smem + a16_off[ks] + (C::a_buf(stage) - C::a_buf(0)) + i * 16 * C::A_ROW);
       } else {
         const int j = (piece - 1) / RB, t = (piece - 1) % RB;
         constexpr uint32_t kB0 = C::b_buf(0);
         if constexpr (BT)
-          fbt[set][j][0] = *(const u32x4*)(smem + bt16_off[ks] + (C::b_buf(stage) - kB0) + j * 16 * C::A_ROW);
+          fbt[set][j][0] =
+              *(const u32x4*)(smem + bt16_off[ks] + (C::b_buf(stage) - kB0) + j * 16 * C::A_ROW);
         else
-          fb[set][j][t] = lds_read_tr<DT>(smem + b16_off[j] + (C::b_buf(stage) - kB0) + (32 * ks + 4 * t) * C::B_ROW);
+          fb[set][j][t] =
+              lds_read_tr<DT>(smem + b16_off[j] + (C::b_buf(stage) - kB0) + (32 * ks + 4 * t) * C::B_ROW);
       }
     } else {
       const uint8_t* const st = smem + stage * C::STAGE_BYTES;
@@ -948,11 +965,12 @@ __global__ void __launch_bounds__(C::NT, 1) gemm_epilogue_kernel(GemmArgs p) {
   auto mfma_one = [&](int set, int t) {
     if constexpr (M16) {
       const int i = t / C::FN16, j = t % C::FN16;
+      const int sf = kLean ? 0 : set;
       if constexpr (BT)
-        acc16[i][j] = mfma16<DT>(fbt[set][j][0], fa[set][i][0], acc16[i][j]);
+        acc16[i][j] = mfma16<DT>(fbt[set][j][0], fa[sf][i][0], acc16[i][j]);
       else
         acc16[i][j] = mfma16<DT>(u32x4{fb[set][j][0][0], fb[set][j][0][1], fb[set][j][1][0], fb[set][j][1][1]},
-                                 fa[set][i][0], acc16[i][j]);
+                                 fa[sf][i][0], acc16[i][j]);
     } else {
       const int i = t / C::FN, j = t % C::FN;
       if constexpr (BT && C::ES == 2) {
@@ -994,6 +1012,14 @@ __global__ void __launch_bounds__(C::NT, 1) gemm_epilogue_kernel(GemmArgs p) {
     }
   };
 
+  auto lean_row = [&](int set, int i, int rstage, int rks) {
+#pragma unroll
+    for (int j = 0; j < FNB; ++j) mfma_one(set, i * FNB + j);
+    if (i < RB * FNB) read_piece(set ^ 1, rstage, rks, 1 + i);
+    read_piece(set ^ 1, rstage, rks, i == 0 ? 0 : RB * FNB + i);
+  };
+  static_assert(!kLean || C::NS == 2, "lean 16x16 tile: two k-slices per slab");
+
   // ------------------------------------------------------------------ main loop
   // Ring of STAGES slabs; slab kt sits in buffer kt % STAGES.  Per slab:
   //   for each k-slice but the last: read the next k-slice | its MFMAs
@@ -1023,12 +1049,17 @@ __global__ void __launch_bounds__(C::NT, 1) gemm_epilogue_kernel(GemmArgs p) {
     // to keep the count
     auto slab = [&](int kt, int st, bool refill) {
       const int st_next = st + 1 == C::STAGES ? 0 : st + 1;
+      if constexpr (kLean) {
 #pragma unroll
-      for (int ks = 0; ks < C::NS - 1; ++ks) {
-        read_slice((ks + 1) & 1, st, ks + 1);
-        mfmas(ks & 1);
-        interleave();
-        __builtin_amdgcn_sched_barrier(0);
+        for (int i = 0; i < FMB; ++i) lean_row(0, i, st, 1);
+      } else {
+#pragma unroll
+        for (int ks = 0; ks < C::NS - 1; ++ks) {
+          read_slice((ks + 1) & 1, st, ks + 1);
+          mfmas(ks & 1);
+          interleave();
+          __builtin_amdgcn_sched_barrier(0);
+        }
       }
       wait_lgkmcnt<0>();
       wait_vmcnt<(C::STAGES - 2) * C::PW>();
@@ -1066,21 +1097,30 @@ __global__ void __launch_bounds__(C::NT, 1) gemm_epilogue_kernel(GemmArgs p) {
         // refill first; spreading the copies one per MFMA as the fp8 tile
         // does was 2-4 % slower here).  A uniform branch drops the per-lane
         // k check of the A copies in every slab below K.
-        const uint32_t sa = smem_lds + C::a_buf(st);
-        if (r.full) {
+        const uint32_t sa = (kLean ? copy_base() : smem_lds) + C::a_buf(st);
+        if (!kLean || refill) {
+          if (r.full) {
 #pragma unroll
-          for (int q = 0; q < C::A_PW; ++q) dma16(r.a, sa + (wave * C::A_PW + q) * 1024u, a_off[q]);
-        } else {
+            for (int q = 0; q < C::A_PW; ++q) dma16(r.a, sa + (wave * C::A_PW + q) * 1024u, off_of(a_off, q, a_step));
+          } else {
 #pragma unroll
-          for (int q = 0; q < C::A_PW; ++q) issue_one(r, st, q);
+            for (int q = 0; q < C::A_PW; ++q) issue_one(r, st, q);
+          }
         }
         __builtin_amdgcn_sched_barrier(0);
-        read_slice(0, st_next, 0);
-        mfmas((C::NS - 1) & 1);
-        interleave();
-        __builtin_amdgcn_sched_barrier(0);
+        if constexpr (kLean) {
 #pragma unroll
-        for (int q = C::A_PW; q < C::PW; ++q) issue_one(r, st, q);
+          for (int i = 0; i < FMB; ++i) lean_row(1, i, st_next, 0);
+        } else {
+          read_slice(0, st_next, 0);
+          mfmas((C::NS - 1) & 1);
+          interleave();
+          __builtin_amdgcn_sched_barrier(0);
+        }
+        if (!kLean || refill) {
+#pragma unroll
+          for (int q = C::A_PW; q < C::PW; ++q) issue_one(r, st, q);
+        }
         __builtin_amdgcn_sched_barrier(0);
       } else {
         // one wave per SIMD: the refill loads go out one at a time between the
@@ -1119,7 +1159,7 @@ __global__ void __launch_bounds__(C::NT, 1) gemm_epilogue_kernel(GemmArgs p) {
     }
 #pragma unroll
     for (int s = 0; s < C::STAGES - 1; ++s)
-      if (kt + s < KT) slab(kt + s, s, !(kTight && C::STAGES == 2));
+      if (kt + s < KT) slab(kt + s, s, !((kTight || kLean) && C::STAGES == 2));
   }
 
   // The epilogue takes the accumulators one 32-row block-row at a time, in
@@ -1164,7 +1204,7 @@ __global__ void __launch_bounds__(C::NT, 1) gemm_epilogue_kernel(GemmArgs p) {
   wait_vmcnt<0>();
   // the ring is free once every wave is past its last fragment read
   __syncthreads();
-  epilogue_store<DT, EPI, C::WM, C::WN, F8 != 0, C::FM, C::FN>(p, block_row, m0, n0, wm0, wn0, kTight ? lane_fresh() : lane,
+  epilogue_store<DT, EPI, C::WM, C::WN, F8 != 0, C::FM, C::FN>(p, block_row, m0, n0, wm0, wn0, kTight || kLean ? lane_fresh() : lane,
                                                                smem + wave * C::EPI_STAGE, bias_lds,
                                                                (float*)(smem + C::RED_OFF), scale);
 }

@@ -17,6 +17,14 @@
 #ifndef EGM_F8
 #define EGM_F8 0
 #endif
+// -DEGM_LEAN=1: only the lean tile's kernels (config 7), compiled with the
+// register-minimising scheduler; every other unit leaves them out
+#ifndef EGM_LEAN
+#define EGM_LEAN 0
+#endif
+#if EGM_LEAN && EGM_F8
+#error "the lean tile is built for 16-bit operands only"
+#endif
 
 namespace egm {
 namespace {
@@ -32,21 +40,32 @@ void launch_gemm(dim3 grid, hipStream_t s, const GemmArgs& a) {
   hipLaunchKernelGGL((gemm_epilogue_kernel<DT, EPI, C, F8, BT>), grid, dim3(C::NT), 0, s, a);
 }
 
-// configs this unit builds: 16x16 MFMA blocks are 16-bit only
+// configs this unit builds: 16x16 MFMA blocks are 16-bit only, and the lean
+// tile lives in units of its own
 template <int CFG>
 constexpr bool built_here() {
-  return F8 == 0 || kConfigs[CFG].mi == 32;
+  return (F8 == 0 || kConfigs[CFG].mi == 32) && lean_config(CFG) == (EGM_LEAN != 0);
+}
+
+// a config this unit builds, named in place of those it does not (the
+// conditional below instantiates both of its branches)
+constexpr int fallback_config() {
+  for (int c = 0; c < kNumConfigs; ++c)
+    if (lean_config(c) == (EGM_LEAN != 0)) return c;
+  return 0;
 }
 
 template <int EPI, bool BT, int... CFG>
 GemmLaunch pick_gemm(int cfg, std::integer_sequence<int, CFG...>) {
   GemmLaunch out = nullptr;
-  ((cfg == CFG ? (out = built_here<CFG>() ? &launch_gemm<EPI, (built_here<CFG>() ? CFG : 0), BT> : nullptr) : out),
+  ((cfg == CFG ? (out = built_here<CFG>() ? &launch_gemm<EPI, (built_here<CFG>() ? CFG : fallback_config()), BT>
+                                          : nullptr)
+               : out),
    ...);
   return out;
 }
 
-#if EGM_F8 == 0
+#if EGM_F8 == 0 && !EGM_LEAN
 template <int EPI>
 void launch_epi(dim3 grid, hipStream_t s, const EpiArgs& a) {
   hipLaunchKernelGGL((epilogue_kernel<DT, EPI>), grid, dim3(256), 0, s, a);
@@ -102,7 +121,7 @@ GemmLaunch gemm_table_bt(int epi, int cfg) {
 
 GemmLaunch gemm_table(int epi, int cfg, bool bt) { return bt ? gemm_table_bt<true>(epi, cfg) : gemm_table_bt<false>(epi, cfg); }
 
-#if EGM_F8 == 0
+#if EGM_F8 == 0 && !EGM_LEAN
 EpiLaunch epi_table(int epi) {
   switch (epi) {
     case EPI_BIAS: return &launch_epi<EPI_BIAS>;
@@ -118,7 +137,11 @@ EpiLaunch epi_table(int epi) {
 
 }  // namespace
 
-#if EGM_F8 != 0
+#if EGM_LEAN && EGM_DTYPE == 0
+GemmLaunch gemm_launcher_lean_f16(int epi, int cfg, bool bt) { return gemm_table(epi, cfg, bt); }
+#elif EGM_LEAN
+GemmLaunch gemm_launcher_lean_bf16(int epi, int cfg, bool bt) { return gemm_table(epi, cfg, bt); }
+#elif EGM_F8 != 0
 #define EGM_CAT3(a, b, c) a##b##_##c
 #define EGM_FP8_LAUNCHER(dt, f8) EGM_CAT3(gemm_launcher_fp8_, dt, f8)
 GemmLaunch EGM_FP8_LAUNCHER(EGM_DTYPE, EGM_F8)(int epi, int cfg, bool bt) { return gemm_table(epi, cfg, bt); }

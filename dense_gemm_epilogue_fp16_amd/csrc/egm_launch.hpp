@@ -38,10 +38,17 @@ struct ConfigInfo {
 // waves (2 per SIMD, 2 x 4 of 128x64 each) so that one wave's MFMAs can issue
 // while its SIMD partner waits on LDS reads or copies; its 64 KiB slabs leave
 // room for a ring of 2.  The smaller tiles run 4 waves (2 x 2) with deeper rings.
-// 32x32x16 MFMA blocks, except config 5: the 64x64 tile with 16x16x32 blocks
-// (four independent accumulator chains per 32x32 wave tile instead of one;
-// 16-bit operands only), which the per-shape choice takes over config 4
-// for 16-bit operands.
+// 32x32x16 MFMA blocks, except configs 5-7, with 16x16x32 blocks (16-bit
+// operands only): config 5, the 64x64 tile (four independent accumulator
+// chains per 32x32 wave tile instead of one), which the per-shape choice
+// takes over config 4; config 6, the 32x64 tile of two waves; and config 7,
+// the 256x256 tile of config 0 with 16x16x32 blocks and one set of
+// fragments (the "lean" tile: 16x16x32 MFMAs sustain more flops than
+// 32x32x16 ones at the board's power limit, and only a single fragment set
+// fits beside the accumulators at two waves per SIMD).  Config 7's kernels
+// are compiled in units of their own with the register-minimising scheduler
+// (see build.py); the per-shape choice takes it over config 0 for 16-bit
+// operands when K is long enough to amortise its epilogue's block shuffles.
 inline constexpr ConfigInfo kConfigs[] = {
     {256, 256, 2, 4, 2, 64, 1.00, 32},
     {256, 128, 2, 2, 3, 64, 0.90, 32},
@@ -50,8 +57,13 @@ inline constexpr ConfigInfo kConfigs[] = {
     {64, 64, 2, 2, 4, 64, 0.40, 32},
     {64, 64, 2, 2, 4, 64, 0.41, 16},
     {32, 64, 1, 2, 4, 64, 0.25, 16},
+    {256, 256, 2, 4, 2, 64, 1.02, 16},
 };
 inline constexpr int kNumConfigs = int(sizeof(kConfigs) / sizeof(kConfigs[0]));
+// the lean tile: 16x16x32 blocks with 8 waves (built in its own units)
+constexpr bool lean_config(int c) { return kConfigs[c].mi == 16 && kConfigs[c].wm * kConfigs[c].wn == 8; }
+// the shortest K for which the per-shape choice considers the lean tile
+inline constexpr int64_t kLeanMinK = 12288;
 
 using GemmLaunch = void (*)(dim3 grid, hipStream_t stream, const GemmArgs& args);
 using EpiLaunch = void (*)(dim3 grid, hipStream_t stream, const EpiArgs& args);
@@ -63,6 +75,9 @@ using PartialsLaunch = void (*)(dim3 grid, hipStream_t stream, const void* D, in
 // bt: B given transposed ([N, K] row-major)
 GemmLaunch gemm_launcher_f16(int epi, int cfg, bool bt);
 GemmLaunch gemm_launcher_bf16(int epi, int cfg, bool bt);
+// the lean tile's kernels (egm_kernels.hip built with -DEGM_LEAN=1)
+GemmLaunch gemm_launcher_lean_f16(int epi, int cfg, bool bt);
+GemmLaunch gemm_launcher_lean_bf16(int epi, int cfg, bool bt);
 EpiLaunch epi_launcher_f16(int epi);
 EpiLaunch epi_launcher_bf16(int epi);
 PartialsLaunch partials_launcher_f16();
@@ -93,6 +108,8 @@ inline GemmLaunch gemm_launcher_fp8(int dt, int f8, int epi, int cfg, bool bt) {
 }
 
 inline GemmLaunch gemm_launcher(int dt, int epi, int cfg, bool bt) {
+  if (cfg >= 0 && cfg < kNumConfigs && lean_config(cfg))
+    return dt == DT_F16 ? gemm_launcher_lean_f16(epi, cfg, bt) : gemm_launcher_lean_bf16(epi, cfg, bt);
   return dt == DT_F16 ? gemm_launcher_f16(epi, cfg, bt) : gemm_launcher_bf16(epi, cfg, bt);
 }
 inline EpiLaunch epi_launcher(int dt, int epi) { return dt == DT_F16 ? epi_launcher_f16(epi) : epi_launcher_bf16(epi); }

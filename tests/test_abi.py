@@ -210,12 +210,23 @@ def test_execute_validation_before_any_hip_call(monkeypatch):
     (4096, 4096, 1024, 0),    # FFN up-projection: 256 tiles of 256x256, one per CU
     (4096, 1024, 4096, 3),    # FFN down-projection: 256 tiles of 128x128
     (8192, 8192, 8192, 0),
-    (65536, 16384, 16384, 0),
+    (8192, 8192, 12280, 0),   # K below the lean tile's threshold
+    (8192, 8192, 12288, 7),   # from K = 12288 on: the lean 256x256 tile (16x16x32 blocks)
+    (65536, 16384, 16384, 7),
 ])
 def test_per_shape_choice(m, n, k, cfg):
     h = egm.egm_plan(m, n, k, F16, E["BIAS"], FAKE, ROW)
     try:
         assert egm.egm_plan_config(h) == cfg
+    finally:
+        egm.egm_free(h)
+
+
+def test_fp8_long_k_keeps_the_32x32_tile():
+    # the lean tile has 16x16x32 blocks, which exist for 16-bit operands only
+    h = egm.egm_plan_fp8(8192, 8192, 16384, egm.EGM_E4M3, egm.EGM_E4M3, BF16, FAKE, FAKE, E["BIAS"], FAKE, COL)
+    try:
+        assert egm.egm_plan_config(h) == 0
     finally:
         egm.egm_free(h)
 
@@ -266,8 +277,10 @@ def test_grid_limit_narrows_the_choice():
 
 def test_config_table():
     n = egm.egm_num_configs()
-    assert n == 7
+    assert n == 8
     assert egm.egm_config_describe(0).startswith("tile=256x256 kslab=64 waves=2x4")
+    d7 = egm.egm_config_describe(7)
+    assert d7.startswith("tile=256x256 kslab=64 waves=2x4") and "mfma=16x16x32" in d7
     # configs of 16x16x32 MFMA blocks exist for 16-bit operands only
     for c in range(n):
         d = dict(kv.split("=") for kv in egm.egm_config_describe(c).split())

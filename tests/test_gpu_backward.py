@@ -11,7 +11,7 @@ from parity import compare, compare_bias_grad, exact_bits, run, run_backward, to
 
 pytestmark = pytest.mark.gpu
 
-CONFIGS = tuple(range(7))  # every tile config (5, 6: 16x16x32 MFMA blocks)
+CONFIGS = tuple(range(8))  # every tile config (5, 6, 7: 16x16x32 MFMA blocks)
 RAGGED = (300, 264, 136)
 
 

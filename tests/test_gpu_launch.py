@@ -24,7 +24,7 @@ def _stack(arrs, dtype):
     return torch.stack([to_device(a, dtype) for a in arrs])
 
 
-@pytest.mark.parametrize("cfg", list(range(7)))
+@pytest.mark.parametrize("cfg", list(range(8)))
 def test_strided_batch_shared_weight(cfg):
     """Five problems with their own A and one shared B (a weight), RELU_AUX_BIAS."""
     import torch
@@ -57,7 +57,7 @@ def test_strided_batch_random_sweep():
         n = 8 * int(rng.integers(1, 41))
         k = 8 * int(rng.integers(1, 66))
         dtype = ("fp16", "bf16")[int(rng.integers(2))]
-        cfg = int(rng.integers(7))
+        cfg = int(rng.integers(8))
         layout = ("row", "col")[int(rng.integers(2))]
         epilog = ("DEFAULT", "BIAS", "RELU_BIAS")[int(rng.integers(3))]
         shared_b = bool(rng.integers(2))

@@ -14,7 +14,7 @@ pytestmark = pytest.mark.gpu
 
 EPILOGS_EXACT = ("DEFAULT", "BIAS", "RELU_BIAS", "RELU_AUX_BIAS", "BIAS_RESIDUAL")
 ALL_EPILOGS = EPILOGS_EXACT + ("GELU_BIAS",)
-CONFIGS = tuple(range(7))  # every tile config (5, 6: 16x16x32 MFMA blocks)
+CONFIGS = tuple(range(8))  # every tile config (5, 6, 7: 16x16x32 MFMA blocks)
 RAGGED = (300, 264, 136)  # m = 256+44, n = 256+8, k = 2*64+8
 
 

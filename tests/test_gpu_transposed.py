@@ -10,7 +10,7 @@ from parity import bias_tensor, compare, exact_bits, fp8_to_device, run_backward
 
 pytestmark = pytest.mark.gpu
 
-CONFIGS = tuple(range(7))  # every tile config (5, 6: 16x16x32 MFMA blocks)
+CONFIGS = tuple(range(8))  # every tile config (5, 6, 7: 16x16x32 MFMA blocks)
 FP8_CONFIGS = (0, 1, 2, 3, 4)  # the configs built for fp8 operands
 
 
