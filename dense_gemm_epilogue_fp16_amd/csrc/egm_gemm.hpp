@@ -644,6 +644,12 @@ __global__ void __launch_bounds__(C::NT, 1) gemm_epilogue_kernel(GemmArgs p) {
   // with B given transposed, the logical chunk of every copy sits in one
   // register, 4 bits each, copy q at bits 4q: k_lc)
   constexpr bool kTight = C::ES == 1 && C::NW == 8;
+  // kLean: the 256x256 tile of 8 waves with 16x16x32 blocks.  Its k-slices
+  // are 32 deep, so a fragment set is twice that of the 32x32 blocks; only one
+  // set of A fragments fits beside the 128 accumulators (see lean_row), and
+  // the register tricks of the fp8 tile apply (packed chunk indices for B not
+  // transposed, opaque LDS base, no empty refills after the loop, a fresh
+  // lane index in the epilogue), plus the copy offsets of off_of.
   constexpr bool kLean = C::MI == 16 && C::NW == 8;
   static_assert(!(kTight || kLean) || C::PW <= 8, "packed chunk indices: at most 8 copies per wave and slab");
   uint32_t a_off[C::A_PW], a_k8[C::A_PW], k_lc = 0;
@@ -732,6 +738,12 @@ __global__ void __launch_bounds__(C::NT, 1) gemm_epilogue_kernel(GemmArgs p) {
     } else
       return k8[u];
   };
+  // Global offset of copy u.  kLean: copies u and u + 2 of a wave cover rows
+  // 16 apart (B not transposed: k-rows 4 apart), which the swizzles map to the
+  // same chunks, so copies 2 and 3 add a uniform step to the offsets of 0 and
+  // 1 at the copy (an opaque value, so that the sums are not hoisted out of
+  // the main loop into registers of their own).  OOB_OFFSET plus a step stays
+  // past every buffer range.
   const uint32_t a_step = 2u * C::A_ROWS_PER_DMA * (uint32_t)K * C::ES;
   const uint32_t b_step = BT ? a_step : 2u * C::B_ROWS_PER_DMA * (uint32_t)N * C::ES;
   static_assert(!kLean || (C::A_PW == 4 && C::B_PW == 4 && C::A_ROWS_PER_DMA == 8 && (BT || C::B_ROWS_PER_DMA == 2)),
@@ -916,7 +928,7 @@ __global__ void __launch_bounds__(C::NT, 1) gemm_epilogue_kernel(GemmArgs p) {
   constexpr int RA = C::ES == 2 ? 1 : 2;                   // reads per A fragment
   constexpr int RB = BT ? RA : (C::ES == 2 ? 2 : 4);        // reads per B fragment
   constexpr int NRD = RA * FMB + RB * FNB;                  // LDS read instructions per k-slice
-  u32x4 fa[kLean ? 1 : 2][FMB][RA];
+  u32x4 fa[kLean ? 1 : 2][FMB][RA];  // kLean: one set of A fragments (see lean_row)
   u32x2 fb[2][FNB][BT ? 1 : RB];
   u32x4 fbt[2][FNB][RA];  // transposed B: A-like 16-byte pieces
   auto read_piece = [&](int set, int stage, int ks, int piece) {
@@ -1012,6 +1024,11 @@ __global__ void __launch_bounds__(C::NT, 1) gemm_epilogue_kernel(GemmArgs p) {
     }
   };
 
+  // kLean: the MFMAs of block row i of a k-slice (A fragment i, B fragments of
+  // set `set`), then the reads of k-slice `rks` of ring buffer `rstage` that
+  // this row frees or spreads: A fragment i (its last use was this row) and,
+  // while any are left, one piece of the B fragments, into the other set.
+  // The 16x16 blocks' accumulators go to the 32x32 layout in block_row.
   auto lean_row = [&](int set, int i, int rstage, int rks) {
 #pragma unroll
     for (int j = 0; j < FNB; ++j) mfma_one(set, i * FNB + j);
@@ -1050,6 +1067,7 @@ __global__ void __launch_bounds__(C::NT, 1) gemm_epilogue_kernel(GemmArgs p) {
     auto slab = [&](int kt, int st, bool refill) {
       const int st_next = st + 1 == C::STAGES ? 0 : st + 1;
       if constexpr (kLean) {
+        // k-slice 0 (set 0), reading k-slice 1 of this slab
 #pragma unroll
         for (int i = 0; i < FMB; ++i) lean_row(0, i, st, 1);
       } else {
@@ -1109,6 +1127,7 @@ __global__ void __launch_bounds__(C::NT, 1) gemm_epilogue_kernel(GemmArgs p) {
         }
         __builtin_amdgcn_sched_barrier(0);
         if constexpr (kLean) {
+          // k-slice 1 (set 1), reading k-slice 0 of the next slab
 #pragma unroll
           for (int i = 0; i < FMB; ++i) lean_row(1, i, st_next, 0);
         } else {
