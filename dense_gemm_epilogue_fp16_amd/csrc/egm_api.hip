@@ -67,10 +67,10 @@ bool grid_fits(int64_t m, int64_t n, int c) {
 bool config_built(int c, bool fp8) { return !fp8 || kConfigs[c].mi == 32; }
 
 // The per-shape choice takes the lean 256x256 tile (16x16x32 blocks) only
-// when K is long: its epilogue first moves the 16x16 blocks into the 32x32
-// layout, and at K = 8192 that cost ate the MFMA shape's gain (measured
-// 1-3 % slower with the mask epilogue, equal without); from K = 16384 on it
-// was 2-5 % faster on every shape measured.
+// when K is long: from K = 16384 on it measured 2-5 % faster than config 0
+// on every 16-bit shape tried; at K = 8192 it was equal (fp16 RELU_BIAS) or
+// 3-4 % slower (the mask epilogue, B transposed, the bias-gradient
+// backward), and 1.4 % slower on the FFN up-projection (K = 1024).
 bool config_considered(int c, bool fp8, int64_t k) {
   return config_built(c, fp8) && (!egm::lean_config(c) || k >= egm::kLeanMinK);
 }

@@ -48,7 +48,7 @@ struct ConfigInfo {
 // fits beside the accumulators at two waves per SIMD).  Config 7's kernels
 // are compiled in units of their own with the register-minimising scheduler
 // (see build.py); the per-shape choice takes it over config 0 for 16-bit
-// operands when K is long enough to amortise its epilogue's block shuffles.
+// operands from K = kLeanMinK on, where it measured faster.
 inline constexpr ConfigInfo kConfigs[] = {
     {256, 256, 2, 4, 2, 64, 1.00, 32},
     {256, 128, 2, 2, 3, 64, 0.90, 32},
