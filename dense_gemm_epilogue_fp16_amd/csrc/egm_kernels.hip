@@ -17,8 +17,10 @@
 #ifndef EGM_F8
 #define EGM_F8 0
 #endif
-// -DEGM_LEAN=1: only the lean tile's kernels (config 7), compiled with the
-// register-minimising scheduler; every other unit leaves them out
+// -DEGM_LEAN=1 / 2: only the lean tile's kernels (config 7), for B not
+// transposed with the forward epilogues (1) or for the rest (2), each unit
+// compiled with the instruction scheduler that keeps its kernels free of
+// scratch and fastest (build.py); every other unit leaves them out
 #ifndef EGM_LEAN
 #define EGM_LEAN 0
 #endif
@@ -97,9 +99,18 @@ LnLaunch ln_row(int cfg) {
 }
 #endif
 
+// the (epilogue, B layout) pairs this unit builds
+template <int EPI, bool BT>
+constexpr bool unit_builds() {
+  return EGM_LEAN == 0 || lean_unit(EPI, BT) == EGM_LEAN;
+}
+
 template <int EPI, bool BT>
 GemmLaunch gemm_row(int cfg) {
-  return pick_gemm<EPI, BT>(cfg, std::make_integer_sequence<int, kNumConfigs>{});
+  if constexpr (unit_builds<EPI, BT>())
+    return pick_gemm<EPI, BT>(cfg, std::make_integer_sequence<int, kNumConfigs>{});
+  else
+    return nullptr;
 }
 
 template <bool BT>
@@ -137,10 +148,14 @@ EpiLaunch epi_table(int epi) {
 
 }  // namespace
 
-#if EGM_LEAN && EGM_DTYPE == 0
-GemmLaunch gemm_launcher_lean_f16(int epi, int cfg, bool bt) { return gemm_table(epi, cfg, bt); }
-#elif EGM_LEAN
-GemmLaunch gemm_launcher_lean_bf16(int epi, int cfg, bool bt) { return gemm_table(epi, cfg, bt); }
+#if EGM_LEAN == 1 && EGM_DTYPE == 0
+GemmLaunch gemm_launcher_lean1_f16(int epi, int cfg, bool bt) { return gemm_table(epi, cfg, bt); }
+#elif EGM_LEAN == 1
+GemmLaunch gemm_launcher_lean1_bf16(int epi, int cfg, bool bt) { return gemm_table(epi, cfg, bt); }
+#elif EGM_LEAN == 2 && EGM_DTYPE == 0
+GemmLaunch gemm_launcher_lean2_f16(int epi, int cfg, bool bt) { return gemm_table(epi, cfg, bt); }
+#elif EGM_LEAN == 2
+GemmLaunch gemm_launcher_lean2_bf16(int epi, int cfg, bool bt) { return gemm_table(epi, cfg, bt); }
 #elif EGM_F8 != 0
 #define EGM_CAT3(a, b, c) a##b##_##c
 #define EGM_FP8_LAUNCHER(dt, f8) EGM_CAT3(gemm_launcher_fp8_, dt, f8)

@@ -46,8 +46,8 @@ struct ConfigInfo {
 // fragments (the "lean" tile: 16x16x32 MFMAs sustain more flops than
 // 32x32x16 ones at the board's power limit, and only a single fragment set
 // fits beside the accumulators at two waves per SIMD).  Config 7's kernels
-// are compiled in units of their own with the register-minimising scheduler
-// (see build.py); the per-shape choice takes it over config 0 for 16-bit
+// are compiled in units of their own with other instruction schedulers (see
+// build.py); the per-shape choice takes it over config 0 for 16-bit
 // operands from K = kLeanMinK on, where it measured faster.
 inline constexpr ConfigInfo kConfigs[] = {
     {256, 256, 2, 4, 2, 64, 1.00, 32},
@@ -75,9 +75,14 @@ using PartialsLaunch = void (*)(dim3 grid, hipStream_t stream, const void* D, in
 // bt: B given transposed ([N, K] row-major)
 GemmLaunch gemm_launcher_f16(int epi, int cfg, bool bt);
 GemmLaunch gemm_launcher_bf16(int epi, int cfg, bool bt);
-// the lean tile's kernels (egm_kernels.hip built with -DEGM_LEAN=1)
-GemmLaunch gemm_launcher_lean_f16(int epi, int cfg, bool bt);
-GemmLaunch gemm_launcher_lean_bf16(int epi, int cfg, bool bt);
+// the lean tile's kernels (egm_kernels.hip built with -DEGM_LEAN=1: B not
+// transposed, forward epilogues; -DEGM_LEAN=2: the others)
+GemmLaunch gemm_launcher_lean1_f16(int epi, int cfg, bool bt);
+GemmLaunch gemm_launcher_lean1_bf16(int epi, int cfg, bool bt);
+GemmLaunch gemm_launcher_lean2_f16(int epi, int cfg, bool bt);
+GemmLaunch gemm_launcher_lean2_bf16(int epi, int cfg, bool bt);
+// which lean unit builds an (epilogue, B layout): 1 or 2
+constexpr int lean_unit(int epi, bool bt) { return !bt && !epi_reads_mask(epi) ? 1 : 2; }
 EpiLaunch epi_launcher_f16(int epi);
 EpiLaunch epi_launcher_bf16(int epi);
 PartialsLaunch partials_launcher_f16();
@@ -108,8 +113,11 @@ inline GemmLaunch gemm_launcher_fp8(int dt, int f8, int epi, int cfg, bool bt) {
 }
 
 inline GemmLaunch gemm_launcher(int dt, int epi, int cfg, bool bt) {
-  if (cfg >= 0 && cfg < kNumConfigs && lean_config(cfg))
-    return dt == DT_F16 ? gemm_launcher_lean_f16(epi, cfg, bt) : gemm_launcher_lean_bf16(epi, cfg, bt);
+  if (cfg >= 0 && cfg < kNumConfigs && lean_config(cfg)) {
+    if (lean_unit(epi, bt) == 1)
+      return dt == DT_F16 ? gemm_launcher_lean1_f16(epi, cfg, bt) : gemm_launcher_lean1_bf16(epi, cfg, bt);
+    return dt == DT_F16 ? gemm_launcher_lean2_f16(epi, cfg, bt) : gemm_launcher_lean2_bf16(epi, cfg, bt);
+  }
   return dt == DT_F16 ? gemm_launcher_f16(epi, cfg, bt) : gemm_launcher_bf16(epi, cfg, bt);
 }
 inline EpiLaunch epi_launcher(int dt, int epi) { return dt == DT_F16 ? epi_launcher_f16(epi) : epi_launcher_bf16(epi); }
