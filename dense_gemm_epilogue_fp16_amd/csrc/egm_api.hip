@@ -66,25 +66,39 @@ bool grid_fits(int64_t m, int64_t n, int c) {
 // operands only.
 bool config_built(int c, bool fp8) { return !fp8 || kConfigs[c].mi == 32; }
 
+// The shortest K for which the per-shape choice considers the lean tile for
+// a GEMM kernel with B not transposed whose epilogue neither writes nor reads
+// the ReLU mask (every other kernel: kLeanMinK).
+constexpr int64_t kLeanMinKPlain = 2048;
+bool lean_plain(int gemm_epi, bool bt) {
+  return egm::lean_unit(gemm_epi, bt) == 1 && gemm_epi != egm::EPI_RELU_AUX;
+}
+
 // The per-shape choice takes the lean 256x256 tile (16x16x32 blocks) only
-// when K is long: from K = 16384 on it measured 2-5 % faster than config 0
-// on every 16-bit shape tried; at K = 8192 it was equal (fp16 RELU_BIAS) or
-// 3-4 % slower (the mask epilogue, B transposed, the bias-gradient
-// backward), and 1.4 % slower on the FFN up-projection (K = 1024).
-bool config_considered(int c, bool fp8, int64_t k) {
-  return config_built(c, fp8) && (!egm::lean_config(c) || k >= egm::kLeanMinK);
+// where it measured faster than config 0.  Kernels with B not transposed and
+// no mask: 0.5-5 % faster from K = 2048 on (8192x8192x2048 to 8192^3, bf16
+// and fp16, the bias, ReLU, GELU and residual epilogues; 4096^3 GELU 5 %),
+// equal at K = 1024 (the FFN up-projection).  The others (the mask epilogue,
+// B transposed, the backward epilogues): from K = 16384 on equal to 4.8 %
+// faster, at K = 8192 1-4 % slower.  gemm_epi: the epilogue the GEMM kernel
+// itself applies (EPI_NONE on the two-kernel path).
+bool config_considered(int c, bool fp8, int64_t k, int gemm_epi, bool bt) {
+  if (!config_built(c, fp8)) return false;
+  if (!egm::lean_config(c)) return true;
+  return k >= (lean_plain(gemm_epi, bt) ? kLeanMinKPlain : egm::kLeanMinK);
 }
 
 // Per-shape choice: among the configs whose grid fits, the one with the
 // smallest estimated time, counting whole waves of tiles over the 256 CUs,
 // scaled by the config's relative efficiency.  Ties go to the lower id.  -1
-// when no config fits.  batch > 1: a strided batch of that many problems in
+// when no config fits.  gemm_epi, bt: the GEMM kernel's epilogue and B
+// layout (config_considered).  batch > 1: a strided batch of that many problems in
 // one launch (grid.y), whose tiles fill the CUs together.
-int choose_config(int64_t m, int64_t n, int64_t k, bool fp8, int64_t batch = 1) {
+int choose_config(int64_t m, int64_t n, int64_t k, bool fp8, int gemm_epi, bool bt, int64_t batch = 1) {
   int best = -1;
   double best_t = 0;
   for (int c = 0; c < kNumConfigs; ++c) {
-    if (!grid_fits(m, n, c) || !config_considered(c, fp8, k)) continue;
+    if (!grid_fits(m, n, c) || !config_considered(c, fp8, k, gemm_epi, bt)) continue;
     const int64_t tiles = cdiv(m, kConfigs[c].bm) * cdiv(n, kConfigs[c].bn) * batch;
     const int64_t waves = cdiv(tiles, kNumCUs);
     const double t = double(waves) * kConfigs[c].bm * kConfigs[c].bn * double(k > 0 ? k : 1) / kConfigs[c].rel_eff;
@@ -124,6 +138,13 @@ struct egm_plan_s {
 };
 
 namespace {
+
+// The epilogue the GEMM kernel applies: the plan's, or none on the
+// two-kernel path (where a second kernel applies it).
+int gemm_epi_of(const egm_plan_s* p) {
+  const int epi = epi_of(p->epilog);
+  return !p->fused && epi != egm::EPI_NONE ? int(egm::EPI_NONE) : epi;
+}
 
 // Live plans.  A handle is a number handed out once and never again, not the
 // plan's address: a NULL, freed or foreign handle is recognised by a lookup
@@ -242,7 +263,7 @@ hipError_t launch_plan(const egm_plan_s* p, int cfg, const void* A, const void* 
   const int epi = epi_of(p->epilog);
   const bool two_kernels = !p->fused && epi != egm::EPI_NONE;
   g.D = two_kernels ? ws : D;
-  const int gemm_epi = two_kernels ? egm::EPI_NONE : epi;
+  const int gemm_epi = gemm_epi_of(p);
   const bool b_t = p->b_transposed != 0;
   GemmLaunch gl = p->f8 != 0 ? egm::gemm_launcher_fp8(dt, p->f8, gemm_epi, cfg, b_t)
                              : egm::gemm_launcher(dt, gemm_epi, cfg, b_t);
@@ -422,7 +443,7 @@ egm_status_t plan_impl(egm_plan_t* out, int64_t m, int64_t n, int64_t k, egm_dty
   p->scale_b = scale_b;
   p->b_transposed = b_transposed;
   p->fused = fused;
-  p->config = force >= 0 ? force : choose_config(m, n, k, f8 != 0);
+  p->config = force >= 0 ? force : choose_config(m, n, k, f8 != 0, gemm_epi_of(p), b_transposed != 0);
   p->chosen_per_shape = force < 0 && !tune;
   // the launch must fit one grid dimension and the config exist for the
   // operand type (autotuning tries only such configs, and the per-shape
@@ -607,7 +628,7 @@ egm_status_t egm_execute_strided(egm_plan_t plan, int64_t batch, const void* A, 
   // its problems share the CUs); a forced or autotuned config is kept
   int cfg = p->config;
   if (p->chosen_per_shape && batch > 1) {
-    const int c = choose_config(p->m, p->n, p->k, p->f8 != 0, batch);
+    const int c = choose_config(p->m, p->n, p->k, p->f8 != 0, gemm_epi_of(p), p->b_transposed != 0, batch);
     if (c >= 0) cfg = c;
   }
   const hipError_t err =

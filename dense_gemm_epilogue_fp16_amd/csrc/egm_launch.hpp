@@ -48,7 +48,8 @@ struct ConfigInfo {
 // fits beside the accumulators at two waves per SIMD).  Config 7's kernels
 // are compiled in units of their own with other instruction schedulers (see
 // build.py); the per-shape choice takes it over config 0 for 16-bit
-// operands from K = kLeanMinK on, where it measured faster.
+// operands where it measured faster: from K = 2048 on for the kernels with B
+// not transposed and no mask, from K = kLeanMinK on for the others.
 inline constexpr ConfigInfo kConfigs[] = {
     {256, 256, 2, 4, 2, 64, 1.00, 32},
     {256, 128, 2, 2, 3, 64, 0.90, 32},
@@ -62,7 +63,8 @@ inline constexpr ConfigInfo kConfigs[] = {
 inline constexpr int kNumConfigs = int(sizeof(kConfigs) / sizeof(kConfigs[0]));
 // the lean tile: 16x16x32 blocks with 8 waves (built in its own units)
 constexpr bool lean_config(int c) { return kConfigs[c].mi == 16 && kConfigs[c].wm * kConfigs[c].wn == 8; }
-// the shortest K for which the per-shape choice considers the lean tile
+// the shortest K for which the per-shape choice considers the lean tile for
+// every kernel (those with B not transposed and no mask: from K = 2048 on)
 inline constexpr int64_t kLeanMinK = 12288;
 
 using GemmLaunch = void (*)(dim3 grid, hipStream_t stream, const GemmArgs& args);

@@ -207,15 +207,51 @@ def test_execute_validation_before_any_hip_call(monkeypatch):
 @pytest.mark.parametrize("m,n,k,cfg", [
     (256, 256, 512, 6),       # small square: 32 tiles of 32x64 (16x16x32 blocks, 16-bit operands)
     (1024, 512, 2048, 6),     # the bias-fusion page's example shape: 256 tiles of 32x64, one per CU
-    (4096, 4096, 1024, 0),    # FFN up-projection: 256 tiles of 256x256, one per CU
+    (4096, 4096, 1024, 0),    # FFN up-projection: 256 tiles of 256x256, one per CU (K below 2048)
+    (4096, 4096, 2040, 0),
+    (4096, 4096, 2048, 7),    # from K = 2048 on: the lean 256x256 tile (16x16x32 blocks)
     (4096, 1024, 4096, 3),    # FFN down-projection: 256 tiles of 128x128
-    (8192, 8192, 8192, 0),
-    (8192, 8192, 12280, 0),   # K below the lean tile's threshold
-    (8192, 8192, 12288, 7),   # from K = 12288 on: the lean 256x256 tile (16x16x32 blocks)
+    (8192, 8192, 8192, 7),
     (65536, 16384, 16384, 7),
 ])
 def test_per_shape_choice(m, n, k, cfg):
+    # a forward epilogue without the mask, B not transposed
     h = egm.egm_plan(m, n, k, F16, E["BIAS"], FAKE, ROW)
+    try:
+        assert egm.egm_plan_config(h) == cfg
+    finally:
+        egm.egm_free(h)
+
+
+@pytest.mark.parametrize("kind", ["mask", "b_transposed", "backward"])
+@pytest.mark.parametrize("k,cfg", [(8192, 0), (12280, 0), (12288, 7), (16384, 7)])
+def test_per_shape_choice_long_k_only(kind, k, cfg):
+    # the mask epilogue, B transposed and the backward epilogues take the lean
+    # tile only from K = 12288 on
+    kw = dict(epilog=E["BIAS"], bias=FAKE, bias_layout=ROW)
+    if kind == "mask":
+        kw["epilog"] = E["RELU_AUX_BIAS"]
+    elif kind == "b_transposed":
+        kw["b_transposed"] = 1
+    else:
+        kw = dict(epilog=E["DRELU_BGRAD"], bias=0, bias_layout=ROW, bias_grad=FAKE)
+    h = egm.egm_plan(8192, 8192, k, F16, kw.pop("epilog"), kw.pop("bias"), kw.pop("bias_layout"), **kw)
+    try:
+        assert egm.egm_plan_config(h) == cfg
+    finally:
+        egm.egm_free(h)
+
+
+@pytest.mark.parametrize("epilog", ["DEFAULT", "BIAS", "RELU_AUX_BIAS", "DRELU"])
+@pytest.mark.parametrize("fused,cfg", [(1, None), (0, 7)])
+def test_per_shape_choice_two_kernel_path(epilog, fused, cfg):
+    # on the two-kernel path the GEMM kernel applies no epilogue (a second
+    # kernel does), so its GEMM takes the lean tile at K = 8192 whatever the
+    # epilogue; fused, only the epilogues without the mask do
+    if cfg is None:
+        cfg = 0 if epilog in ("RELU_AUX_BIAS", "DRELU") else 7
+    bias, layout = (FAKE, ROW) if epilog in ("BIAS", "RELU_AUX_BIAS") else (0, egm.EGM_BIAS_NONE)
+    h = egm.egm_plan(8192, 8192, 8192, F16, E[epilog], bias, layout, fused=fused)
     try:
         assert egm.egm_plan_config(h) == cfg
     finally:
