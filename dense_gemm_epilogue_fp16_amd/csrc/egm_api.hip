@@ -77,11 +77,13 @@ bool lean_plain(int gemm_epi, bool bt) {
 // The per-shape choice takes the lean 256x256 tile (16x16x32 blocks) only
 // where it measured faster than config 0.  Kernels with B not transposed and
 // no mask: 0.5-5 % faster from K = 2048 on (8192x8192x2048 to 8192^3, bf16
-// and fp16, the bias, ReLU, GELU and residual epilogues; 4096^3 GELU 5 %),
-// equal at K = 1024 (the FFN up-projection).  The others (the mask epilogue,
-// B transposed, the backward epilogues): from K = 16384 on equal to 4.8 %
-// faster, at K = 8192 1-4 % slower.  gemm_epi: the epilogue the GEMM kernel
-// itself applies (EPI_NONE on the two-kernel path).
+// and fp16, the bias, ReLU, GELU and residual epilogues; 4096^3 GELU 5 %;
+// 2.5-5.3 % on the 17 shapes of an 87-shape fp16 sweep where it is chosen),
+// equal at K = 1024 (the FFN up-projection), mostly 2-4 % slower at K = 512.
+// The others (the mask epilogue, B transposed, the backward epilogues): from
+// K = 16384 on equal (the mask) to 3.5 % faster (B transposed), at K = 8192
+// 1-4 % slower.  gemm_epi: the epilogue the GEMM kernel itself applies
+// (EPI_NONE on the two-kernel path).
 bool config_considered(int c, bool fp8, int64_t k, int gemm_epi, bool bt) {
   if (!config_built(c, fp8)) return false;
   if (!egm::lean_config(c)) return true;
@@ -92,8 +94,8 @@ bool config_considered(int c, bool fp8, int64_t k, int gemm_epi, bool bt) {
 // smallest estimated time, counting whole waves of tiles over the 256 CUs,
 // scaled by the config's relative efficiency.  Ties go to the lower id.  -1
 // when no config fits.  gemm_epi, bt: the GEMM kernel's epilogue and B
-// layout (config_considered).  batch > 1: a strided batch of that many problems in
-// one launch (grid.y), whose tiles fill the CUs together.
+// layout (config_considered).  batch > 1: a strided batch of that many
+// problems in one launch (grid.y), whose tiles fill the CUs together.
 int choose_config(int64_t m, int64_t n, int64_t k, bool fp8, int gemm_epi, bool bt, int64_t batch = 1) {
   int best = -1;
   double best_t = 0;
